@@ -1,0 +1,603 @@
+/*
+ * vc_oracle.c -- plain CPU oracle for VC-Attention FP8 (V-Smooth + ExpCast-FP8).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it.  It shares no code, header, table or constant generator with the HIP
+ * library: every step below is written from the source pages and from the OCP
+ * 8-bit floating point definition, in the order those describe it, with no
+ * blocking or fusion beyond what the method states.
+ *
+ * Sources (the pages are web articles about VC-Attention):
+ *   [P1] "VC-Attention et FLUX 3 accelerent la generation d'images sur Blackwell"
+ *        (ip73.fr), introduction (block scales fixed by the block maximum; V-Smooth
+ *        reorders value tokens by a light online clustering; ExpCast-FP8 maps
+ *        log-domain scores straight to E4M3 probability codes) and section
+ *        "Le compromis entre vitesse et fidelite" (repair budget rho = 0.005 picks
+ *        the tokens with the largest quantisation error and corrects their residual).
+ *   [P5] "VC-Attention acelera atencao em modelos de video de IA em ate 3,58x sem
+ *        retreinamento" (noticiai.com.br): section "Por que a atencao e o gargalo"
+ *        (Q/K smoothing of earlier methods; FP32 softmax is the slowest stage),
+ *        section "V-Smooth: corrigindo outliers de valor" (Group / Demean / Restore),
+ *        section "ExpCast-FP8: eliminando o gargalo do softmax" (an E4M3 byte read
+ *        as an integer is about 8*log2(v)+56; one fused multiply-add writes it).
+ *   OCP "8-bit Floating Point Specification (OFP8)", E4M3 format.
+ *
+ * Readings taken where the pages are silent (each is also listed in the design
+ * notes of the repository):
+ *   - k-means is Lloyd's algorithm with a fixed iteration count, Forgy initial
+ *     centroids drawn by a seeded splitmix64 partial Fisher-Yates shuffle, squared
+ *     L2 distance evaluated as ||c||^2 - 2 v.c with explicit fp32 fma chains in
+ *     channel order, ties to the lowest cluster id, empty clusters keep their
+ *     centroid, labels taken from the last assignment.
+ *   - means (K channel mean, V block means, centroids) are exact sums of values
+ *     rounded to 2^-24 fixed point, divided once in fp64, rounded to fp32.
+ *   - the permutation is a stable sort of positions by cluster id; Q follows it
+ *     when VC_PERMUTE_Q is set and the output is written back in original order.
+ *   - ExpCast code = clamp(rne(fma_f32(S_raw, alpha, bias - M)), 0, 126) with
+ *     bias = 56 + 8k (k = 8 by default): the shift 8k cancels between P.V and the
+ *     row sum; the row maximum M moves once per 128-key block, before that block's
+ *     codes, and only when the block maximum exceeds it by more than tau code
+ *     units (tau = 0 is the textbook online softmax).
+ *   - the row sum adds the decoded codes that P.V uses; Restore adds
+ *     (row sum of the block) * (block mean) to the accumulator.
+ *   - repair: m = ceil(rho*N) tokens per (batch, head) with the largest
+ *     sum_c (sV_c * delta_c)^2, ties to the lower position; their residual error
+ *     delta (in V code units, stored as bf16) is added with codes formed from the
+ *     final row maximum; the row sum is left unchanged.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma -shared -fPIC (fp32 operations
+ * must not be contracted; fmaf is always an explicit single-rounding fma).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OC_VSMOOTH 1u
+#define OC_REPAIR 2u
+#define OC_PERMUTE_Q 4u
+
+typedef struct {
+  int32_t B, H, N, d;     /* d must be 128 */
+  int32_t C, T;           /* clusters, Lloyd iterations */
+  uint64_t seed;
+  float rho;              /* repair budget */
+  float sm_scale;         /* softmax scale (1/sqrt(d) when <= 0) */
+  int32_t expcast_k;      /* additive shift k of the ExpCast bias 56 + 8k */
+  float tau;              /* lazy-max slack, code units */
+  uint32_t flags;
+} oc_params;
+
+/* Per-head outputs of the prepare stage; every array holds nheads slots. */
+typedef struct {
+  int32_t *labels;   /* [nh][N]   cluster id of each original token            */
+  int32_t *perm;     /* [nh][N]   position -> original token index              */
+  int32_t *iperm;    /* [nh][N]   original token index -> position              */
+  float *centroids;  /* [nh][C][d] centroids after the last update               */
+  float *kbar;       /* [nh][d]   channel mean of K                             */
+  uint8_t *q8;       /* [nh][Npad][d] Q codes, position order                    */
+  uint8_t *k8;       /* [nh][Npad][d] K codes (smoothed K), position order       */
+  float *sq, *sk;    /* [nh][nblk] block scales                                  */
+  float *mu;         /* [nh][nblk][d] block means of V (real units)              */
+  float *mup;        /* [nh][nblk][d] block means in V code units (mu * inv)     */
+  uint8_t *v8;       /* [nh][Npad][d] residual codes, position order             */
+  float *sv, *inv;   /* [nh][d] per-channel residual scale and its inverse       */
+  float *err;        /* [nh][N]  repair criterion per position                   */
+  int32_t *rep_pos;  /* [nh][mcap] repaired positions, ascending                 */
+  uint16_t *rep_delta; /* [nh][mcap][d] bf16 residual error, V code units        */
+  int32_t mcap;      /* capacity of the repair arrays (>= m)                     */
+} oc_prep;
+
+/* ------------------------------------------------------------------------- */
+/* Scalar formats                                                            */
+/* ------------------------------------------------------------------------- */
+
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* bf16 round-to-nearest-even from fp32 (finite inputs). */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* OCP E4M3 (E4M3FN): 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent
+ * field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; no infinities. */
+double oc_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest E4M3 value with ties to even mantissa, magnitudes at or above 448
+ * saturate to 448, the sign is kept (so -0 and tiny negatives give 0x80). */
+uint8_t oc_e4m3_encode(float xf) {
+  double x = (double)xf, a = fabs(x);
+  uint8_t sign = signbit(xf) ? 0x80 : 0x00;
+  int code;
+  if (isnan(xf)) return 0x7f;
+  if (a >= 448.0) {
+    code = 0x7e;
+  } else if (a < ldexp(1.0, -6)) {
+    /* subnormal band: multiples of 2^-9; m == 8 is the smallest normal (code 8) */
+    code = (int)rint(a * 512.0);
+  } else {
+    int e;
+    double fr = frexp(a, &e); /* a = fr * 2^e, fr in [0.5, 1) */
+    int ue = e - 1;           /* a = (2 fr) * 2^ue, 2 fr in [1, 2) */
+    int m = (int)rint((2.0 * fr - 1.0) * 8.0);
+    if (m == 8) {
+      m = 0;
+      ue += 1;
+    }
+    code = ((ue + 7) << 3) | m;
+    if (code > 0x7e) code = 0x7e;
+  }
+  return (uint8_t)(sign | code);
+}
+
+/* ExpCast-FP8 [P5 "ExpCast-FP8"]: one fp32 fma from the raw score to the byte. */
+uint8_t oc_expcast(float s_raw, float alpha, float beta) {
+  float y = rintf(fmaf(s_raw, alpha, beta));
+  if (!(y > 0.0f)) return 0; /* also maps -inf (masked keys) to 0 */
+  if (y > 126.0f) return 126;
+  return (uint8_t)y;
+}
+
+/* splitmix64 (Steele, Lea, Flood 2014; Vigna's public-domain reference). */
+static uint64_t sm64_next(uint64_t *s) {
+  uint64_t z = (*s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* Value rounded to the 2^-24 fixed-point grid, as an exact integer. */
+static int64_t fx24(float x) { return llrintf(x * 16777216.0f); }
+
+static float fixed_mean(int64_t sum, int64_t n) {
+  return (float)(((double)sum * 0x1p-24) / (double)n);
+}
+
+/* Block scale and inverse from the block maximum [P1 introduction]. */
+static void scale_from_amax(float amax, float *s, float *inv) {
+  if (amax < 0x1p-100f) {
+    *s = 1.0f;
+    *inv = 1.0f;
+  } else {
+    *s = amax / 448.0f;
+    *inv = 448.0f / amax;
+  }
+}
+
+static int32_t repair_count(const oc_params *P) {
+  double m;
+  if (!(P->flags & OC_REPAIR) || !(P->rho > 0.0f)) return 0;
+  m = ceil((double)P->rho * (double)P->N);
+  if (m > P->N) m = P->N;
+  return (int32_t)m;
+}
+
+int32_t oc_repair_count(const oc_params *P) { return repair_count(P); }
+
+/* ------------------------------------------------------------------------- */
+/* Prepare: V-Smooth Group [P5 "V-Smooth", Group]                             */
+/* ------------------------------------------------------------------------- */
+
+/* Forgy initial centroid indices: partial Fisher-Yates over [0, N). */
+void oc_kmeans_init_indices(uint64_t seed, int64_t head, int32_t N, int32_t C, int32_t *out) {
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  uint64_t st = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(head + 1));
+  for (int32_t i = 0; i < N; ++i) idx[i] = i;
+  for (int32_t i = 0; i < C; ++i) {
+    uint64_t r = sm64_next(&st);
+    int32_t j = i + (int32_t)(r % (uint64_t)(N - i));
+    int32_t t = idx[i];
+    idx[i] = idx[j];
+    idx[j] = t;
+    out[i] = idx[i];
+  }
+  free(idx);
+}
+
+static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d]*/,
+                        int32_t *labels, float *cent /*[C][d]*/) {
+  const int N = P->N, d = P->d, C = P->C;
+  int32_t *init = (int32_t *)malloc(sizeof(int32_t) * (size_t)C);
+  float *cc = (float *)malloc(sizeof(float) * (size_t)C);
+  int64_t *sum = (int64_t *)malloc(sizeof(int64_t) * (size_t)C * d);
+  int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * (size_t)C);
+
+  oc_kmeans_init_indices(P->seed, head, N, C, init);
+  for (int k = 0; k < C; ++k)
+    for (int c = 0; c < d; ++c) cent[(size_t)k * d + c] = v[(size_t)init[k] * d + c];
+
+  for (int it = 0; it < P->T; ++it) {
+    /* assignment step: argmin_k ||c_k||^2 - 2 v.c_k */
+    for (int k = 0; k < C; ++k) {
+      float s = 0.0f;
+      for (int c = 0; c < d; ++c) s = fmaf(cent[(size_t)k * d + c], cent[(size_t)k * d + c], s);
+      cc[k] = s;
+    }
+    for (int j = 0; j < N; ++j) {
+      const float *vj = v + (size_t)j * d;
+      int best = 0;
+      float bestD = 0.0f;
+      for (int k = 0; k < C; ++k) {
+        float dot = 0.0f, D;
+        for (int c = 0; c < d; ++c) dot = fmaf(vj[c], cent[(size_t)k * d + c], dot);
+        D = fmaf(-2.0f, dot, cc[k]);
+        if (k == 0 || D < bestD) {
+          best = k;
+          bestD = D;
+        }
+      }
+      labels[j] = best;
+    }
+    /* update step: each non-empty cluster moves to the mean of its members */
+    memset(sum, 0, sizeof(int64_t) * (size_t)C * d);
+    memset(cnt, 0, sizeof(int64_t) * (size_t)C);
+    for (int j = 0; j < N; ++j) {
+      int k = labels[j];
+      cnt[k] += 1;
+      for (int c = 0; c < d; ++c) sum[(size_t)k * d + c] += fx24(v[(size_t)j * d + c]);
+    }
+    for (int k = 0; k < C; ++k)
+      if (cnt[k] > 0)
+        for (int c = 0; c < d; ++c) cent[(size_t)k * d + c] = fixed_mean(sum[(size_t)k * d + c], cnt[k]);
+  }
+  free(init);
+  free(cc);
+  free(sum);
+  free(cnt);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Prepare: one (batch, head)                                                 */
+/* ------------------------------------------------------------------------- */
+
+static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, const uint16_t *kh,
+                         const uint16_t *vh, oc_prep *o, int slot) {
+  const int N = P->N, d = P->d, C = P->C;
+  const int nblk = (N + 127) / 128, Npad = nblk * 128;
+  const int vs = (P->flags & OC_VSMOOTH) != 0;
+  const int m = repair_count(P);
+  float *q = (float *)malloc(sizeof(float) * (size_t)N * d);
+  float *k = (float *)malloc(sizeof(float) * (size_t)N * d);
+  float *v = (float *)malloc(sizeof(float) * (size_t)N * d);
+  float *x = (float *)malloc(sizeof(float) * (size_t)N * d); /* scaled residual, position order */
+  int32_t *labels = o->labels + (size_t)slot * N;
+  int32_t *perm = o->perm + (size_t)slot * N;
+  int32_t *iperm = o->iperm + (size_t)slot * N;
+  float *kbar = o->kbar + (size_t)slot * d;
+  uint8_t *q8 = o->q8 + (size_t)slot * Npad * d;
+  uint8_t *k8 = o->k8 + (size_t)slot * Npad * d;
+  uint8_t *v8 = o->v8 + (size_t)slot * Npad * d;
+  float *sq = o->sq + (size_t)slot * nblk, *sk = o->sk + (size_t)slot * nblk;
+  float *mu = o->mu + (size_t)slot * nblk * d, *mup = o->mup + (size_t)slot * nblk * d;
+  float *sv = o->sv + (size_t)slot * d, *inv = o->inv + (size_t)slot * d;
+  float *err = o->err + (size_t)slot * N;
+
+  for (size_t i = 0; i < (size_t)N * d; ++i) {
+    q[i] = bf16_to_f32(qh[i]);
+    k[i] = bf16_to_f32(kh[i]);
+    v[i] = bf16_to_f32(vh[i]);
+  }
+
+  /* Group: k-means labels, then a stable sort of positions by label. */
+  if (vs) {
+    int64_t *start = (int64_t *)calloc((size_t)C + 1, sizeof(int64_t));
+    kmeans_head(P, head, v, labels, o->centroids + (size_t)slot * C * d);
+    for (int j = 0; j < N; ++j) start[labels[j] + 1] += 1;
+    for (int kk = 0; kk < C; ++kk) start[kk + 1] += start[kk];
+    for (int j = 0; j < N; ++j) perm[start[labels[j]]++] = j;
+    free(start);
+  } else {
+    for (int j = 0; j < N; ++j) {
+      labels[j] = 0;
+      perm[j] = j;
+    }
+    memset(o->centroids + (size_t)slot * C * d, 0, sizeof(float) * (size_t)C * d);
+  }
+  for (int p = 0; p < N; ++p) iperm[perm[p]] = p;
+
+  /* K smoothing: subtract the channel mean of K over all N tokens [P5 "Por que..."]. */
+  for (int c = 0; c < d; ++c) {
+    int64_t s = 0;
+    for (int j = 0; j < N; ++j) s += fx24(k[(size_t)j * d + c]);
+    kbar[c] = fixed_mean(s, N);
+  }
+
+  /* Per-128-position-block E4M3 quantisation of Q and smoothed K [P1 intro]. */
+  memset(q8, 0, (size_t)Npad * d);
+  memset(k8, 0, (size_t)Npad * d);
+  for (int b = 0; b < nblk; ++b) {
+    int p0 = b * 128, p1 = p0 + 128 < N ? p0 + 128 : N;
+    float aq = 0.0f, ak = 0.0f, s, iv;
+    for (int p = p0; p < p1; ++p) {
+      int jq = (P->flags & OC_PERMUTE_Q) ? perm[p] : p, jk = perm[p];
+      for (int c = 0; c < d; ++c) {
+        float xq = q[(size_t)jq * d + c];
+        float xk = k[(size_t)jk * d + c] - kbar[c];
+        if (fabsf(xq) > aq) aq = fabsf(xq);
+        if (fabsf(xk) > ak) ak = fabsf(xk);
+      }
+    }
+    scale_from_amax(aq, &s, &iv);
+    sq[b] = s;
+    for (int p = p0; p < p1; ++p) {
+      int jq = (P->flags & OC_PERMUTE_Q) ? perm[p] : p;
+      for (int c = 0; c < d; ++c) q8[(size_t)p * d + c] = oc_e4m3_encode(q[(size_t)jq * d + c] * iv);
+    }
+    scale_from_amax(ak, &s, &iv);
+    sk[b] = s;
+    for (int p = p0; p < p1; ++p) {
+      int jk = perm[p];
+      for (int c = 0; c < d; ++c) {
+        float xk = k[(size_t)jk * d + c] - kbar[c];
+        k8[(size_t)p * d + c] = oc_e4m3_encode(xk * iv);
+      }
+    }
+  }
+
+  /* Demean: each 128-position block of permuted V subtracts its own mean
+   * [P5 "V-Smooth", Demean]; residuals get one E4M3 scale per channel. */
+  for (int b = 0; b < nblk; ++b) {
+    int p0 = b * 128, p1 = p0 + 128 < N ? p0 + 128 : N;
+    for (int c = 0; c < d; ++c) {
+      int64_t s = 0;
+      if (vs) {
+        for (int p = p0; p < p1; ++p) s += fx24(v[(size_t)perm[p] * d + c]);
+        mu[(size_t)b * d + c] = fixed_mean(s, p1 - p0);
+      } else {
+        mu[(size_t)b * d + c] = 0.0f;
+      }
+    }
+  }
+  for (int c = 0; c < d; ++c) {
+    float a = 0.0f;
+    for (int p = 0; p < N; ++p) {
+      float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
+      if (fabsf(r) > a) a = fabsf(r);
+    }
+    scale_from_amax(a, &sv[c], &inv[c]);
+  }
+  memset(v8, 0, (size_t)Npad * d);
+  for (int p = 0; p < N; ++p)
+    for (int c = 0; c < d; ++c) {
+      float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
+      float xx = r * inv[c];
+      x[(size_t)p * d + c] = xx;
+      v8[(size_t)p * d + c] = oc_e4m3_encode(xx);
+    }
+  for (int b = 0; b < nblk; ++b)
+    for (int c = 0; c < d; ++c) mup[(size_t)b * d + c] = mu[(size_t)b * d + c] * inv[c];
+
+  /* Repair set [P1 "Le compromis..."]: per-position squared quantisation error of
+   * the value residual in real units, fp32 fma chain over channels. */
+  for (int p = 0; p < N; ++p) {
+    float e = 0.0f;
+    for (int c = 0; c < d; ++c) {
+      float dl = x[(size_t)p * d + c] - (float)oc_e4m3_decode(v8[(size_t)p * d + c]);
+      float t = sv[c] * dl;
+      e = fmaf(t, t, e);
+    }
+    err[p] = e;
+  }
+  if (m > 0) {
+    /* top m by (err descending, position ascending): repeated selection of the
+     * best remaining position is slow but plainly correct. */
+    uint8_t *taken = (uint8_t *)calloc((size_t)N, 1);
+    int32_t *sel = o->rep_pos + (size_t)slot * o->mcap;
+    uint16_t *dl = o->rep_delta + (size_t)slot * o->mcap * d;
+    int32_t n = 0;
+    for (int i = 0; i < m; ++i) {
+      int best = -1;
+      for (int p = 0; p < N; ++p) {
+        if (taken[p]) continue;
+        if (best < 0 || err[p] > err[best]) best = p;
+      }
+      taken[best] = 1;
+    }
+    for (int p = 0; p < N; ++p)
+      if (taken[p]) {
+        sel[n] = p;
+        for (int c = 0; c < d; ++c) {
+          float de = x[(size_t)p * d + c] - (float)oc_e4m3_decode(v8[(size_t)p * d + c]);
+          dl[(size_t)n * d + c] = f32_to_bf16(de);
+        }
+        ++n;
+      }
+    free(taken);
+  }
+  free(q);
+  free(k);
+  free(v);
+  free(x);
+}
+
+/* Prepare the heads listed in heads[0..nheads) (global index b*H + h); slot i of
+ * every output array receives heads[i].  Inputs are bf16 [B][H][N][d]. */
+int oc_prepare(const oc_params *P, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+               const int32_t *heads, int32_t nheads, oc_prep *o) {
+  if (P->d != 128 || P->N < 1 || P->C < 1 || P->C > P->N || P->T < 1) return 1;
+  if (o->mcap < repair_count(P)) return 2;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < nheads; ++i) {
+    size_t off = (size_t)heads[i] * P->N * P->d;
+    prepare_head(P, heads[i], q + off, k + off, v + off, o, i);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Forward: online ExpCast softmax with Restore and repair                    */
+/* ------------------------------------------------------------------------- */
+
+static float sm_scale_of(const oc_params *P) {
+  return P->sm_scale > 0.0f ? P->sm_scale : (float)(1.0 / sqrt((double)P->d));
+}
+
+/* c0 converts a raw score (code units of Q times code units of K, times the two
+ * block scales) to ExpCast code units: 8 * log2(e) * softmax scale. */
+static float code_gain(const oc_params *P) {
+  return (float)(8.0 * 1.4426950408889634074 * (double)sm_scale_of(P));
+}
+
+/* Decoded value of every code, filled from oc_e4m3_decode before any
+ * parallel region (a cache of the decoder, nothing more). */
+static double DEC[256];
+static int dec_ready = 0;
+static void init_dec(void) {
+  if (dec_ready) return;
+  for (int c = 0; c < 256; ++c) DEC[c] = oc_e4m3_decode((uint8_t)c);
+  dec_ready = 1;
+}
+
+/* Exact dot product of two E4M3 code rows (every product is a multiple of
+ * 2^-18 below 2^18, so the fp64 sum is exact), rounded once to fp32. */
+static float raw_score(const uint8_t *a, const uint8_t *b, int d) {
+  double s = 0.0;
+  for (int c = 0; c < d; ++c) s += DEC[a[c]] * DEC[b[c]];
+  return (float)s;
+}
+
+static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t row, double *out,
+                        uint8_t *pcodes) {
+  const int N = P->N, d = P->d;
+  const int nblk = (N + 127) / 128, Npad = nblk * 128;
+  const int m = repair_count(P);
+  const uint8_t *q8 = o->q8 + (size_t)slot * Npad * d;
+  const uint8_t *k8 = o->k8 + (size_t)slot * Npad * d;
+  const uint8_t *v8 = o->v8 + (size_t)slot * Npad * d;
+  const float *sq = o->sq + (size_t)slot * nblk, *sk = o->sk + (size_t)slot * nblk;
+  const float *mup = o->mup + (size_t)slot * nblk * d;
+  const float *sv = o->sv + (size_t)slot * d;
+  const int p = (P->flags & OC_PERMUTE_Q) ? o->iperm[(size_t)slot * N + row] : row;
+  const int a = p / 128;
+  const float c0 = code_gain(P);
+  const float bias = (float)(56 + 8 * P->expcast_k);
+  float M = -INFINITY;
+  double ell = 0.0, acc[128];
+  float S[128];
+  uint8_t code[128];
+
+  for (int c = 0; c < d; ++c) acc[c] = 0.0;
+  for (int b = 0; b < nblk; ++b) {
+    int j0 = b * 128, j1 = j0 + 128 < N ? j0 + 128 : N;
+    float alpha = (sq[a] * sk[b]) * c0;
+    float smax = -INFINITY, tmax, Mn, beta;
+    double r, lb = 0.0;
+    for (int j = j0; j < j1; ++j) {
+      S[j - j0] = raw_score(q8 + (size_t)p * d, k8 + (size_t)j * d, d);
+      if (S[j - j0] > smax) smax = S[j - j0];
+    }
+    tmax = smax * alpha;
+    Mn = (isinf(M) || (tmax - M) > P->tau) ? tmax : M;
+    beta = bias - Mn;
+    r = isinf(M) ? 0.0 : exp2(((double)M - (double)Mn) / 8.0);
+    for (int j = j0; j < j1; ++j) {
+      code[j - j0] = oc_expcast(S[j - j0], alpha, beta);
+      lb += DEC[code[j - j0]];
+      if (pcodes) pcodes[j] = code[j - j0];
+    }
+    ell = ell * r + lb;
+    for (int c = 0; c < d; ++c) {
+      double pv = 0.0;
+      for (int j = j0; j < j1; ++j) pv += DEC[code[j - j0]] * DEC[v8[(size_t)j * d + c]];
+      acc[c] = acc[c] * r + lb * (double)mup[(size_t)b * d + c] + pv;
+    }
+    M = Mn;
+  }
+  if (pcodes)
+    for (int j = N; j < Npad; ++j) pcodes[j] = 0;
+
+  /* repair: residual error of the selected tokens, weighted by final-M codes */
+  for (int i = 0; i < m; ++i) {
+    int j = o->rep_pos[(size_t)slot * o->mcap + i];
+    int b = j / 128;
+    float alpha = (sq[a] * sk[b]) * c0;
+    float s = raw_score(q8 + (size_t)p * d, k8 + (size_t)j * d, d);
+    double pw = DEC[oc_expcast(s, alpha, bias - M)];
+    const uint16_t *dl = o->rep_delta + ((size_t)slot * o->mcap + i) * d;
+    for (int c = 0; c < d; ++c) acc[c] += pw * (double)bf16_to_f32(dl[c]);
+  }
+  for (int c = 0; c < d; ++c) out[c] = (double)sv[c] * acc[c] / ell;
+}
+
+/* Simulated output rows.  row_slot[i] selects the prepared head, row_index[i] is
+ * the query row in ORIGINAL token order; out is [nrows][d] fp64.  pcodes, when
+ * not NULL, receives [nrows][Npad] P codes in key position order. */
+int oc_forward_rows(const oc_params *P, const oc_prep *o, const int32_t *row_slot,
+                    const int32_t *row_index, int32_t nrows, double *out, uint8_t *pcodes) {
+  const int Npad = ((P->N + 127) / 128) * 128;
+  if (P->d != 128) return 1;
+  init_dec();
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int i = 0; i < nrows; ++i)
+    forward_row(P, o, row_slot[i], row_index[i], out + (size_t)i * P->d,
+                pcodes ? pcodes + (size_t)i * Npad : NULL);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Exact FP64 attention: softmax(q K^T * scale) V from the bf16 inputs.        */
+/* ------------------------------------------------------------------------- */
+
+int oc_exact_rows(const oc_params *P, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const int32_t *row_head, const int32_t *row_index, int32_t nrows, double *out) {
+  const int N = P->N, d = P->d;
+  const double scale = (double)sm_scale_of(P);
+  if (d != 128) return 1;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int i = 0; i < nrows; ++i) {
+    size_t off = (size_t)row_head[i] * N * d;
+    const uint16_t *qi = q + off + (size_t)row_index[i] * d;
+    double *s = (double *)malloc(sizeof(double) * (size_t)N);
+    double mx = -INFINITY, den = 0.0;
+    double *o = out + (size_t)i * d;
+    for (int j = 0; j < N; ++j) {
+      double t = 0.0;
+      for (int c = 0; c < d; ++c)
+        t += (double)bf16_to_f32(qi[c]) * (double)bf16_to_f32(k[off + (size_t)j * d + c]);
+      s[j] = t * scale;
+      if (s[j] > mx) mx = s[j];
+    }
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j < N; ++j) {
+      double w = exp(s[j] - mx);
+      den += w;
+      for (int c = 0; c < d; ++c) o[c] += w * (double)bf16_to_f32(v[off + (size_t)j * d + c]);
+    }
+    for (int c = 0; c < d; ++c) o[c] /= den;
+    free(s);
+  }
+  return 0;
+}
+
+/* Array helpers used by the pins. */
+void oc_e4m3_decode_array(const uint8_t *c, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_e4m3_decode(c[i]);
+}
+void oc_e4m3_encode_array(const float *x, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_e4m3_encode(x[i]);
+}
+void oc_expcast_array(const float *s, float alpha, float beta, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_expcast(s[i], alpha, beta);
+}
+void oc_splitmix64_array(uint64_t state, uint64_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = sm64_next(&state);
+}

@@ -1,0 +1,485 @@
+"""Pins of the CPU oracle against facts fixed outside it: the OCP E4M3 definition
+(checked through torch's independent float8_e4m3fn codec), the ExpCast byte
+relation the VC-Attention article states, closed forms, special cases that
+reduce to plain means, invariances of non-causal attention, brute force on tiny
+inputs and torch's fp64 attention.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from synthetic import inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page_facts():
+    facts, ms = {}, {}
+    for line in open(os.path.join(GOLD, "page_facts.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        if line[0] == "repair_m":
+            ms[int(line[1])] = int(line[2])
+        else:
+            facts[line[0]] = float(line[1])
+    return facts, ms
+
+
+def _torch_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def _torch_e4m3_decode(c: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(c, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------- codec
+
+def test_e4m3_decode_ocp_points():
+    for line in open(os.path.join(GOLD, "e4m3_ocp_points.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        code, val = int(line[0], 16), float(line[1])
+        got = orc.e4m3_decode([code])[0]
+        if math.isnan(val):
+            assert math.isnan(got)
+        else:
+            assert got == val and math.copysign(1, got) == math.copysign(1, val)
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = orc.e4m3_decode(codes), _torch_e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.all(np.diff(ours[:127]) > 0)  # strictly increasing over 0x00..0x7e
+
+
+def test_e4m3_encode_vs_torch_sweep():
+    rng = np.random.default_rng(0)
+    # every bf16-representable value in [-448, 448], random fp32 in several scales,
+    # and the exact midpoints between neighbouring codes (ties go to even codes)
+    bf = (np.arange(0, 1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    bf = bf[np.isfinite(bf) & (np.abs(bf) <= 448)]
+    rnd = np.concatenate([rng.standard_normal(200000) * s for s in (1e-3, 0.05, 1, 30, 200)])
+    vals = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([bf, rnd.astype(np.float32), mids, -mids]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3_encode(x))
+    # ties: midpoint between codes c and c+1 rounds to the even code
+    mc = orc.e4m3_encode(mids.astype(np.float32))
+    assert np.all(mc % 2 == 0)
+
+
+def test_e4m3_encode_saturates_and_keeps_sign():
+    out = orc.e4m3_encode(np.array([448, 449, 470, 1e6, -1e6, -0.0, -1e-9, 1e-9], np.float32))
+    assert list(out) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x80, 0x00]
+
+
+def test_byte_is_about_8log2_plus_56():
+    """The page's reading of an E4M3 byte as 8*log2(v)+56 holds within 0.7 over
+    every positive normal code (and exactly on powers of two); a decoder with the
+    wrong exponent bias is off by a multiple of 8."""
+    facts, _ = _page_facts()
+    codes = np.arange(8, 127, dtype=np.uint8)
+    v = orc.e4m3_decode(codes)
+    dev = codes - (facts["expcast_slope"] * np.log2(v) + facts["expcast_offset"])
+    assert np.max(np.abs(dev)) < 0.7
+    pw = codes[codes % 8 == 0]
+    assert np.all(pw == facts["expcast_slope"] * np.log2(orc.e4m3_decode(pw)) + facts["expcast_offset"])
+
+
+# --------------------------------------------------------------------------- ExpCast
+
+@pytest.mark.parametrize("k", [0, 8])
+def test_expcast_within_one_code_of_rne_exp2(k):
+    """code = rne(8*u + 56 + 8k) for u = log2(p); over the normal range of E4M3 it
+    is within one code of the round-to-nearest E4M3 encoding of p*2^k; below it
+    (the subnormal band) the value error stays under 2^-6 in the shifted domain."""
+    u = np.linspace(-25.0, 0.0, 400001).astype(np.float32)  # log2 of the probability
+    s_raw = (u * np.float32(8.0)).astype(np.float32)  # alpha = 1: raw score in code units
+    bias = np.float32(56 + 8 * k)
+    codes = orc.expcast(s_raw, 1.0, float(bias))  # row maximum M = 0
+    target = np.exp2(u.astype(np.float64) + k)
+    rne = _torch_e4m3_encode(target)
+    normal = target >= 2.0 ** -6
+    assert np.max(np.abs(codes[normal].astype(int) - rne[normal].astype(int))) <= 1
+    val = orc.e4m3_decode(codes)
+    assert np.max(np.abs(val[~normal] - target[~normal])) <= 2.0 ** -6
+    assert np.all(np.diff(codes.astype(int)) >= 0)  # monotone in the score
+    assert codes[-1] == 56 + 8 * k  # p = 1 maps to 56 + 8k
+
+
+def test_expcast_clamps():
+    c = orc.expcast(np.array([-np.inf, -1e30, 1e30, 0.4, 0.5, 1.5, 2.5], np.float32), 1.0, 0.0)
+    assert list(c) == [0, 0, 126, 0, 0, 2, 2]  # rne: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2
+
+
+# --------------------------------------------------------------------------- generator
+
+def test_splitmix64_reference_value_and_counter_form():
+    # first output for state 0 of Vigna's reference splitmix64
+    assert int(orc.splitmix64(0, 1)[0]) == 0xE220A8397B1DCDAF
+    seq = orc.splitmix64(12345, 1000)
+    assert np.array_equal(seq, inputs.stream(12345, 1000))
+
+
+def test_kmeans_init_indices_distinct():
+    for N, C_ in [(10, 3), (1024, 8), (16544, 32), (75600, 64)]:
+        idx = orc.kmeans_init_indices(0, 5, N, C_)
+        assert len(set(idx.tolist())) == C_ and idx.min() >= 0 and idx.max() < N
+
+
+# --------------------------------------------------------------------------- k-means
+
+def _lloyd_fp64(v, init_idx, T):
+    cent = v[init_idx].astype(np.float64)
+    lab = None
+    for _ in range(T):
+        d2 = ((v[:, None, :] - cent[None, :, :]) ** 2).sum(-1)
+        lab = np.argmin(d2, axis=1)
+        srt = np.sort(d2, axis=1)
+        margin = (srt[:, 1] - srt[:, 0]).min() if d2.shape[1] > 1 else np.inf
+        for kk in range(cent.shape[0]):
+            if np.any(lab == kk):
+                cent[kk] = v[lab == kk].mean(0)
+        if margin < 1e-3:
+            return None, None
+    return lab, cent
+
+
+def test_kmeans_tiny_brute_force():
+    """Labels of the oracle's fp32 Lloyd equal an independent fp64 Lloyd from the
+    same initial indices on tiny inputs without near ties."""
+    checked = 0
+    for seed in range(40):
+        N = 4 + seed % 7
+        C_ = 1 + seed % 3
+        T = 1 + seed % 3
+        q, k, v = inputs.make_custom(1, 1, N, seed=seed, rate=0.0)
+        P = orc.make_params(1, 1, N, C_=C_, T=T, seed=seed, rho=0.0)
+        pr = orc.prepare(P, q, k, v)
+        vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+        lab, cent = _lloyd_fp64(vf, orc.kmeans_init_indices(seed, 0, N, C_), T)
+        if lab is None:
+            continue
+        checked += 1
+        assert np.array_equal(pr["labels"][0], lab)
+        np.testing.assert_allclose(pr["centroids"][0], cent, rtol=1e-6, atol=1e-6)
+    assert checked >= 25
+
+
+def test_kmeans_recovers_planted_blobs():
+    rng = np.random.default_rng(3)
+    N, C_ = 600, 4
+    centers = rng.standard_normal((C_, 128)) * 6.0
+    truth = rng.integers(0, C_, N)
+    v = centers[truth] + 0.3 * rng.standard_normal((N, 128))
+    vb = inputs.to_bf16_bits(v)[None, None]
+    z = np.zeros_like(vb)
+    # Forgy init may put two seeds in one blob; enough rounds and a seed that
+    # draws one per blob make the recovery exact
+    for seed in range(20):
+        init = orc.kmeans_init_indices(seed, 0, N, C_)
+        if len(set(truth[init].tolist())) == C_:
+            break
+    P = orc.make_params(1, 1, N, C_=C_, T=5, seed=seed, rho=0.0)
+    lab = orc.prepare(P, z, z, vb)["labels"][0]
+    # identical partition up to relabelling
+    pairs = set(zip(truth.tolist(), lab.tolist()))
+    assert len(pairs) == C_ and len({a for a, _ in pairs}) == C_ and len({b for _, b in pairs}) == C_
+
+
+def test_kmeans_sse_non_increasing():
+    q, k, v = inputs.make_custom(1, 1, 700, seed=7)
+    vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+    sse = []
+    for T in range(1, 8):
+        P = orc.make_params(1, 1, 700, C_=6, T=T, seed=1, rho=0.0)
+        pr = orc.prepare(P, q, k, v)
+        cent = pr["centroids"][0].astype(np.float64)
+        sse.append(((vf - cent[pr["labels"][0]]) ** 2).sum())
+    assert all(b <= a * (1 + 1e-6) for a, b in zip(sse, sse[1:]))
+
+
+# --------------------------------------------------------------------------- prepare
+
+@pytest.fixture(scope="module")
+def ragged():
+    """Two heads, N = 300 (two full blocks and a 44-token tail), outliers."""
+    B, H, N = 1, 2, 300
+    q, k, v = inputs.make_custom(B, H, N, seed=11, rate=0.03, sigma=25.0, vmean=0.3)
+    P = orc.make_params(B, H, N, C_=5, T=6, seed=2, rho=0.05)
+    return P, q, k, v, orc.prepare(P, q, k, v)
+
+
+def test_permutation_is_stable_sort_by_label(ragged):
+    P, q, k, v, pr = ragged
+    for s in range(2):
+        lab, perm, iperm = pr["labels"][s], pr["perm"][s], pr["iperm"][s]
+        assert np.array_equal(perm, np.argsort(lab, kind="stable"))
+        assert np.array_equal(iperm[perm], np.arange(P.N))
+
+
+def test_k_smoothing_and_qk_codes(ragged):
+    P, q, k, v, pr = ragged
+    N = P.N
+    for s in range(2):
+        kf = inputs.bf16_bits_to_f32(k[0, s]).astype(np.float64)
+        qf = inputs.bf16_bits_to_f32(q[0, s]).astype(np.float64)
+        # fixed-point grid (2^-25 per term) plus one fp32 rounding of the mean
+        km = kf.mean(0)
+        assert np.all(np.abs(pr["kbar"][s] - km) <= np.abs(km) * 2.0 ** -24 + 2.0 ** -24)
+        perm = pr["perm"][s]
+        kt = (kf - pr["kbar"][s].astype(np.float64))[perm]
+        qt = qf[perm]
+        for name, x, sc in (("k8", kt, pr["sk"][s]), ("q8", qt, pr["sq"][s])):
+            codes = pr[name][s]
+            assert np.all(codes[N:] == 0)
+            for b in range((N + 127) // 128):
+                blk = x[b * 128:min(N, b * 128 + 128)]
+                amax = np.abs(blk).max()
+                assert abs(sc[b] - amax / 448) <= 1e-6 * amax / 448
+                deq = orc.e4m3_decode(codes[b * 128:b * 128 + len(blk)]) * sc[b]
+                # half an E4M3 ulp in the normal range, 2^-10 (code units) below it
+                bound = np.abs(blk) * 2.0 ** -4 * 1.0001 + sc[b] * 2.0 ** -10 + 1e-7 * amax
+                assert np.all(np.abs(deq - blk) <= bound)
+                assert np.abs(orc.e4m3_decode(codes[b * 128:b * 128 + len(blk)])).max() == 448
+
+
+def test_v_demean_residual_codes(ragged):
+    P, q, k, v, pr = ragged
+    N = P.N
+    for s in range(2):
+        vf = inputs.bf16_bits_to_f32(v[0, s]).astype(np.float64)[pr["perm"][s]]
+        mu, sv = pr["mu"][s].astype(np.float64), pr["sv"][s].astype(np.float64)
+        for b in range((N + 127) // 128):
+            blk = vf[b * 128:min(N, b * 128 + 128)]
+            bm = blk.mean(0)
+            assert np.all(np.abs(mu[b] - bm) <= np.abs(bm) * 2.0 ** -24 + 2.0 ** -24)
+            deq = mu[b] + sv * orc.e4m3_decode(pr["v8"][s][b * 128:b * 128 + len(blk)])
+            bound = np.abs(blk - mu[b]) * 2.0 ** -4 * 1.001 + sv * 2.0 ** -10 + 1e-6
+            assert np.all(np.abs(deq - blk) <= bound)
+        resid = vf - mu[np.arange(N) // 128]
+        np.testing.assert_allclose(sv, np.abs(resid).max(0) / 448, rtol=1e-6)
+        np.testing.assert_allclose(pr["mup"][s], pr["mu"][s] * pr["inv"][s][None, :], rtol=1e-6)
+
+
+def test_demean_removes_more_energy_after_clustering():
+    """The pages report that block demeaning removes a larger share of block energy
+    once tokens are sorted by cluster than in sequence order."""
+    q, k, v = inputs.make_inputs(0)
+    P = orc.make_params(1, 2, 1024, C_=8)
+    pr = orc.prepare(P, q, k, v)
+    for s in range(2):
+        vf = inputs.bf16_bits_to_f32(v[0, s]).astype(np.float64)
+
+        def removed(x):
+            blocks = x.reshape(-1, 128, 128)
+            return 1 - ((blocks - blocks.mean(1, keepdims=True)) ** 2).sum() / (blocks ** 2).sum()
+
+        assert removed(vf[pr["perm"][s]]) > 2 * removed(vf)
+
+
+def test_repair_set_is_topm_of_error(ragged):
+    P, q, k, v, pr = ragged
+    m = pr["m"]
+    assert m == math.ceil(float(np.float32(P.rho)) * P.N)
+    for s in range(2):
+        err = pr["err"][s]
+        order = np.lexsort((np.arange(P.N), -err.astype(np.float64)))
+        assert np.array_equal(pr["rep_pos"][s][:m], np.sort(order[:m]))
+        # criterion recomputed in fp64 from the codes
+        vf = inputs.bf16_bits_to_f32(v[0, s]).astype(np.float64)[pr["perm"][s]]
+        x = (vf - pr["mu"][s].astype(np.float64)[np.arange(P.N) // 128]) * pr["inv"][s]
+        dl = x - orc.e4m3_decode(pr["v8"][s][:P.N])
+        e64 = ((pr["sv"][s] * dl) ** 2).sum(1)
+        np.testing.assert_allclose(err, e64, rtol=1e-4, atol=1e-12)
+        sel = pr["rep_pos"][s][:m]
+        d16 = inputs.bf16_bits_to_f32(pr["rep_delta"][s][:m]).astype(np.float64)
+        # bf16 rounding, plus fp32 rounding of x = (v - mu) * inv (|x| <= 448)
+        np.testing.assert_allclose(d16, dl[sel], rtol=2.0 ** -8, atol=448 * 2.0 ** -22)
+
+
+def test_repair_counts_match_page_budget():
+    facts, ms = _page_facts()
+    for N, m in ms.items():
+        P = orc.make_params(1, 1, N, rho=facts["rho"])
+        assert orc.repair_count(P) == m
+    assert orc.repair_count(orc.make_params(1, 1, 100, rho=0.0)) == 0
+    assert orc.repair_count(orc.make_params(1, 1, 100, rho=1.0)) == 100
+
+
+# --------------------------------------------------------------------------- forward
+
+def _sim(P, q, k, v, rows=None, pcodes=False):
+    pr = orc.prepare(P, q, k, v)
+    BH = P.B * P.H
+    rows = np.arange(P.N) if rows is None else np.asarray(rows)
+    slot = np.repeat(np.arange(BH), len(rows)).astype(np.int32)
+    idx = np.tile(rows, BH).astype(np.int32)
+    res = orc.forward_rows(P, pr, slot, idx, want_pcodes=pcodes)
+    return res, pr, slot, idx
+
+
+def _dequant_v(pr, s, N, with_repair=True):
+    """V in real units as the method represents it: sV * (mu' + code [+ delta]),
+    mu' being the fp32 block mean in V code units."""
+    mup = pr["mup"][s].astype(np.float64)[np.arange(N) // 128]
+    codes = orc.e4m3_decode(pr["v8"][s][:N])
+    if with_repair:
+        m = pr["m"]
+        codes[pr["rep_pos"][s][:m]] += inputs.bf16_bits_to_f32(pr["rep_delta"][s][:m])
+    return pr["sv"][s].astype(np.float64) * (mup + codes)
+
+
+@pytest.mark.parametrize("N", [300, 128, 1])
+def test_zero_query_gives_mean_of_dequantised_v(N):
+    """Q = 0 makes every score 0, so every code is 56+8k and the output is the plain
+    mean of the dequantised V (block means restored through the row sum, tail keys
+    excluded, repaired residuals included)."""
+    q, k, v = inputs.make_custom(1, 2, N, seed=5, rate=0.05, vmean=0.7)
+    q[:] = 0
+    P = orc.make_params(1, 2, N, C_=min(4, N), T=3, rho=0.05)
+    out, pr, slot, idx = _sim(P, q, k, v)
+    out = out.reshape(2, N, 128)
+    for s in range(2):
+        want = _dequant_v(pr, s, N).mean(0)
+        np.testing.assert_allclose(out[s], np.broadcast_to(want, (N, 128)), rtol=1e-12, atol=1e-12)
+        vf = inputs.bf16_bits_to_f32(v[0, s]).astype(np.float64)
+        assert np.abs(want - vf.mean(0)).max() < 0.02 * np.abs(vf).max()
+
+
+def test_constant_keys_are_smoothed_away():
+    """K rows all equal: the channel mean removes K entirely, so scores vanish and
+    the output is the mean of the dequantised V whatever Q is."""
+    N = 260
+    q, k, v = inputs.make_custom(1, 1, N, seed=9)
+    k[0, 0] = k[0, 0, 17][None, :]
+    P = orc.make_params(1, 1, N, C_=3, T=2, rho=0.01)
+    out, pr, _, _ = _sim(P, q, k, v)
+    assert np.all(pr["k8"][0] & 0x7F == 0)
+    np.testing.assert_allclose(out, np.broadcast_to(_dequant_v(pr, 0, N).mean(0), out.shape),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_row_max_code_is_bias():
+    q, k, v = inputs.make_custom(1, 1, 400, seed=4)
+    for tau, lo, hi in ((0.0, 120, 120), (6.0, 120, 126)):
+        P = orc.make_params(1, 1, 400, C_=4, T=2, tau=tau)
+        (out, pc), pr, _, _ = _sim(P, q, k, v, pcodes=True)
+        mx = pc[:, :400].max(1)
+        assert mx.min() >= lo and mx.max() <= hi
+        assert np.all(pc[:, 400:] == 0)
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+def test_simulation_tracks_exact_attention_with_uneven_block_scales():
+    """With V-Smooth off (identity order) and Q/K blocks scaled by very different
+    powers of two, a wrong block scale, a dropped rescale or restore, or a
+    transposed operand would move the output far from exact attention."""
+    B, H, N = 1, 2, 520
+    q, k, v = inputs.make_custom(B, H, N, seed=21, vmean=1.5)
+    qf = inputs.bf16_bits_to_f32(q).astype(np.float64)
+    kf = inputs.bf16_bits_to_f32(k).astype(np.float64)
+    blk = np.arange(N) // 128
+    # per-block Q and K magnitudes differ by up to 4x each (alpha by up to 16x
+    # between block pairs) while logits keep a std between 1/8 and 2
+    mq = 2.0 ** np.array([-1, 1, 0, 1, -1])[blk]
+    mk = 2.0 ** np.array([1, -1, 0, 1, -1])[blk]
+    q = inputs.to_bf16_bits(qf * mq[None, None, :, None] * 0.5)
+    k = inputs.to_bf16_bits(kf * mk[None, None, :, None] + 2.0)
+    for flags in (orc.REPAIR, orc.DEFAULT_FLAGS):
+        P = orc.make_params(B, H, N, C_=4, T=3, rho=0.01, flags=flags)
+        out, pr, slot, idx = _sim(P, q, k, v)
+        ex = orc.exact_rows(P, q, k, v, slot, idx)
+        assert _rel(out, ex) < 0.08
+
+
+def test_vsmooth_and_tau_variants_agree_with_exact():
+    q, k, v = inputs.make_inputs(0)
+    rows = np.arange(0, 1024, 3)
+    res = {}
+    for name, kw in dict(full={}, tau6=dict(tau=6.0), k0=dict(expcast_k=0),
+                         off=dict(flags=0), noq=dict(flags=orc.VSMOOTH | orc.REPAIR)).items():
+        P = orc.make_params(1, 2, 1024, C_=8, **kw)
+        out, pr, slot, idx = _sim(P, q, k, v, rows=rows)
+        res[name] = out
+    ex = orc.exact_rows(P, q, k, v, slot, idx)
+    for name, out in res.items():
+        assert _rel(out, ex) < 0.08, name
+    # tau only changes the P codes (same Q/K/V codes), so the two stay close
+    assert _rel(res["tau6"], res["full"]) < 0.03
+
+
+def test_repair_moves_output_toward_unquantised_v():
+    """Raising rho corrects more residual error: with rho = 1 the V used by the
+    simulation equals the bf16-rounded residual, so its distance to exact V-side
+    arithmetic shrinks."""
+    q, k, v = inputs.make_custom(1, 1, 384, seed=8, rate=0.05, sigma=40)
+    errs = []
+    for rho in (0.0, 0.05, 1.0):
+        P = orc.make_params(1, 1, 384, C_=4, T=3, rho=rho)
+        pr = orc.prepare(P, q, k, v)
+        vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)[pr["perm"][0]]
+        errs.append(np.linalg.norm(_dequant_v(pr, 0, 384) - vf))
+    assert errs[0] > errs[1] > errs[2] and errs[2] < 1e-2 * errs[0]
+
+
+# --------------------------------------------------------------------------- exact
+
+def test_exact_matches_torch_sdpa_fp64():
+    q, k, v = inputs.make_custom(1, 2, 150, seed=13)
+    P = orc.make_params(1, 2, 150)
+    slot = np.repeat([0, 1], 150)
+    idx = np.tile(np.arange(150), 2)
+    ours = orc.exact_rows(P, q, k, v, slot, idx).reshape(1, 2, 150, 128)
+    t = [torch.from_numpy(inputs.bf16_bits_to_f32(x).astype(np.float64)) for x in (q, k, v)]
+    # the oracle's scale is the fp32 parameter 1/sqrt(128) rounded to fp32
+    scale = float(np.float32(1.0 / math.sqrt(128)))
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, scale=scale).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_exact_invariant_to_joint_kv_permutation():
+    """Permuting K and V together leaves non-causal attention unchanged; permuting Q
+    as well permutes the output rows."""
+    q, k, v = inputs.make_custom(1, 1, 200, seed=17)
+    perm = np.random.default_rng(1).permutation(200)
+    P = orc.make_params(1, 1, 200)
+    rows = np.arange(200)
+    base = orc.exact_rows(P, q, k, v, np.zeros(200), rows)
+    kp, vp, qp = (np.ascontiguousarray(t[:, :, perm]) for t in (k, v, q))
+    np.testing.assert_allclose(orc.exact_rows(P, q, kp, vp, np.zeros(200), rows), base,
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(orc.exact_rows(P, qp, kp, vp, np.zeros(200), rows), base[perm],
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_demean_restore_identity_fp64():
+    """Restore identity stated by the pages: with block means removed from V and
+    added back through each block's row sum, attention is unchanged."""
+    rng = np.random.default_rng(2)
+    N, nb = 384, 3
+    s = rng.standard_normal((5, N))
+    v = rng.standard_normal((N, 128)) + 3
+    p = np.exp(s - s.max(1, keepdims=True))
+    ref = p @ v / p.sum(1, keepdims=True)
+    acc = np.zeros((5, 128))
+    for b in range(nb):
+        sl = slice(b * 128, b * 128 + 128)
+        mu = v[sl].mean(0)
+        acc += p[:, sl] @ (v[sl] - mu) + p[:, sl].sum(1, keepdims=True) * mu
+    np.testing.assert_allclose(acc / p.sum(1, keepdims=True), ref, rtol=1e-12)

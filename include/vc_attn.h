@@ -1,0 +1,159 @@
+/*
+ * vc_attn.h -- C ABI of the VC-Attention FP8 library for AMD Instinct MI355X (gfx950).
+ *
+ * VC-Attention is training-free low-bit non-causal self-attention for image and
+ * video diffusion transformers.  It is described by the articles
+ *   "VC-Attention acelera atencao em modelos de video de IA em ate 3,58x sem
+ *    retreinamento" (noticiai.com.br), sections "V-Smooth: corrigindo outliers de
+ *    valor" (Group / Demean / Restore) and "ExpCast-FP8: eliminando o gargalo do
+ *    softmax" (an E4M3 byte read as an integer is about 8*log2(v)+56, written by
+ *    one fused multiply-add from the log-domain score), and
+ *   "VC-Attention et FLUX 3 accelerent la generation d'images sur Blackwell"
+ *    (ip73.fr), introduction (block scales are fixed by the block maximum) and
+ *    section "Le compromis entre vitesse et fidelite" (repair budget rho: the
+ *    fraction of tokens with the largest quantisation error gets its residual
+ *    corrected; rho = 0.005).
+ *
+ * The work is split in two calls on the caller's HIP stream:
+ *   vc_attn_prepare  K smoothing and per-block Q/K E4M3 codes; V-Smooth (k-means
+ *                    over value tokens per (batch, head), joint permutation,
+ *                    128-token block demeaning, per-channel E4M3 residual codes);
+ *                    selection of the repaired tokens.
+ *   vc_attn_forward  one fused kernel: QK^T on FP8 MFMA, online row maximum and
+ *                    row sum, ExpCast P bytes, PV on FP8 MFMA, restore of the
+ *                    block means through the row sum, repair of the selected
+ *                    tokens, normalisation and un-permutation of the output.
+ *
+ * Tensors.  Q, K, V are bf16, contiguous [B][H][N][d] with d = 128, device memory,
+ * 16-byte aligned.  O is bf16 [B][H][N][d] in the ORIGINAL token order.
+ *
+ * Ownership.  The caller allocates Q, K, V, O and the workspace on the device and
+ * keeps them alive until the stream has finished the calls.  The library never
+ * allocates or frees device memory and never synchronises the stream, except
+ * vc_attn_prepare with VC_REUSE_CLUSTERS, which reads 64 bytes of the workspace
+ * header back to the host (one stream synchronisation) to check that clusters
+ * exist for the same shape.  The library has no global mutable state; calls on
+ * different streams with different workspaces may run concurrently.  Two calls
+ * that share a workspace must be ordered by the caller.
+ *
+ * Errors.  Every entry point checks its arguments before touching the device and
+ * returns a vc_status; nothing is launched when the status is not VC_OK.  A HIP
+ * launch failure returns VC_ERR_HIP (work launched earlier in the same call may
+ * have run).  Inputs must be finite with |x| < 2^22 (the fixed-point means are
+ * exact under that bound); this is not checked.
+ */
+#ifndef VC_ATTN_H
+#define VC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VC_OK = 0,
+  VC_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, out-of-range parameter */
+  VC_ERR_UNSUPPORTED = 2,  /* d != 128 or block != 128 */
+  VC_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
+  VC_ERR_NOT_PREPARED = 4, /* VC_REUSE_CLUSTERS without clusters for this shape */
+  VC_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
+  VC_ERR_INTERNAL = 6
+} vc_status;
+
+/* Flags (vc_attn_params.flags). */
+enum {
+  VC_VSMOOTH = 1u,       /* V-Smooth: cluster, permute, demean (else identity, no mean) */
+  VC_REPAIR = 2u,        /* correct the ceil(rho*N) worst-quantised value tokens */
+  VC_PERMUTE_Q = 4u,     /* queries follow the cluster permutation too (output is
+                            scattered back to original order either way) */
+  VC_REUSE_CLUSTERS = 8u /* prepare skips k-means and reuses labels/permutation
+                            already in the workspace (clustering runs only in the
+                            early denoising steps, as the V-Smooth section says) */
+};
+
+typedef struct {
+  int32_t B, H, N;       /* batch, heads, tokens; B*H >= 1, 1 <= N <= 2^20 */
+  int32_t d;             /* head dimension, must be 128 */
+  int32_t block;         /* quantisation block in tokens, must be 128 */
+  int32_t n_clusters;    /* k-means clusters C, 1 <= C <= min(N, 64) */
+  int32_t kmeans_iters;  /* Lloyd iterations T, 1 <= T <= 1000 */
+  int32_t expcast_k;     /* ExpCast bias is 56 + 8k, 0 <= k <= 8 */
+  uint64_t seed;         /* k-means initialisation seed */
+  float rho;             /* repair budget, 0 <= rho <= 1 */
+  float sm_scale;        /* softmax scale; <= 0 means 1/sqrt(d) */
+  float tau;             /* row-maximum slack in code units: the maximum moves only
+                            when a block maximum exceeds it by more than tau;
+                            0 <= tau and 56 + 8k + tau <= 126 */
+  uint32_t flags;        /* VC_* flags */
+} vc_attn_params;
+
+/* Byte offsets (from the workspace base) of the arrays prepare writes.  Each is
+ * 256-byte aligned.  nblk = ceil(N/128), Npad = 128*nblk, BH = B*H,
+ * m = ceil(rho*N) (0 without VC_REPAIR), mpad = 128*ceil(m/128). */
+typedef struct {
+  size_t total;      /* workspace bytes required                                 */
+  size_t header;     /* 256 B: magic, shape, state                               */
+  size_t kbar;       /* f32 [BH][128] channel mean of K                          */
+  size_t ksum;       /* i64 [BH][nkc][128] fixed-point partial sums of K         */
+  size_t init_idx;   /* i32 [BH][C] k-means initial token indices                */
+  size_t centroids;  /* f32 [BH][C][128]                                         */
+  size_t labels;     /* i32 [BH][N] cluster of each original token               */
+  size_t perm;       /* i32 [BH][N] position -> original token                   */
+  size_t iperm;      /* i32 [BH][N] original token -> position                   */
+  size_t q8;         /* u8  [BH][Npad][128] Q codes, position order               */
+  size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order      */
+  size_t sq;         /* f32 [BH][nblk] Q block scales                            */
+  size_t sk;         /* f32 [BH][nblk] K block scales                            */
+  size_t mu;         /* f32 [BH][nblk][128] V block means (real units)           */
+  size_t bamax;      /* f32 [BH][nblk][128] block maxima of |V - mu|             */
+  size_t mup;        /* f32 [BH][nblk][128] block means in V code units          */
+  size_t sv;         /* f32 [BH][128] per-channel V residual scale               */
+  size_t inv;        /* f32 [BH][128] its inverse                                */
+  size_t v8t;        /* u8  [BH][128][Npad] residual codes, channel-major; inside
+                        each 128-key block key 16t+4g+v sits at column 32g+4t+v  */
+  size_t err;        /* f32 [BH][N] repair criterion per position                */
+  size_t rep_pos;    /* i32 [BH][mpad] repaired positions ascending, padded with -1 */
+  size_t rep_dt;     /* bf16 [BH][128][mpad] residual error of the repaired tokens
+                        in V code units, channel-major; inside each 128-slot group
+                        slot 32u+16t'+4g+v sits at column 32u+8g+4t'+v           */
+} vc_attn_ws_layout;
+
+/* Fill *p with the defaults: d = block = 128, C = 16, T = 10, k = 8, seed 0,
+ * rho = 0.005, sm_scale 0 (1/sqrt(d)), tau = 0, flags VSMOOTH|REPAIR|PERMUTE_Q.
+ * B, H, N are set to 0 and must be filled in. */
+void vc_attn_default_params(vc_attn_params* p);
+
+/* Required workspace size in bytes, or 0 when the parameters are invalid. */
+size_t vc_attn_workspace_size(const vc_attn_params* p);
+
+/* Workspace layout for these parameters (host only, no device access). */
+vc_status vc_attn_workspace_layout(const vc_attn_params* p, vc_attn_ws_layout* out);
+
+/* Checks the parameters without touching the device. */
+vc_status vc_attn_check_params(const vc_attn_params* p);
+
+/* Prepare stage (see above).  q, k, v: device bf16 [B][H][N][128].  workspace:
+ * device buffer of ws_bytes >= vc_attn_workspace_size(p), 256-byte aligned.
+ * stream: a hipStream_t (NULL = default stream).  Asynchronous. */
+vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
+                          const void* v, void* workspace, size_t ws_bytes, void* stream);
+
+/* Forward stage: reads the prepared workspace and writes o (device bf16
+ * [B][H][N][128], original token order).  p must equal the parameters of the
+ * prepare call that filled the workspace.  Asynchronous. */
+vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
+                          void* o, void* stream);
+
+/* Static description of a status code. */
+const char* vc_attn_status_string(vc_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t vc_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VC_ATTN_H */

@@ -1,0 +1,242 @@
+// Host side of the VC-Attention FP8 C ABI: argument checks, workspace layout,
+// and the two stream-ordered entry points.  No device allocation, no global state.
+#include <cmath>
+#include <cstring>
+
+#include "vc_internal.h"
+
+namespace vc {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static int32_t repair_count(const vc_attn_params* p) {
+  if (!(p->flags & VC_REPAIR) || !(p->rho > 0.0f)) return 0;
+  double m = std::ceil((double)p->rho * (double)p->N);
+  if (m > p->N) m = p->N;
+  return (int32_t)m;
+}
+
+static vc_status check(const vc_attn_params* p) {
+  if (!p) return VC_ERR_INVALID_ARG;
+  if (p->d != D || p->block != BLK) return VC_ERR_UNSUPPORTED;
+  if (p->B < 1 || p->H < 1 || p->N < 1 || p->N > (1 << 20)) return VC_ERR_INVALID_ARG;
+  if ((int64_t)p->B * p->H > (1 << 24)) return VC_ERR_INVALID_ARG;
+  if (p->n_clusters < 1 || p->n_clusters > MAX_CLUSTERS || p->n_clusters > p->N) return VC_ERR_INVALID_ARG;
+  if (p->kmeans_iters < 1 || p->kmeans_iters > 1000) return VC_ERR_INVALID_ARG;
+  if (p->expcast_k < 0 || p->expcast_k > 8) return VC_ERR_INVALID_ARG;
+  if (!(p->rho >= 0.0f && p->rho <= 1.0f)) return VC_ERR_INVALID_ARG;  // also rejects NaN
+  if (!std::isfinite(p->sm_scale)) return VC_ERR_INVALID_ARG;
+  if (!(p->tau >= 0.0f) || 56.0f + 8.0f * p->expcast_k + p->tau > 126.0f) return VC_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS))
+    return VC_ERR_INVALID_ARG;
+  return VC_OK;
+}
+
+bool shape_of(const vc_attn_params* p, Shape* s) {
+  if (check(p) != VC_OK) return false;
+  s->B = p->B;
+  s->H = p->H;
+  s->N = p->N;
+  s->BH = p->B * p->H;
+  s->nblk = (p->N + BLK - 1) / BLK;
+  s->Npad = s->nblk * BLK;
+  s->C = p->n_clusters;
+  s->T = p->kmeans_iters;
+  s->m = repair_count(p);
+  s->mpad = ((s->m + BLK - 1) / BLK) * BLK;
+  s->nkc = (p->N + KSUM_CHUNK - 1) / KSUM_CHUNK;
+  s->nkm = (p->N + KM_CHUNK - 1) / KM_CHUNK;
+  return true;
+}
+
+void layout_of(const Shape& s, FullLayout* out) {
+  const size_t BH = (size_t)s.BH, N = (size_t)s.N, Np = (size_t)s.Npad, nb = (size_t)s.nblk;
+  const size_t C = (size_t)s.C;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  vc_attn_ws_layout& L = out->pub;
+  L.header = take(sizeof(Header));
+  L.kbar = take(BH * D * 4);
+  L.ksum = take(BH * (size_t)s.nkc * D * 8);
+  L.init_idx = take(BH * C * 4);
+  L.centroids = take(BH * C * D * 4);
+  out->kmpart = take(BH * (size_t)s.nkm * C * D * 8);
+  out->kmcnt = take(BH * (size_t)s.nkm * C * 4);
+  L.labels = take(BH * N * 4);
+  L.perm = take(BH * N * 4);
+  L.iperm = take(BH * N * 4);
+  L.q8 = take(BH * Np * D);
+  L.k8 = take(BH * Np * D);
+  L.sq = take(BH * nb * 4);
+  L.sk = take(BH * nb * 4);
+  L.mu = take(BH * nb * D * 4);
+  L.bamax = take(BH * nb * D * 4);
+  L.mup = take(BH * nb * D * 4);
+  L.sv = take(BH * D * 4);
+  L.inv = take(BH * D * 4);
+  L.v8t = take(BH * D * Np);
+  L.err = take(BH * N * 4);
+  L.rep_pos = take(BH * (size_t)s.mpad * 4);
+  L.rep_dt = take(BH * D * (size_t)s.mpad * 2);
+  L.total = off;
+}
+
+Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, void* ws) {
+  const vc_attn_ws_layout& L = FL.pub;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = s.B;
+  a.H = s.H;
+  a.N = s.N;
+  a.BH = s.BH;
+  a.nblk = s.nblk;
+  a.Npad = s.Npad;
+  a.C = s.C;
+  a.T = s.T;
+  a.m = s.m;
+  a.mpad = s.mpad;
+  a.nkc = s.nkc;
+  a.nkm = s.nkm;
+  a.flags = p->flags;
+  a.seed = p->seed;
+  const float scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)D));
+  a.c0 = (float)(8.0 * 1.4426950408889634074 * (double)scale);
+  a.bias = (float)(56 + 8 * p->expcast_k);
+  a.tau = p->tau;
+  a.header = reinterpret_cast<Header*>(b + L.header);
+  a.kbar = reinterpret_cast<float*>(b + L.kbar);
+  a.ksum = reinterpret_cast<long long*>(b + L.ksum);
+  a.init_idx = reinterpret_cast<int*>(b + L.init_idx);
+  a.cent = reinterpret_cast<float*>(b + L.centroids);
+  a.kmpart = reinterpret_cast<long long*>(b + FL.kmpart);
+  a.kmcnt = reinterpret_cast<int*>(b + FL.kmcnt);
+  a.labels = reinterpret_cast<int*>(b + L.labels);
+  a.perm = reinterpret_cast<int*>(b + L.perm);
+  a.iperm = reinterpret_cast<int*>(b + L.iperm);
+  a.q8 = b + L.q8;
+  a.k8 = b + L.k8;
+  a.sq = reinterpret_cast<float*>(b + L.sq);
+  a.sk = reinterpret_cast<float*>(b + L.sk);
+  a.mu = reinterpret_cast<float*>(b + L.mu);
+  a.bamax = reinterpret_cast<float*>(b + L.bamax);
+  a.mup = reinterpret_cast<float*>(b + L.mup);
+  a.sv = reinterpret_cast<float*>(b + L.sv);
+  a.inv = reinterpret_cast<float*>(b + L.inv);
+  a.v8t = b + L.v8t;
+  a.err = reinterpret_cast<float*>(b + L.err);
+  a.rep_pos = reinterpret_cast<int*>(b + L.rep_pos);
+  a.rep_dt = reinterpret_cast<uint16_t*>(b + L.rep_dt);
+  return a;
+}
+
+static bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" {
+
+void vc_attn_default_params(vc_attn_params* p) {
+  if (!p) return;
+  std::memset(p, 0, sizeof(*p));
+  p->d = D;
+  p->block = BLK;
+  p->n_clusters = 16;
+  p->kmeans_iters = 10;
+  p->expcast_k = 8;
+  p->seed = 0;
+  p->rho = 0.005f;
+  p->sm_scale = 0.0f;
+  p->tau = 0.0f;
+  p->flags = VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q;
+}
+
+vc_status vc_attn_check_params(const vc_attn_params* p) { return check(p); }
+
+size_t vc_attn_workspace_size(const vc_attn_params* p) {
+  Shape s;
+  if (!shape_of(p, &s)) return 0;
+  FullLayout L;
+  layout_of(s, &L);
+  return L.pub.total;
+}
+
+vc_status vc_attn_workspace_layout(const vc_attn_params* p, vc_attn_ws_layout* out) {
+  if (!out) return VC_ERR_INVALID_ARG;
+  const vc_status st = check(p);
+  if (st != VC_OK) return st;
+  Shape s;
+  shape_of(p, &s);
+  FullLayout L;
+  layout_of(s, &L);
+  *out = L.pub;
+  return VC_OK;
+}
+
+vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k, const void* v,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  const vc_status st = check(p);
+  if (st != VC_OK) return st;
+  if (!q || !k || !v || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return VC_ERR_INVALID_ARG;
+  Shape s;
+  shape_of(p, &s);
+  FullLayout L;
+  layout_of(s, &L);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.pub.total) return VC_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool vs = (p->flags & VC_VSMOOTH) != 0;
+  const bool reuse = vs && (p->flags & VC_REUSE_CLUSTERS);
+  if (reuse) {
+    Header h;
+    if (hipMemcpyAsync(&h, static_cast<uint8_t*>(workspace) + L.pub.header, sizeof(h),
+                       hipMemcpyDeviceToHost, hs) != hipSuccess)
+      return VC_ERR_HIP;
+    if (hipStreamSynchronize(hs) != hipSuccess) return VC_ERR_HIP;
+    if (h.magic != MAGIC || h.clustered != 1u || h.B != p->B || h.H != p->H || h.N != p->N ||
+        h.C != p->n_clusters)
+      return VC_ERR_NOT_PREPARED;
+  }
+  Args a = make_args(p, s, L, workspace);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  return launch_prepare(a, !reuse, hs) == hipSuccess ? VC_OK : VC_ERR_HIP;
+}
+
+vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t ws_bytes, void* o,
+                          void* stream) {
+  const vc_status st = check(p);
+  if (st != VC_OK) return st;
+  if (!o || !aligned(o, 16)) return VC_ERR_INVALID_ARG;
+  Shape s;
+  shape_of(p, &s);
+  FullLayout L;
+  layout_of(s, &L);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.pub.total) return VC_ERR_WORKSPACE;
+  Args a = make_args(p, s, L, const_cast<void*>(workspace));
+  a.o = static_cast<uint16_t*>(o);
+  return launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? VC_OK : VC_ERR_HIP;
+}
+
+const char* vc_attn_status_string(vc_status s) {
+  switch (s) {
+    case VC_OK: return "ok";
+    case VC_ERR_INVALID_ARG: return "invalid argument";
+    case VC_ERR_UNSUPPORTED: return "unsupported shape (d and block must be 128)";
+    case VC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case VC_ERR_NOT_PREPARED: return "no clusters in the workspace for this shape";
+    case VC_ERR_HIP: return "HIP runtime error";
+    case VC_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+int32_t vc_attn_version(void) { return 100; }
+
+}  // extern "C"

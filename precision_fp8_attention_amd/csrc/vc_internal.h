@@ -1,0 +1,83 @@
+// Internal declarations of the VC-Attention FP8 library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "vc_attn.h"
+
+namespace vc {
+
+constexpr int D = 128;              // head dimension
+constexpr int BLK = 128;            // quantisation block (tokens)
+constexpr int KSUM_CHUNK = 512;     // tokens per partial K-sum workgroup
+constexpr int KM_CHUNK = 1024;      // tokens per k-means assignment workgroup
+constexpr int MAX_CLUSTERS = 64;    // centroids and bins live in LDS
+constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
+
+// Shape derived from the public parameters.
+struct Shape {
+  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm;
+};
+
+// Workspace header (first 256 bytes of the workspace).
+struct Header {
+  uint32_t magic;
+  uint32_t clustered;  // labels/perm/centroids valid for (B, H, N, C)
+  int32_t B, H, N, C;
+  uint32_t pad[58];
+};
+
+// Everything a kernel needs, passed by value.
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm;
+  uint32_t flags;
+  uint64_t seed;
+  float c0;    // 8*log2(e)*softmax scale, fp32
+  float bias;  // 56 + 8k
+  float tau;
+  Header* header;
+  float* kbar;
+  long long* ksum;
+  int* init_idx;
+  float* cent;
+  long long* kmpart;  // [BH][nkm][C][128] fixed-point partial sums of members
+  int* kmcnt;         // [BH][nkm][C] member counts
+  int* labels;
+  int* perm;
+  int* iperm;
+  uint8_t* q8;
+  uint8_t* k8;
+  float* sq;
+  float* sk;
+  float* mu;
+  float* bamax;
+  float* mup;
+  float* sv;
+  float* inv;
+  uint8_t* v8t;
+  float* err;
+  int* rep_pos;
+  uint16_t* rep_dt;
+};
+
+// Private extension of the public layout (partial k-means sums).
+struct FullLayout {
+  vc_attn_ws_layout pub;
+  size_t kmpart, kmcnt;
+};
+
+bool shape_of(const vc_attn_params* p, Shape* s);
+void layout_of(const Shape& s, FullLayout* out);
+Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& L, void* ws);
+
+hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st);
+hipError_t launch_forward(const Args& a, hipStream_t st);
+
+}  // namespace vc

@@ -1,0 +1,633 @@
+// Prepare-stage kernels of VC-Attention FP8 for gfx950.
+//
+// Method (articles on VC-Attention: noticiai.com.br, sections "Por que a atencao
+// e o gargalo" and "V-Smooth: corrigindo outliers de valor"; ip73.fr,
+// introduction and section "Le compromis entre vitesse et fidelite"):
+//   K smoothing     subtract the channel mean of K (softmax ignores it);
+//   Q/K codes       one E4M3 scale per 128-token block, set by the block maximum;
+//   Group           k-means over value tokens per (batch, head), then K and V (and
+//                   Q) are permuted jointly so that clusters are contiguous;
+//   Demean          each 128-position block subtracts its own mean, and only the
+//                   residual is quantised, E4M3 with one scale per channel;
+//   repair set      the ceil(rho*N) positions whose value codes lose the most.
+//
+// Every decision that yields an integer (cluster id, E4M3 code, selected token)
+// is taken in fixed-order fp32 (explicit fma) or in exact integer arithmetic, so
+// that the result does not depend on the order in which threads run: means are
+// exact int64 sums of values rounded to a 2^-24 grid, divided once in fp64.
+// The library is built with -ffp-contract=off.
+#include "vc_internal.h"
+
+namespace vc {
+namespace {
+
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float((h & 0xffffu) << 16); }
+
+__device__ __forceinline__ long long fx24(float x) {
+  return (long long)__builtin_rintf(x * 16777216.0f);
+}
+
+__device__ __forceinline__ float fixed_mean(long long s, long long n) {
+  return (float)(((double)s * 0x1p-24) / (double)n);
+}
+
+// Two fp32 -> two OCP E4M3 bytes (round to nearest even) in bits 0..15.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+__device__ __forceinline__ float e4m3_val(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+__device__ __forceinline__ void scale_from_amax(float amax, float* s, float* inv) {
+  if (amax < 0x1p-100f) {
+    *s = 1.0f;
+    *inv = 1.0f;
+  } else {
+    *s = amax / 448.0f;
+    *inv = 448.0f / amax;
+  }
+}
+
+__device__ __forceinline__ uint16_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint64_t splitmix(uint64_t& st) {
+  uint64_t z = (st += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Column of key r inside a 128-key block of the channel-major V codes: the fused
+// kernel's accumulator layout gives lane group g the keys 16t+4g+v (t = 0..7,
+// v = 0..3) and the PV operand wants them as 32 consecutive bytes.
+__device__ __forceinline__ int v_col(int r) { return 32 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
+
+// Column of repair slot s inside a 128-slot group of the repair residuals (bf16
+// MFMA operand with 32-wide K chunks): slot 32u+16t'+4g+v -> column 32u+8g+4t'+v.
+__device__ __forceinline__ int rep_col(int s) {
+  const int u = s >> 5, tp = (s >> 4) & 1, g = (s >> 2) & 3, v = s & 3;
+  return 32 * u + 8 * g + 4 * tp + v;
+}
+
+// ---------------------------------------------------------------------------
+// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens.
+// grid (nkc, BH), 256 threads: thread = (row r = t/16, 8-channel group t%16).
+__global__ __launch_bounds__(256) void k_ksum(Args a) {
+  __shared__ long long red[16][D];
+  const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
+  const int cg = t & 15, r = t >> 4;
+  const int j0 = ch * KSUM_CHUNK, j1 = min(j0 + KSUM_CHUNK, a.N);
+  const uint16_t* kh = a.k + (size_t)bh * a.N * D;
+  long long s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0;
+  for (int j = j0 + r; j < j1; j += 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(kh + (size_t)j * D + cg * 8);
+    s[0] += fx24(bf2f(u.x));
+    s[1] += fx24(bf2f(u.x >> 16));
+    s[2] += fx24(bf2f(u.y));
+    s[3] += fx24(bf2f(u.y >> 16));
+    s[4] += fx24(bf2f(u.z));
+    s[5] += fx24(bf2f(u.z >> 16));
+    s[6] += fx24(bf2f(u.w));
+    s[7] += fx24(bf2f(u.w >> 16));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = s[i];
+  __syncthreads();
+  if (t < D) {
+    long long tot = 0;
+    for (int rr = 0; rr < 16; ++rr) tot += red[rr][t];
+    a.ksum[((size_t)bh * a.nkc + ch) * D + t] = tot;
+  }
+}
+
+// K channel mean.  grid BH, 128 threads.
+__global__ __launch_bounds__(128) void k_kbar(Args a) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  long long tot = 0;
+  for (int ch = 0; ch < a.nkc; ++ch) tot += a.ksum[((size_t)bh * a.nkc + ch) * D + c];
+  a.kbar[(size_t)bh * D + c] = fixed_mean(tot, a.N);
+}
+
+// ---------------------------------------------------------------------------
+// k-means initialisation (Forgy): seeded partial Fisher-Yates over [0, N).
+// grid BH, 128 threads.
+__global__ __launch_bounds__(128) void k_km_init(Args a) {
+  __shared__ int key[2 * MAX_CLUSTERS], val[2 * MAX_CLUSTERS];
+  __shared__ int idx[MAX_CLUSTERS];
+  const int bh = blockIdx.x, C = a.C;
+  if (threadIdx.x == 0) {
+    uint64_t st = a.seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(bh + 1));
+    int n = 0;
+    for (int i = 0; i < C; ++i) {
+      const uint64_t r = splitmix(st);
+      const int j = i + (int)(r % (uint64_t)(a.N - i));
+      int vi = i, vj = j, si = -1, sj = -1;
+      for (int e = 0; e < n; ++e) {
+        if (key[e] == i) { vi = val[e]; si = e; }
+        if (key[e] == j) { vj = val[e]; sj = e; }
+      }
+      if (si < 0) { key[n] = i; si = n++; }
+      if (sj < 0 && j != i) { key[n] = j; sj = n++; }
+      val[si] = vj;
+      if (j != i) val[sj] = vi;
+      idx[i] = vj;
+    }
+  }
+  __syncthreads();
+  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
+  for (int e = threadIdx.x; e < C * D; e += blockDim.x) {
+    const int kk = e / D, c = e % D;
+    a.cent[(size_t)bh * C * D + e] = bf2f(vh[(size_t)idx[kk] * D + c]);
+  }
+  for (int kk = threadIdx.x; kk < C; kk += blockDim.x) a.init_idx[(size_t)bh * C + kk] = idx[kk];
+}
+
+// Assignment step plus per-workgroup member sums.
+// grid (nkm, BH), 512 threads, KM_CHUNK tokens per workgroup (2 per thread).
+__global__ __launch_bounds__(512) void k_km_assign(Args a) {
+  __shared__ __align__(16) float cs[MAX_CLUSTERS * D];
+  __shared__ float cn[MAX_CLUSTERS];
+  __shared__ unsigned long long bins[MAX_CLUSTERS * D];
+  __shared__ int cnt[MAX_CLUSTERS];
+  const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, C = a.C;
+  const float* cent = a.cent + (size_t)bh * C * D;
+  for (int e = t; e < C * D; e += 512) {
+    cs[e] = cent[e];
+    bins[e] = 0ull;
+  }
+  if (t < C) cnt[t] = 0;
+  __syncthreads();
+  if (t < C) {
+    float s = 0.0f;
+    for (int c = 0; c < D; ++c) s = __builtin_fmaf(cs[t * D + c], cs[t * D + c], s);
+    cn[t] = s;
+  }
+  __syncthreads();
+  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
+  for (int rep = 0; rep < KM_CHUNK / 512; ++rep) {
+    const int j = chunk * KM_CHUNK + rep * 512 + t;
+    if (j < a.N) {
+      float v[D];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + i * 8);
+        v[i * 8 + 0] = bf2f(u.x);
+        v[i * 8 + 1] = bf2f(u.x >> 16);
+        v[i * 8 + 2] = bf2f(u.y);
+        v[i * 8 + 3] = bf2f(u.y >> 16);
+        v[i * 8 + 4] = bf2f(u.z);
+        v[i * 8 + 5] = bf2f(u.z >> 16);
+        v[i * 8 + 6] = bf2f(u.w);
+        v[i * 8 + 7] = bf2f(u.w >> 16);
+      }
+      int best = 0;
+      float bestD = 0.0f;
+      int kk = 0;
+      // four independent channel-ordered fma chains at a time
+      for (; kk + 4 <= C; kk += 4) {
+        const float* c0p = cs + kk * D;
+        float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D; c += 4) {
+          const float4 x0 = *reinterpret_cast<const float4*>(c0p + c);
+          const float4 x1 = *reinterpret_cast<const float4*>(c0p + D + c);
+          const float4 x2 = *reinterpret_cast<const float4*>(c0p + 2 * D + c);
+          const float4 x3 = *reinterpret_cast<const float4*>(c0p + 3 * D + c);
+          d0 = __builtin_fmaf(v[c], x0.x, d0);
+          d1 = __builtin_fmaf(v[c], x1.x, d1);
+          d2 = __builtin_fmaf(v[c], x2.x, d2);
+          d3 = __builtin_fmaf(v[c], x3.x, d3);
+          d0 = __builtin_fmaf(v[c + 1], x0.y, d0);
+          d1 = __builtin_fmaf(v[c + 1], x1.y, d1);
+          d2 = __builtin_fmaf(v[c + 1], x2.y, d2);
+          d3 = __builtin_fmaf(v[c + 1], x3.y, d3);
+          d0 = __builtin_fmaf(v[c + 2], x0.z, d0);
+          d1 = __builtin_fmaf(v[c + 2], x1.z, d1);
+          d2 = __builtin_fmaf(v[c + 2], x2.z, d2);
+          d3 = __builtin_fmaf(v[c + 2], x3.z, d3);
+          d0 = __builtin_fmaf(v[c + 3], x0.w, d0);
+          d1 = __builtin_fmaf(v[c + 3], x1.w, d1);
+          d2 = __builtin_fmaf(v[c + 3], x2.w, d2);
+          d3 = __builtin_fmaf(v[c + 3], x3.w, d3);
+        }
+        const float e0 = __builtin_fmaf(-2.0f, d0, cn[kk]);
+        const float e1 = __builtin_fmaf(-2.0f, d1, cn[kk + 1]);
+        const float e2 = __builtin_fmaf(-2.0f, d2, cn[kk + 2]);
+        const float e3 = __builtin_fmaf(-2.0f, d3, cn[kk + 3]);
+        if (kk == 0 || e0 < bestD) { best = kk; bestD = e0; }
+        if (e1 < bestD) { best = kk + 1; bestD = e1; }
+        if (e2 < bestD) { best = kk + 2; bestD = e2; }
+        if (e3 < bestD) { best = kk + 3; bestD = e3; }
+      }
+      for (; kk < C; ++kk) {
+        float d0 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) d0 = __builtin_fmaf(v[c], cs[kk * D + c], d0);
+        const float e0 = __builtin_fmaf(-2.0f, d0, cn[kk]);
+        if (kk == 0 || e0 < bestD) { best = kk; bestD = e0; }
+      }
+      a.labels[(size_t)bh * a.N + j] = best;
+      atomicAdd(&cnt[best], 1);
+#pragma unroll
+      for (int c = 0; c < D; ++c)
+        atomicAdd(&bins[best * D + c], (unsigned long long)fx24(v[c]));
+    }
+  }
+  __syncthreads();
+  long long* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
+  for (int e = t; e < C * D; e += 512) part[e] = (long long)bins[e];
+  if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
+}
+
+// Update step: centroid = exact mean of its members (empty clusters stay).
+// grid (C, BH), 128 threads.
+__global__ __launch_bounds__(128) void k_km_update(Args a) {
+  const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
+  long long s = 0, n = 0;
+  for (int ch = 0; ch < a.nkm; ++ch) {
+    s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
+    n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
+  }
+  if (n > 0) a.cent[((size_t)bh * C + kk) * D + c] = fixed_mean(s, n);
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of positions by cluster id.  grid BH, 1024 threads.
+__global__ __launch_bounds__(1024) void k_perm(Args a) {
+  __shared__ int base[MAX_CLUSTERS + 1];
+  __shared__ int wcnt[16][MAX_CLUSTERS + 1];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
+  const int* lab = a.labels + (size_t)bh * a.N;
+  int* perm = a.perm + (size_t)bh * a.N;
+  int* iperm = a.iperm + (size_t)bh * a.N;
+  if (t <= MAX_CLUSTERS) base[t] = 0;
+  __syncthreads();
+  for (int j = t; j < a.N; j += 1024) atomicAdd(&base[lab[j] + 1], 1);
+  __syncthreads();
+  if (t == 0)
+    for (int kk = 0; kk < C; ++kk) base[kk + 1] += base[kk];
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < a.N; j0 += 1024) {
+    const int j = j0 + t;
+    const int l = j < a.N ? lab[j] : MAX_CLUSTERS;  // sentinel bucket for the tail
+    unsigned long long peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+      const unsigned long long m = __ballot((l >> b) & 1);
+      peers &= ((l >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    for (int e = t; e < 16 * (MAX_CLUSTERS + 1); e += 1024) (&wcnt[0][0])[e] = 0;
+    __syncthreads();
+    if (rank == 0) wcnt[w][l] = __popcll(peers);
+    __syncthreads();
+    if (j < a.N) {
+      int pre = 0;
+      for (int ww = 0; ww < w; ++ww) pre += wcnt[ww][l];
+      const int pos = base[l] + pre + rank;
+      perm[pos] = j;
+      iperm[j] = pos;
+    }
+    __syncthreads();
+    if (t < C) {
+      int tot = 0;
+      for (int ww = 0; ww < 16; ++ww) tot += wcnt[ww][t];
+      base[t] += tot;
+    }
+    __syncthreads();
+  }
+}
+
+// Identity permutation (V-Smooth off).  grid (ceil(N/256), BH), 256 threads.
+__global__ __launch_bounds__(256) void k_perm_identity(Args a) {
+  const int j = blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
+  if (j < a.N) {
+    a.perm[(size_t)bh * a.N + j] = j;
+    a.iperm[(size_t)bh * a.N + j] = j;
+    a.labels[(size_t)bh * a.N + j] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-block E4M3 codes of Q (z = 0) and smoothed K (z = 1).
+// grid (nblk, BH, 2), 256 threads: thread = (row t/2, 64-channel half t%2).
+__global__ __launch_bounds__(256) void k_qk_quant(Args a) {
+  __shared__ float wmax[4];
+  const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z, t = threadIdx.x;
+  const int r = t >> 1, hf = t & 1, p = blk * BLK + r;
+  const bool real = p < a.N;
+  const bool follow = isk || (a.flags & VC_PERMUTE_Q);
+  const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
+  const float* kbar = a.kbar + (size_t)bh * D + hf * 64;
+  float x[64];
+  float amax = 0.0f;
+  if (real) {
+    const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
+    const uint16_t* row = src + (size_t)j * D + hf * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      x[i * 8 + 0] = bf2f(u.x);
+      x[i * 8 + 1] = bf2f(u.x >> 16);
+      x[i * 8 + 2] = bf2f(u.y);
+      x[i * 8 + 3] = bf2f(u.y >> 16);
+      x[i * 8 + 4] = bf2f(u.z);
+      x[i * 8 + 5] = bf2f(u.z >> 16);
+      x[i * 8 + 6] = bf2f(u.w);
+      x[i * 8 + 7] = bf2f(u.w >> 16);
+    }
+    if (isk) {
+#pragma unroll
+      for (int c = 0; c < 64; ++c) x[c] = x[c] - kbar[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 64; ++c) amax = fmaxf(amax, fabsf(x[c]));
+  }
+  amax = wave_max(amax);
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float s, inv;
+  scale_from_amax(amax, &s, &inv);
+  uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + hf * 64;
+  uint32_t w[16];
+  if (real) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w[i] = e4m3x2(x[4 * i] * inv, x[4 * i + 1] * inv) |
+             (e4m3x2(x[4 * i + 2] * inv, x[4 * i + 3] * inv) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  if (t == 0) (isk ? a.sk : a.sq)[(size_t)bh * a.nblk + blk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// V block means and block maxima of |V - mu|.  grid (nblk, BH), 256 threads:
+// thread = (channel t%128, row half t/128).
+__global__ __launch_bounds__(256) void k_v_stats(Args a) {
+  __shared__ long long ssum[2][D];
+  __shared__ float smax[2][D];
+  __shared__ float smu[D];
+  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int c = t & 127, hf = t >> 7;
+  const int p0 = blk * BLK, n = min(BLK, a.N - p0);
+  const bool vs = (a.flags & VC_VSMOOTH) != 0;
+  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
+  const int* perm = a.perm + (size_t)bh * a.N;
+  float x[64];
+  long long s = 0;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int r = hf * 64 + i;
+    x[i] = 0.0f;
+    if (r < n) {
+      x[i] = bf2f(vh[(size_t)perm[p0 + r] * D + c]);
+      s += fx24(x[i]);
+    }
+  }
+  ssum[hf][c] = s;
+  __syncthreads();
+  if (t < D) smu[c] = vs ? fixed_mean(ssum[0][c] + ssum[1][c], n) : 0.0f;
+  __syncthreads();
+  const float mu = smu[c];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    if (hf * 64 + i < n) m = fmaxf(m, fabsf(x[i] - mu));
+  smax[hf][c] = m;
+  __syncthreads();
+  if (t < D) {
+    const size_t o = ((size_t)bh * a.nblk + blk) * D + c;
+    a.mu[o] = mu;
+    a.bamax[o] = fmaxf(smax[0][c], smax[1][c]);
+  }
+}
+
+// Per-channel residual scales and block means in code units.  grid BH, 128 threads.
+__global__ __launch_bounds__(128) void k_v_scale(Args a) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  float A = 0.0f;
+  for (int b = 0; b < a.nblk; ++b) A = fmaxf(A, a.bamax[((size_t)bh * a.nblk + b) * D + c]);
+  float s, inv;
+  scale_from_amax(A, &s, &inv);
+  a.sv[(size_t)bh * D + c] = s;
+  a.inv[(size_t)bh * D + c] = inv;
+  for (int b = 0; b < a.nblk; ++b) {
+    const size_t o = ((size_t)bh * a.nblk + b) * D + c;
+    a.mup[o] = a.mu[o] * inv;
+  }
+}
+
+// Residual codes (channel-major, interleaved) and the repair criterion.
+// grid (nblk, BH), 128 threads: thread = position in the block.
+__global__ __launch_bounds__(128) void k_v_quant(Args a) {
+  __shared__ float smu[D], sinv[D], ssv[D];
+  __shared__ __align__(16) uint8_t tile[D * BLK];
+  const int blk = blockIdx.x, bh = blockIdx.y, r = threadIdx.x;
+  const int p = blk * BLK + r;
+  smu[r] = a.mu[((size_t)bh * a.nblk + blk) * D + r];
+  sinv[r] = a.inv[(size_t)bh * D + r];
+  ssv[r] = a.sv[(size_t)bh * D + r];
+  __syncthreads();
+  const int col = v_col(r);
+  if (p < a.N) {
+    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
+    float e = 0.0f;
+    for (int i = 0; i < D / 8; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = i * 8 + 2 * j;
+        const float x0 = (bf2f(h[j]) - smu[c]) * sinv[c];
+        const float x1 = (bf2f(h[j] >> 16) - smu[c + 1]) * sinv[c + 1];
+        const uint32_t cc = e4m3x2(x0, x1);
+        tile[c * BLK + col] = (uint8_t)(cc & 0xff);
+        tile[(c + 1) * BLK + col] = (uint8_t)(cc >> 8);
+        const float t0 = ssv[c] * (x0 - e4m3_val(cc & 0xff));
+        e = __builtin_fmaf(t0, t0, e);
+        const float t1 = ssv[c + 1] * (x1 - e4m3_val(cc >> 8));
+        e = __builtin_fmaf(t1, t1, e);
+      }
+    }
+    a.err[(size_t)bh * a.N + p] = e;
+  } else {
+    for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
+  }
+  __syncthreads();
+  // thread r stores channel row r of the tile (128 contiguous bytes)
+  uint8_t* dst = a.v8t + ((size_t)bh * D + r) * a.Npad + (size_t)blk * BLK;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + r * BLK + 16 * i);
+}
+
+// ---------------------------------------------------------------------------
+// Repair set: the m positions with the largest error (ties: lower position),
+// by an exact radix select on the 64-bit key (~err_bits, position), then a
+// compaction in position order.  grid BH, 1024 threads.
+__global__ __launch_bounds__(1024) void k_rep_select(Args a) {
+  __shared__ int hist[256];
+  __shared__ unsigned long long s_prefix, s_mask;
+  __shared__ int s_kth, s_base;
+  __shared__ int wtot[16];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float* err = a.err + (size_t)bh * a.N;
+  if (t == 0) {
+    s_prefix = 0ull;
+    s_mask = 0ull;
+    s_kth = a.m;
+  }
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+    const unsigned long long pre = s_prefix, msk = s_mask;
+    for (int j = t; j < a.N; j += 1024) {
+      const unsigned long long key =
+          ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
+      if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+      int kth = s_kth, cum = 0, dg = 0;
+      for (dg = 0; dg < 256; ++dg) {
+        if (cum + hist[dg] >= kth) break;
+        cum += hist[dg];
+      }
+      s_kth = kth - cum;
+      s_prefix = pre | ((unsigned long long)dg << shift);
+      s_mask = msk | (255ull << shift);
+    }
+    __syncthreads();
+  }
+  const unsigned long long thr = s_prefix;  // the m-th smallest key
+  int* out = a.rep_pos + (size_t)bh * a.mpad;
+  if (t == 0) s_base = 0;
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < a.N; j0 += 1024) {
+    const int j = j0 + t;
+    bool sel = false;
+    if (j < a.N) {
+      const unsigned long long key =
+          ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
+      sel = key <= thr;
+    }
+    const unsigned long long b = __ballot(sel);
+    if (lane == 0) wtot[w] = __popcll(b);
+    __syncthreads();
+    int pre = s_base;
+    for (int ww = 0; ww < w; ++ww) pre += wtot[ww];
+    const int slot = pre + __popcll(b & lt);
+    if (sel && slot < a.mpad) out[slot] = j;  // exactly m keys are <= thr
+    __syncthreads();
+    if (t == 0) {
+      int tot = 0;
+      for (int ww = 0; ww < 16; ++ww) tot += wtot[ww];
+      s_base += tot;
+    }
+    __syncthreads();
+  }
+  for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
+}
+
+// Residual error (code units, bf16) of the repaired positions, channel-major
+// with the repair-slot interleave.  grid (mpad/128, BH), 128 threads = slots.
+__global__ __launch_bounds__(128) void k_rep_delta(Args a) {
+  __shared__ __align__(16) uint16_t tile[D * BLK];
+  const int grp = blockIdx.x, bh = blockIdx.y, s = threadIdx.x;
+  const int gs = grp * BLK + s;
+  const int col = rep_col(s);
+  const int p = gs < a.m ? a.rep_pos[(size_t)bh * a.mpad + gs] : -1;
+  if (p >= 0) {
+    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
+    const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
+    const float* inv = a.inv + (size_t)bh * D;
+    for (int i = 0; i < D / 8; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = i * 8 + 2 * j;
+        const float x0 = (bf2f(h[j]) - mu[c]) * inv[c];
+        const float x1 = (bf2f(h[j] >> 16) - mu[c + 1]) * inv[c + 1];
+        const uint32_t cc = e4m3x2(x0, x1);
+        tile[c * BLK + col] = f2bf_rne(x0 - e4m3_val(cc & 0xff));
+        tile[(c + 1) * BLK + col] = f2bf_rne(x1 - e4m3_val(cc >> 8));
+      }
+    }
+  } else {
+    for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
+  }
+  __syncthreads();
+  uint16_t* dst = a.rep_dt + ((size_t)bh * D + s) * a.mpad + (size_t)grp * BLK;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *reinterpret_cast<uint4*>(dst + 8 * i) = *reinterpret_cast<const uint4*>(tile + s * BLK + 8 * i);
+}
+
+// Header: marks the clusters valid for this shape.  grid 1, 64 threads.
+__global__ void k_header(Args a, uint32_t clustered) {
+  if (threadIdx.x == 0) {
+    a.header->magic = MAGIC;
+    a.header->clustered = clustered;
+    a.header->B = a.B;
+    a.header->H = a.H;
+    a.header->N = a.N;
+    a.header->C = a.C;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
+  const unsigned BH = (unsigned)a.BH;
+  const bool vs = (a.flags & VC_VSMOOTH) != 0;
+  hipLaunchKernelGGL(k_ksum, dim3(a.nkc, BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_kbar, dim3(BH), dim3(128), 0, st, a);
+  if (vs) {
+    if (recluster) {
+      hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
+      for (int it = 0; it < a.T; ++it) {
+        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(512), 0, st, a);
+        hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
+      }
+      hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);
+      hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 1u);
+    }
+  } else {
+    hipLaunchKernelGGL(k_perm_identity, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 0u);
+  }
+  hipLaunchKernelGGL(k_qk_quant, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
+  if (a.m > 0) {
+    hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vc

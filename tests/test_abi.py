@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/vc_attn.h, validates parameters and pointers before any
+device call, and lays the workspace out without overlaps."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import precision_fp8_attention_amd as vc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "vc_attn.h")).read()
+    return sorted(set(re.findall(r"\b(vc_attn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = vc.lib()
+    names = _declared()
+    assert set(names) == set(vc.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_defaults_and_version():
+    p = vc.default_params(1, 2, 1024)
+    assert (p.d, p.block, p.n_clusters, p.kmeans_iters, p.expcast_k) == (128, 128, 16, 10, 8)
+    assert abs(p.rho - 0.005) < 1e-9 and p.flags == vc.DEFAULT_FLAGS and p.tau == 0.0
+    assert vc.check_params(p) == vc.OK
+    assert vc.version() >= 100
+    assert vc.status_string(vc.ERR_WORKSPACE).startswith("workspace")
+
+
+BAD = [
+    (dict(d=64), vc.ERR_UNSUPPORTED),
+    (dict(block=64), vc.ERR_UNSUPPORTED),
+    (dict(B=0), vc.ERR_INVALID_ARG),
+    (dict(N=0), vc.ERR_INVALID_ARG),
+    (dict(N=(1 << 20) + 1), vc.ERR_INVALID_ARG),
+    (dict(n_clusters=0), vc.ERR_INVALID_ARG),
+    (dict(n_clusters=65), vc.ERR_INVALID_ARG),
+    (dict(N=10, n_clusters=11), vc.ERR_INVALID_ARG),
+    (dict(kmeans_iters=0), vc.ERR_INVALID_ARG),
+    (dict(expcast_k=9), vc.ERR_INVALID_ARG),
+    (dict(rho=-0.1), vc.ERR_INVALID_ARG),
+    (dict(rho=1.5), vc.ERR_INVALID_ARG),
+    (dict(rho=float("nan")), vc.ERR_INVALID_ARG),
+    (dict(tau=-1.0), vc.ERR_INVALID_ARG),
+    (dict(tau=7.0), vc.ERR_INVALID_ARG),
+    (dict(expcast_k=0, tau=71.0), vc.ERR_INVALID_ARG),
+    (dict(sm_scale=float("inf")), vc.ERR_INVALID_ARG),
+    (dict(flags=64), vc.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_parameter_validation(kw, status):
+    base = dict(B=1, H=2, N=1024)
+    base.update(kw)
+    B, H, N = base.pop("B"), base.pop("H"), base.pop("N")
+    p = vc.default_params(B, H, N, **base)
+    assert vc.check_params(p) == status
+    assert vc.workspace_size(p) == 0
+    with pytest.raises(vc.VCError):
+        vc.workspace_layout(p)
+
+
+def test_pointer_and_workspace_errors_before_device_work():
+    L = vc.lib()
+    p = vc.default_params(1, 2, 1024)
+    need = vc.workspace_size(p)
+    fake = C.c_void_p(0x10000)  # never dereferenced: checks fail first
+    mis = C.c_void_p(0x10008)
+    P = C.byref(p)
+    assert L.vc_attn_prepare(P, None, fake, fake, fake, need, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_prepare(P, mis, fake, fake, fake, need, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_prepare(P, fake, fake, fake, None, need, None) == vc.ERR_WORKSPACE
+    assert L.vc_attn_prepare(P, fake, fake, fake, fake, need - 1, None) == vc.ERR_WORKSPACE
+    assert L.vc_attn_prepare(P, fake, fake, fake, C.c_void_p(0x10080), need, None) == vc.ERR_WORKSPACE
+    assert L.vc_attn_forward(P, fake, need, None, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_forward(P, fake, need - 1, fake, None) == vc.ERR_WORKSPACE
+    assert L.vc_attn_forward(None, fake, need, fake, None) == vc.ERR_INVALID_ARG
+    bad = vc.default_params(1, 2, 1024, d=64)
+    assert L.vc_attn_forward(C.byref(bad), fake, need, fake, None) == vc.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,H,N,C_,rho", [(1, 2, 1024, 8, 0.005), (2, 24, 16544, 32, 0.005),
+                                          (1, 40, 75600, 64, 0.005), (1, 1, 1, 1, 1.0),
+                                          (1, 3, 300, 5, 0.0)])
+def test_layout_aligned_and_disjoint(B, H, N, C_, rho):
+    p = vc.default_params(B, H, N, n_clusters=C_, rho=rho)
+    L = vc.workspace_layout(p)
+    BH, nblk = B * H, (N + 127) // 128
+    npad = nblk * 128
+    m = 0 if rho == 0 else min(N, int(-(-float(C.c_float(rho).value) * N // 1)))
+    mpad = -(-m // 128) * 128
+    sizes = dict(header=256, kbar=BH * 512, ksum=BH * (-(-N // 512)) * 1024, init_idx=BH * C_ * 4,
+                 centroids=BH * C_ * 512, labels=BH * N * 4, perm=BH * N * 4, iperm=BH * N * 4,
+                 q8=BH * npad * 128, k8=BH * npad * 128, sq=BH * nblk * 4, sk=BH * nblk * 4,
+                 mu=BH * nblk * 512, bamax=BH * nblk * 512, mup=BH * nblk * 512, sv=BH * 512,
+                 inv=BH * 512, v8t=BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,
+                 rep_dt=BH * 128 * mpad * 2)
+    spans = sorted((L[k], L[k] + n, k) for k, n in sizes.items())
+    for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (ka, kb)
+    for k in sizes:
+        assert L[k] % 256 == 0
+    assert spans[-1][1] <= L["total"] == vc.workspace_size(p)

@@ -1,0 +1,156 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: every prepare output that is an integer or a code (cluster ids, the
+permutation, Q/K/V E4M3 codes, the repair set) and every fp32 scale, mean and
+criterion it is derived from is bit-identical to the oracle; the output O is
+within max-abs 1e-2 and relative-L2 5e-3 of the oracle's fp64 simulation."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gpu_common as G  # noqa: E402
+
+from oracle import oracle as orc  # noqa: E402
+from synthetic import inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import precision_fp8_attention_amd as vc
+    vc.lib()
+
+
+def _full_case(p, q, k, v, heads, rows, label):
+    G.log(f"[case] {label}: B={p.B} H={p.H} N={p.N} C={p.n_clusters} flags={p.flags} "
+          f"tau={p.tau} k={p.expcast_k} rho={p.rho}")
+    qd, kd, vd = G.to_device(q, k, v)
+    ws, o = G.run(p, qd, kd, vd)
+    P = G.oracle_params(p)
+    ora = orc.prepare(P, q, k, v, heads=heads)
+    gpu = G.read_prepared(p, ws, heads)
+    bad = G.compare_prepared(gpu, ora, vsmooth=bool(p.flags & 1))
+    assert not bad, f"{label}: prepare mismatch: {bad}"
+    return G.check_output(p, q, k, v, o, heads, rows, prep_oracle=ora, label=label)
+
+
+# ------------------------------------------------------------------ small / edge
+
+SMALL = [
+    # (label, B, H, N, C, kwargs)
+    ("one_token", 1, 1, 1, 1, {}),
+    ("one_block_ragged", 1, 2, 100, 3, {}),
+    ("exact_blocks", 1, 1, 256, 4, {}),
+    ("ragged_tail", 2, 2, 300, 5, dict(rho=0.05)),
+    ("several_tiles", 1, 3, 1000, 8, {}),
+    ("vsmooth_off", 1, 2, 700, 4, dict(flags=0)),
+    ("repair_off", 1, 2, 700, 4, dict(flags=1 | 4)),
+    ("q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2)),
+    ("lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0)),
+    ("literal_56", 1, 2, 700, 4, dict(expcast_k=0)),
+    ("repair_all", 1, 1, 260, 3, dict(rho=1.0)),
+    ("custom_scale_seed", 1, 2, 513, 6, dict(sm_scale=0.05, seed=12345, T=3)),
+]
+
+
+@pytest.mark.parametrize("label,B,H,N,C_,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(label, B, H, N, C_, kw):
+    q, k, v = inputs.make_custom(B, H, N, seed=len(label), rate=0.02, sigma=25.0, vmean=0.4)
+    p = G.lib_params(B, H, N, C_, **kw)
+    heads = list(range(B * H))
+    _full_case(p, q, k, v, heads, np.arange(N, dtype=np.int32), label)
+
+
+def test_workload0_all_rows():
+    q, k, v = inputs.make_inputs(0)
+    wl = inputs.WORKLOADS[0]
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+    _full_case(p, q, k, v, [0, 1], np.arange(wl["N"], dtype=np.int32), "workload0")
+
+
+@pytest.mark.parametrize("cfg,heads,nrows", [(1, [0, 23], 160), (2, [5, 17], 160),
+                                             (3, [0, 25, 47], 192)])
+def test_workloads_sampled(cfg, heads, nrows):
+    """Full-size workloads in the benchmark's launch configuration: every head runs
+    on the GPU; prepare is compared bit-exactly and outputs on sampled rows for a
+    few heads (first, middle, last)."""
+    wl = inputs.WORKLOADS[cfg]
+    q, k, v = inputs.make_inputs(cfg)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+    rows = G.sample_rows(wl["N"], nrows, seed=cfg)
+    _full_case(p, q, k, v, heads, rows, f"workload{cfg}")
+
+
+def test_workload4_video_sampled():
+    """Largest workload (75600 video tokens, 40 heads, 64 clusters): all heads on
+    the GPU, two heads compared."""
+    wl = inputs.WORKLOADS[4]
+    q, k, v = inputs.make_inputs(4)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+    rows = G.sample_rows(wl["N"], 96, seed=4)
+    _full_case(p, q, k, v, [0, 39], rows, "workload4")
+
+
+# ------------------------------------------------------------------ behaviour
+
+def test_deterministic_and_reuse_clusters():
+    """Two full runs are bit-identical; a prepare that reuses the clusters gives the
+    same output as the full prepare; reuse on a fresh workspace is refused."""
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    q, k, v = inputs.make_custom(1, 3, 900, seed=3)
+    p = G.lib_params(1, 3, 900, 6)
+    qd, kd, vd = G.to_device(q, k, v)
+    G.log("[case] determinism: two full runs")
+    ws1, o1 = G.run(p, qd, kd, vd)
+    ws2, o2 = G.run(p, qd, kd, vd)
+    assert torch.equal(o1, o2)
+    assert torch.equal(ws1, ws2)
+    G.log("[case] reuse clusters")
+    pr = G.lib_params(1, 3, 900, 6, flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
+    o3 = torch.empty_like(qd)
+    vc.prepare(pr, qd, kd, vd, ws1)
+    vc.forward(pr, ws1, o3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+    fresh = torch.zeros_like(ws1)
+    with pytest.raises(vc.VCError) as e:
+        vc.prepare(pr, qd, kd, vd, fresh)
+    assert e.value.status == vc.ERR_NOT_PREPARED
+    G.log("[case] reuse with drifted V keeps the permutation")
+    v2 = v.copy()
+    v2[..., :64] = inputs.to_bf16_bits(inputs.bf16_bits_to_f32(v2[..., :64]) * 1.1)
+    qd, kd, vd2 = G.to_device(q, k, v2)
+    o4 = torch.empty_like(qd)
+    vc.prepare(pr, qd, kd, vd2, ws1)
+    vc.forward(pr, ws1, o4)
+    torch.cuda.synchronize()
+    gp = G.read_prepared(pr, ws1, [0, 1, 2])
+    P = G.oracle_params(p)
+    ora = orc.prepare(P, q, k, v, heads=[0, 1, 2])
+    assert np.array_equal(gp["perm"], ora["perm"])  # clusters of the first call
+
+
+def test_output_in_original_order_when_inputs_permuted():
+    """Non-causal attention: permuting the input tokens permutes the output rows
+    (up to the quantisation, which depends on the token order through the
+    clusters' initialisation); checked against the oracle on both orders."""
+    q, k, v = inputs.make_custom(1, 1, 384, seed=6)
+    perm = np.random.default_rng(0).permutation(384)
+    p = G.lib_params(1, 1, 384, 4)
+    rows = np.arange(384, dtype=np.int32)
+    for qq, kk, vv, lab in ((q, k, v, "orig"), (q[:, :, perm], k[:, :, perm], v[:, :, perm], "perm")):
+        qq, kk, vv = (np.ascontiguousarray(t) for t in (qq, kk, vv))
+        G.log(f"[case] token order {lab}")
+        qd, kd, vd = G.to_device(qq, kk, vv)
+        ws, o = G.run(p, qd, kd, vd)
+        res = G.check_output(p, qq, kk, vv, o, [0], rows, label=lab)
+        assert res["rel_l2_exact"] < 0.1

@@ -62,7 +62,9 @@ SMALL = [
 
 @pytest.mark.parametrize("label,B,H,N,C_,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_small_cases(label, B, H, N, C_, kw):
-    q, k, v = inputs.make_custom(B, H, N, seed=len(label), rate=0.02, sigma=25.0, vmean=0.4)
+    # the workloads' value distribution (1% outlier tokens, sigma 20, zero mean):
+    # the max-abs bound is absolute, so inputs keep the workloads' magnitudes
+    q, k, v = inputs.make_custom(B, H, N, seed=len(label), rate=0.01, sigma=20.0)
     p = G.lib_params(B, H, N, C_, **kw)
     heads = list(range(B * H))
     _full_case(p, q, k, v, heads, np.arange(N, dtype=np.int32), label)
@@ -113,7 +115,9 @@ def test_deterministic_and_reuse_clusters():
     ws1, o1 = G.run(p, qd, kd, vd)
     ws2, o2 = G.run(p, qd, kd, vd)
     assert torch.equal(o1, o2)
-    assert torch.equal(ws1, ws2)
+    a1, a2 = G.read_prepared(p, ws1, [0, 1, 2]), G.read_prepared(p, ws2, [0, 1, 2])
+    for key in G.EXACT_KEYS:  # every array prepare writes (gaps stay unwritten)
+        assert np.array_equal(a1[key], a2[key]), key
     G.log("[case] reuse clusters")
     pr = G.lib_params(1, 3, 900, 6, flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
     o3 = torch.empty_like(qd)

@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""VC-Attention FP8 benchmark on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident in
+HBM: vc_attn_prepare (K smoothing, Q/K codes, k-means over V, joint permutation,
+block demean, residual codes, repair set) followed by vc_attn_forward (the fused
+ExpCast attention kernel).  The workload is FLUX-like 2048x2048 text-to-image
+joint attention with a CFG pair: B=2, H=24, N=16544, d=128, 32 clusters, 10
+Lloyd iterations, rho=0.005.
+
+Prints one JSON line.  value = attention TFLOP/s of the step, 4*B*H*N^2*d / t.
+roofline: the fused forward kernel (dominant kernel) against the dense FP8
+MFMA peak; its duration comes from HIP events recorded on the stream the
+library launches on (torch's current stream).  cpu_baseline: the CPU oracle
+timed on a bounded sample of the same workload and scaled to the whole job.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_flux2048cfg_traffic.json")
+FWD_SRC = os.path.join(ROOT, "precision_fp8_attention_amd", "csrc", "vc_forward.hip")
+
+
+def _events_ms(fn, n):
+    import torch
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _traffic(launches_per_step: int):
+    """HBM bytes per forward launch from the committed rocprofv3 counter summary,
+    or None when it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(FWD_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if t.get("kernel_source_sha256") != sha:
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(wl, q, k, v, P, flops, gpu_out):
+    """Oracle on the host: prepare of 2 heads (one per batch item) and the
+    simulated forward of 8192 query rows per head, scaled to all heads/rows."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    B, H, N = wl["B"], wl["H"], wl["N"]
+    heads = [0, B * H - 1]
+    t0 = time.perf_counter()
+    prep = orc.prepare(P, q, k, v, heads=heads)
+    t_prep = time.perf_counter() - t0
+    rows = np.linspace(0, N - 1, 8192).astype(np.int32)
+    slot = np.repeat(np.arange(len(heads)), len(rows)).astype(np.int32)
+    idx = np.tile(rows, len(heads)).astype(np.int32)
+    t0 = time.perf_counter()
+    sim = orc.forward_rows(P, prep, slot, idx)
+    t_fwd = time.perf_counter() - t0
+    # prepare ran one head per thread: the full job keeps min(cores, B*H) busy
+    full_prep = t_prep * (B * H) / min(cores, B * H)
+    full_fwd = t_fwd * (B * H * N) / len(idx)
+    total = full_prep + full_fwd
+    got = gpu_out.reshape(B * H, N, 128)[np.asarray(heads)[slot], idx]
+    rel = float(np.linalg.norm(got - sim) / np.linalg.norm(sim))
+    mx = float(np.max(np.abs(got - sim)))
+    base = {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, os.cpu_count() or cores),
+            "kind": "oracle",
+            "sample": (f"prepare of heads {heads} ({t_prep:.2f} s wall, one head per thread) and "
+                       f"simulated forward of {len(idx)} query rows ({t_fwd:.2f} s wall on {cores} "
+                       f"threads), scaled linearly to {B*H} heads x {N} rows: {total:.0f} s per step")}
+    return base, {"rows": int(len(idx)), "max_abs": mx, "rel_l2": rel}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (default 3)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time only vc_attn_forward launches (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    from synthetic import inputs
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+
+    wl = inputs.WORKLOADS[args.workload]
+    B, H, N = wl["B"], wl["H"], wl["N"]
+    q, k, v = inputs.make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+    p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"])
+    ws = vc.alloc_workspace(p, dev)
+    o = torch.empty_like(qd)
+    flops = 4.0 * B * H * N * N * 128
+
+    def step():
+        vc.prepare(p, qd, kd, vd, ws)
+        vc.forward(p, ws, o)
+
+    if args.forward_only:
+        step()
+        for _ in range(args.warmup):
+            vc.forward(p, ws, o)
+        torch.cuda.synchronize()
+        ms = _events_ms(lambda: vc.forward(p, ws, o), args.steps)
+        print(json.dumps({"forward_ms": ms, "launches": args.steps + args.warmup + 1}))
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = _events_ms(step, args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_fwd = _events_ms(lambda: vc.forward(p, ws, o), max(args.steps, 10))
+    ms_prep = _events_ms(lambda: vc.prepare(p, qd, kd, vd, ws), max(args.steps // 2, 5))
+    preuse = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                               flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
+    vc.prepare(p, qd, kd, vd, ws)
+    ms_reuse = _events_ms(lambda: vc.prepare(preuse, qd, kd, vd, ws), max(args.steps // 2, 5))
+    vc.prepare(p, qd, kd, vd, ws)
+    vc.forward(p, ws, o)
+    torch.cuda.synchronize()
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
+    traffic = _traffic(1)
+    res = {
+        "metric": "VC-Attention FP8 TFLOP/s and % of FP8 MFMA peak at N=16544,H=24,d=128",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "B": B, "H": H, "N": N, "d": 128, "clusters": wl["C"],
+                   "kmeans_iters": wl["T"], "rho": wl["rho"], "block": 128, "expcast_k": 8,
+                   "step": "prepare (with k-means) + forward"},
+        "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 3),
+        "forward_ms": round(ms_fwd, 4),
+        "forward_tflops": round(fwd_tflops, 3),
+        "prepare_ms": round(ms_prep, 4),
+        "prepare_reuse_clusters_ms": round(ms_reuse, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_fwd", "achieved": round(fwd_tflops, 3),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 5),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        P = orc.make_params(B, H, N, C_=wl["C"], T=wl["T"], rho=wl["rho"])
+        gpu_out = o.float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"], res["parity_sample"] = cpu_baseline(wl, q, k, v, P, flops, gpu_out)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -109,6 +109,9 @@ typedef struct {
   size_t mu;         /* f32 [BH][nblk][128] V block means (real units)           */
   size_t bamax;      /* f32 [BH][nblk][128] block maxima of |V - mu|             */
   size_t mup;        /* f32 [BH][nblk][128] block means in V code units          */
+  size_t mupt;       /* bf16 [BH][ceil(nblk/16)][2][128][16] the same means split
+                        into a high and a low bf16 part, 16 blocks per group,
+                        channel-major (operand of the restore MFMA)              */
   size_t sv;         /* f32 [BH][128] per-channel V residual scale               */
   size_t inv;        /* f32 [BH][128] its inverse                                */
   size_t v8t;        /* u8  [BH][128][Npad] residual codes, channel-major; inside

@@ -46,6 +46,7 @@ bool shape_of(const vc_attn_params* p, Shape* s) {
   s->mpad = ((s->m + BLK - 1) / BLK) * BLK;
   s->nkc = (p->N + KSUM_CHUNK - 1) / KSUM_CHUNK;
   s->nkm = (p->N + KM_CHUNK - 1) / KM_CHUNK;
+  s->nch16 = (s->nblk + 15) / 16;
   return true;
 }
 
@@ -76,6 +77,7 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.mu = take(BH * nb * D * 4);
   L.bamax = take(BH * nb * D * 4);
   L.mup = take(BH * nb * D * 4);
+  L.mupt = take(BH * (size_t)s.nch16 * 2 * D * 16 * 2);
   L.sv = take(BH * D * 4);
   L.inv = take(BH * D * 4);
   L.v8t = take(BH * D * Np);
@@ -102,6 +104,7 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.mpad = s.mpad;
   a.nkc = s.nkc;
   a.nkm = s.nkm;
+  a.nch16 = s.nch16;
   a.flags = p->flags;
   a.seed = p->seed;
   const float scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)D));
@@ -125,6 +128,7 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.mu = reinterpret_cast<float*>(b + L.mu);
   a.bamax = reinterpret_cast<float*>(b + L.bamax);
   a.mup = reinterpret_cast<float*>(b + L.mup);
+  a.mupt = reinterpret_cast<uint16_t*>(b + L.mupt);
   a.sv = reinterpret_cast<float*>(b + L.sv);
   a.inv = reinterpret_cast<float*>(b + L.inv);
   a.v8t = b + L.v8t;

@@ -19,7 +19,18 @@
 // one query: key 16t+4g+v of the block in S[t][v], g = lane/16.  Those 32 ExpCast
 // bytes are exactly the lane's B operand of O^T = V8^T . P^T because prepare
 // stores V8 channel-major with the same key interleave, so P never touches LDS.
-// The row sum of the block comes from one more MFMA against a ones row.
+// v_cvt_pk_u8_f32 rounds to nearest even, saturates to [0, 255] and inserts the
+// byte, so one fma and one convert produce each packed code.
+//
+// Row sums and restore.  One more MFMA per block multiplies P by a ones row:
+// block b of a 16-block group puts its ones in A row b%16, so the group's row
+// sums collect in a 16x16 accumulator L (lane (g, q), element v = block 4g+v).
+// Every 16 blocks L is split into bf16 high and low parts and one 16x16x16 bf16
+// MFMA group adds sum_b l_b * mu'_b to the accumulator: the restore costs no
+// per-element VALU work and no second pass over the keys.
+//
+// K/V tiles (16 KB each) are double-buffered in LDS and filled by direct
+// global->LDS loads while the previous block is computed.
 #include "vc_internal.h"
 
 namespace vc {
@@ -27,6 +38,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
@@ -34,8 +46,12 @@ __device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+__device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_bf16_k16(v4s a, v4s b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // 32 bytes of row `row` of a 128x128 byte tile, 16-byte chunks 2g and 2g+1,
@@ -62,6 +78,23 @@ __device__ __forceinline__ uint16_t f2bf_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+__device__ __forceinline__ float xmax16(float x) {  // max with lane ^ 16
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {  // max with lane ^ 32
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xsum16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Workgroup id -> (head, query block), so that consecutive logical tiles (same
 // head, sharing its K/V codes in L2) land on the same XCD: the dispatcher deals
 // workgroups round-robin over the 8 XCDs.
@@ -71,10 +104,90 @@ __device__ __forceinline__ int xcd_remap(int lin, int total) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
-__global__ __launch_bounds__(256) void k_fwd(Args a) {
-  __shared__ __align__(16) uint8_t Ks[BLK * D];
-  __shared__ __align__(16) uint8_t Vs[D * BLK];
-  __shared__ float mup_s[D];
+struct RowState {
+  float M;      // running maximum, code units
+  float ell;    // row sum of flushed 16-block groups
+  v4f L;        // row sums of the current group (lane (g,q): blocks 4g..4g+3)
+  v4f acc[8];   // O^T accumulator: channel 16ct+4g+v, query q
+};
+
+// Softmax of one 16-query subtile for one key block: new maximum, rescale of the
+// running state, ExpCast codes packed as the PV B operand.
+__device__ __forceinline__ v8i softmax_codes(v4f (&S)[8], RowState& st, float alpha, float bias,
+                                             float tau) {
+  float mx = S[0][0];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) mx = fmaxf(fmaxf(mx, S[t][0]), fmaxf(fmaxf(S[t][1], S[t][2]), S[t][3]));
+  mx = xmax32(xmax16(mx));
+  const float tmax = mx * alpha;
+  const float Mo = st.M;
+  const bool first = Mo == -INFINITY;
+  const float Mn = (first || tmax - Mo > tau) ? tmax : Mo;
+  if (Mn != Mo) {
+    const float r = first ? 0.0f : exp2f((Mo - Mn) * 0.125f);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= r;
+    st.L *= r;
+    st.ell *= r;
+    st.M = Mn;
+  }
+  const float beta = bias - Mn;
+  v8i pop;
+  if (fabsf(Mn) < 0x1p21f) {
+    // |fma - (bias + tau)| stays below half a code: no upper clamp needed
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t d = 0;
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][0], alpha, beta), 0, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][1], alpha, beta), 1, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][2], alpha, beta), 2, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][3], alpha, beta), 3, d);
+      pop[t] = (int)d;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) d |= expcast_byte(S[t][v], alpha, beta) << (8 * v);
+      pop[t] = (int)d;
+    }
+  }
+  return pop;
+}
+
+// Adds sum_b L[b] * mu'[b] of a finished 16-block group (bf16 hi/lo split, three
+// products) and moves the group's row sums into ell.
+__device__ __forceinline__ void restore_group(RowState& st, const uint16_t* mupt_grp, int l16, int g) {
+  const v4f W = st.L;
+  float s4 = (W[0] + W[1]) + (W[2] + W[3]);
+  s4 = xsum32(xsum16(s4));
+  st.ell += s4;
+  v4s bh, bl;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint16_t h = f2bf_rne(W[v]);
+    bh[v] = (short)h;
+    bl[v] = (short)f2bf_rne(W[v] - __uint_as_float((uint32_t)h << 16));
+  }
+  const uint16_t* hip = mupt_grp;
+  const uint16_t* lop = mupt_grp + D * 16;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const int c = 16 * ct + l16;
+    const v4s ah = *reinterpret_cast<const v4s*>(hip + c * 16 + 4 * g);
+    const v4s al = *reinterpret_cast<const v4s*>(lop + c * 16 + 4 * g);
+    v4f x = st.acc[ct];
+    x = mfma_bf16_k16(ah, bh, x);
+    x = mfma_bf16_k16(ah, bl, x);
+    x = mfma_bf16_k16(al, bh, x);
+    st.acc[ct] = x;
+  }
+  st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+__global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
+  __shared__ __align__(1024) uint8_t smem[2][2][BLK * D];  // [stage][K, V]
   __shared__ float alpha_s[BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -86,98 +199,101 @@ __global__ __launch_bounds__(256) void k_fwd(Args a) {
   const uint8_t* k8 = a.k8 + (size_t)bh * a.Npad * D;
   const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
   const float* sk = a.sk + (size_t)bh * a.nblk;
-  const float* mup = a.mup + (size_t)bh * a.nblk * D;
+  const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
   const float sQa = a.sq[(size_t)bh * a.nblk + qb];
+
+  // direct global->LDS loads of one block's K rows and V^T columns: wave w,
+  // instruction i fills 1 KB region r = 4i+w (8 rows); lane l lands at byte 16l,
+  // i.e. row 8r + l/8, stored chunk l%8, which holds source chunk (l%8)^(row%8)
+  auto issue = [&](int kb, int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + w;
+      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ (row & 7);
+      __builtin_amdgcn_global_load_lds(k8 + ((size_t)kb * BLK + row) * D + cc * 16,
+                                       &smem[st][0][r * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16,
+                                       &smem[st][1][r * 1024], 16, 0, 0);
+    }
+  };
 
   v8i qop[2];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs)
     qop[qs] = *reinterpret_cast<const v8i*>(q8 + (size_t)(w * 32 + qs * 16 + l16) * D + 32 * g);
 
-  // ones in rows 0, 4, 8, 12: every lane receives its query's block row sum in
-  // accumulator element 0 of the ones MFMA
-  v8i ones;
-  {
-    const int o = (l16 & 3) == 0 ? 0x38383838 : 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ones[i] = o;
-  }
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  RowState rs[2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    rs[qs].M = -INFINITY;
+    rs[qs].ell = 0.0f;
+    rs[qs].L = zero;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) rs[qs].acc[ct] = zero;
+  }
 
-  float M[2] = {-INFINITY, -INFINITY}, ell[2] = {0.0f, 0.0f};
-  v4f acc[2][8];
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[qs][ct] = zero;
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   for (int kb = 0; kb < a.nblk; ++kb) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, cc = ch & 7;
-      const uint4 kv = *reinterpret_cast<const uint4*>(k8 + ((size_t)kb * BLK + row) * D + cc * 16);
-      *reinterpret_cast<uint4*>(Ks + row * D + ((cc ^ (row & 7)) << 4)) = kv;
-      const uint4 vv = *reinterpret_cast<const uint4*>(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16);
-      *reinterpret_cast<uint4*>(Vs + row * BLK + ((cc ^ (row & 7)) << 4)) = vv;
-    }
-    if (tid < D) mup_s[tid] = mup[(size_t)kb * D + tid];
-    __syncthreads();
-
+    const int st = kb & 1;
+    if (kb + 1 < a.nblk) issue(kb + 1, st ^ 1);
+    const uint8_t* Ks = smem[st][0];
+    const uint8_t* Vs = smem[st][1];
     const float alpha = (sQa * sk[kb]) * a.c0;
-    const int nvalid = min(BLK, a.N - kb * BLK);
+
+    v4f S[2][8];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      v4f S[8];
+    for (int t = 0; t < 8; ++t) {
+      const v8i kop = lds_row32(Ks, 16 * t + l16, g);
+      S[0][t] = mfma_f8(kop, qop[0], zero);
+      S[1][t] = mfma_f8(kop, qop[1], zero);
+    }
+    const int nvalid = a.N - kb * BLK;
+    if (nvalid < BLK) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = mfma_f8(lds_row32(Ks, 16 * t + l16, g), qop[qs], zero);
-      if (nvalid < BLK) {
+      for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (16 * t + 4 * g + v >= nvalid) S[t][v] = -INFINITY;
-      }
-      float mx = S[0][0];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, S[t][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float tmax = mx * alpha;
-      const float Mo = M[qs];
-      const float Mn = (Mo == -INFINITY || tmax - Mo > a.tau) ? tmax : Mo;
-      const float beta = a.bias - Mn;
-      const float r = (Mo == -INFINITY) ? 0.0f : exp2f((Mo - Mn) * 0.125f);
-      v8i pop;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        uint32_t dw = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) dw |= expcast_byte(S[t][v], alpha, beta) << (8 * v);
-        pop[t] = (int)dw;
-      }
-      const float lb = mfma_f8(ones, pop, zero)[0];
-      if (r != 1.0f) {
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[qs][ct] *= r;
-      }
-      ell[qs] = ell[qs] * r + lb;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[qs][ct][v] += lb * mup_s[16 * ct + 4 * g + v];
-        acc[qs][ct] = mfma_f8(lds_row32(Vs, 16 * ct + l16, g), pop, acc[qs][ct]);
-      }
-      M[qs] = Mn;
+            if (16 * t + 4 * g + v >= nvalid) S[qs][t][v] = -INFINITY;
     }
+    v8i pop[2];
+    pop[0] = softmax_codes(S[0], rs[0], alpha, a.bias, a.tau);
+    pop[1] = softmax_codes(S[1], rs[1], alpha, a.bias, a.tau);
+
+    // ones in A row kb%16: the block's row sum accumulates in L element v of
+    // lane group g where 4g+v = kb%16
+    const int onesrow = kb & 15;
+    const int o = (l16 == onesrow) ? 0x38383838 : 0;
+    v8i onesop;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) onesop[i] = o;
+    rs[0].L = mfma_f8(onesop, pop[0], rs[0].L);
+    rs[1].L = mfma_f8(onesop, pop[1], rs[1].L);
+
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const v8i vop = lds_row32(Vs, 16 * ct + l16, g);
+      rs[0].acc[ct] = mfma_f8(vop, pop[0], rs[0].acc[ct]);
+      rs[1].acc[ct] = mfma_f8(vop, pop[1], rs[1].acc[ct]);
+    }
+    if (onesrow == 15 || kb + 1 == a.nblk) {
+      const uint16_t* grp = mupt + (size_t)(kb >> 4) * 2 * D * 16;
+      restore_group(rs[0], grp, l16, g);
+      restore_group(rs[1], grp, l16, g);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   // Repair: the selected tokens' residual error, weighted by codes formed with
   // the final row maximum and each token's own K block scale; l is unchanged.
   for (int grp = 0; grp < a.mpad / BLK; ++grp) {
-    __syncthreads();
+    uint8_t* Ks = smem[0][0];
     const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -194,32 +310,31 @@ __global__ __launch_bounds__(256) void k_fwd(Args a) {
     const uint16_t* dt = a.rep_dt + (size_t)bh * D * a.mpad + (size_t)grp * BLK;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      v4f S[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = mfma_f8(lds_row32(Ks, 16 * t + l16, g), qop[qs], zero);
-      const float beta = a.bias - M[qs];
-      uint16_t pb[8][4];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t code = expcast_byte(S[t][v], alpha_s[16 * t + 4 * g + v], beta);
-          // E4M3 values are exact in bf16
-          pb[t][v] = f2bf_rne(__builtin_amdgcn_cvt_f32_fp8((int)code, 0));
-        }
-#pragma unroll
+      const float beta = a.bias - rs[qs].M;
+#pragma unroll 1
       for (int u = 0; u < 4; ++u) {
+        // key tiles 2u and 2u+1 feed the 32-key chunk u of the bf16 MFMA: lane
+        // group g holds slots 16(2u+t')+4g+v at K positions 8g+4t'+v
         v8bf bop;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bop[i] = __builtin_bit_cast(__bf16, pb[2 * u + (i >> 2)][i & 3]);
+        for (int tp = 0; tp < 2; ++tp) {
+          const int t = 2 * u + tp;
+          const v4f S = mfma_f8(lds_row32(Ks, 16 * t + l16, g), qop[qs], zero);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t code = expcast_byte(S[v], alpha_s[16 * t + 4 * g + v], beta);
+            // E4M3 values are exact in bf16
+            bop[4 * tp + v] = __builtin_bit_cast(__bf16, f2bf_rne(__builtin_amdgcn_cvt_f32_fp8((int)code, 0)));
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const uint4 av = *reinterpret_cast<const uint4*>(dt + (size_t)(16 * ct + l16) * a.mpad + 32 * u + 8 * g);
-          const v8bf aop = __builtin_bit_cast(v8bf, av);
-          acc[qs][ct] = mfma_bf16(aop, bop, acc[qs][ct]);
+          rs[qs].acc[ct] = mfma_bf16_k32(__builtin_bit_cast(v8bf, av), bop, rs[qs].acc[ct]);
         }
       }
     }
+    __syncthreads();
   }
 
   // Epilogue: O = sV * acc / l, bf16, scattered back to the original row.
@@ -229,16 +344,17 @@ __global__ __launch_bounds__(256) void k_fwd(Args a) {
     const int p = qb * BLK + w * 32 + qs * 16 + l16;
     if (p < a.N) {
       const int orig = (a.flags & VC_PERMUTE_Q) ? a.perm[(size_t)bh * a.N + p] : p;
-      const float il = 1.0f / ell[qs];
+      const float il = 1.0f / rs[qs].ell;
       uint16_t* orow = a.o + ((size_t)bh * a.N + orig) * D;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
         const int c = 16 * ct + 4 * g;
+        const float4 s4 = *reinterpret_cast<const float4*>(sv + c);
         uint2 pk;
-        pk.x = (uint32_t)f2bf_rne(sv[c] * acc[qs][ct][0] * il) |
-               ((uint32_t)f2bf_rne(sv[c + 1] * acc[qs][ct][1] * il) << 16);
-        pk.y = (uint32_t)f2bf_rne(sv[c + 2] * acc[qs][ct][2] * il) |
-               ((uint32_t)f2bf_rne(sv[c + 3] * acc[qs][ct][3] * il) << 16);
+        pk.x = (uint32_t)f2bf_rne(s4.x * rs[qs].acc[ct][0] * il) |
+               ((uint32_t)f2bf_rne(s4.y * rs[qs].acc[ct][1] * il) << 16);
+        pk.y = (uint32_t)f2bf_rne(s4.z * rs[qs].acc[ct][2] * il) |
+               ((uint32_t)f2bf_rne(s4.w * rs[qs].acc[ct][3] * il) << 16);
         *reinterpret_cast<uint2*>(orow + c) = pk;
       }
     }

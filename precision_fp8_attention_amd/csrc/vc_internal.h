@@ -19,7 +19,7 @@ constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 
 // Shape derived from the public parameters.
 struct Shape {
-  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm;
+  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
 };
 
 // Workspace header (first 256 bytes of the workspace).
@@ -36,7 +36,7 @@ struct Args {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm;
+  int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
   uint32_t flags;
   uint64_t seed;
   float c0;    // 8*log2(e)*softmax scale, fp32
@@ -59,6 +59,7 @@ struct Args {
   float* mu;
   float* bamax;
   float* mup;
+  uint16_t* mupt;  // [BH][nch16][2][128][16] bf16 hi/lo of mup
   float* sv;
   float* inv;
   uint8_t* v8t;

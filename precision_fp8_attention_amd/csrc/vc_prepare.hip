@@ -423,19 +423,58 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
   }
 }
 
-// Per-channel residual scales and block means in code units.  grid BH, 128 threads.
+// Per-channel residual scales.  grid BH, 128 threads (one per channel).
 __global__ __launch_bounds__(128) void k_v_scale(Args a) {
   const int bh = blockIdx.x, c = threadIdx.x;
-  float A = 0.0f;
-  for (int b = 0; b < a.nblk; ++b) A = fmaxf(A, a.bamax[((size_t)bh * a.nblk + b) * D + c]);
+  const float* bm = a.bamax + (size_t)bh * a.nblk * D + c;
+  float A[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  int b = 0;
+  for (; b + 8 <= a.nblk; b += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = fmaxf(A[i], bm[(size_t)(b + i) * D]);
+  }
+  for (; b < a.nblk; ++b) A[0] = fmaxf(A[0], bm[(size_t)b * D]);
+  const float amax = fmaxf(fmaxf(fmaxf(A[0], A[1]), fmaxf(A[2], A[3])),
+                           fmaxf(fmaxf(A[4], A[5]), fmaxf(A[6], A[7])));
   float s, inv;
-  scale_from_amax(A, &s, &inv);
+  scale_from_amax(amax, &s, &inv);
   a.sv[(size_t)bh * D + c] = s;
   a.inv[(size_t)bh * D + c] = inv;
-  for (int b = 0; b < a.nblk; ++b) {
-    const size_t o = ((size_t)bh * a.nblk + b) * D + c;
-    a.mup[o] = a.mu[o] * inv;
+}
+
+// Block means in V code units (mu * inv), fp32 and as a bf16 high/low pair in
+// groups of 16 blocks, channel-major (the restore MFMA reads 4 blocks of one
+// channel per lane).  grid (nch16, BH), 128 threads (one per channel).
+__global__ __launch_bounds__(128) void k_v_mup(Args a) {
+  const int grp = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+  const float inv = a.inv[(size_t)bh * D + c];
+  uint32_t hi[8], lo[8];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    float x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int b = grp * 16 + j + e;
+      x[e] = 0.0f;
+      if (b < a.nblk) {
+        const size_t o = ((size_t)bh * a.nblk + b) * D + c;
+        x[e] = a.mu[o] * inv;
+        a.mup[o] = x[e];
+      }
+    }
+    const uint16_t h0 = f2bf_rne(x[0]), h1 = f2bf_rne(x[1]);
+    const uint16_t l0 = f2bf_rne(x[0] - __uint_as_float((uint32_t)h0 << 16));
+    const uint16_t l1 = f2bf_rne(x[1] - __uint_as_float((uint32_t)h1 << 16));
+    hi[j / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[j / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
   }
+  uint16_t* base = a.mupt + (((size_t)bh * a.nch16 + grp) * 2) * D * 16;
+  uint4* dh = reinterpret_cast<uint4*>(base + (size_t)c * 16);
+  uint4* dl = reinterpret_cast<uint4*>(base + (size_t)D * 16 + (size_t)c * 16);
+  dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+  dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
 }
 
 // Residual codes (channel-major, interleaved) and the repair criterion.
@@ -622,6 +661,7 @@ hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
   hipLaunchKernelGGL(k_qk_quant, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
   if (a.m > 0) {
     hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);

@@ -25,11 +25,15 @@
  *
  * Readings taken where the pages are silent (each is also listed in the design
  * notes of the repository):
- *   - k-means is Lloyd's algorithm with a fixed iteration count, Forgy initial
- *     centroids drawn by a seeded splitmix64 partial Fisher-Yates shuffle, squared
- *     L2 distance evaluated as ||c||^2 - 2 v.c with explicit fp32 fma chains in
- *     channel order, ties to the lowest cluster id, empty clusters keep their
- *     centroid, labels taken from the last assignment.
+ *   - k-means is Lloyd's algorithm with a fixed iteration count on fixed-point
+ *     values: per (batch, head) every value is scaled by 2^sh, the largest power
+ *     of two that keeps max|v| * 2^sh below 2^13, and rounded to an integer u
+ *     (the "lightweight" clustering: 14-bit values, exact integer distances).
+ *     Forgy initial centroids are drawn by a seeded splitmix64 partial
+ *     Fisher-Yates shuffle; the distance is ||c||^2 - 2 u.c computed exactly in
+ *     integers; ties go to the lowest cluster id; a non-empty cluster moves to
+ *     the mean of its members rounded to the nearest integer (ties to even), an
+ *     empty one keeps its centroid; labels are those of the last assignment.
  *   - means (K channel mean, V block means, centroids) are exact sums of values
  *     rounded to 2^-24 fixed point, divided once in fp64, rounded to fp32.
  *   - the permutation is a stable sort of positions by cluster id; Q follows it
@@ -213,33 +217,48 @@ void oc_kmeans_init_indices(uint64_t seed, int64_t head, int32_t N, int32_t C, i
   free(idx);
 }
 
+/* Fixed-point exponent of one head: max|v| * 2^sh < 2^13 <= 2 * max|v| * 2^sh. */
+int oc_kmeans_shift(const float *v, int64_t n) {
+  float a = 0.0f;
+  int e;
+  for (int64_t i = 0; i < n; ++i)
+    if (fabsf(v[i]) > a) a = fabsf(v[i]);
+  if (a == 0.0f) return 0;
+  frexpf(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  return 13 - e;
+}
+
 static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d]*/,
                         int32_t *labels, float *cent /*[C][d]*/) {
   const int N = P->N, d = P->d, C = P->C;
+  const int sh = oc_kmeans_shift(v, (int64_t)N * d);
   int32_t *init = (int32_t *)malloc(sizeof(int32_t) * (size_t)C);
-  float *cc = (float *)malloc(sizeof(float) * (size_t)C);
+  int32_t *u = (int32_t *)malloc(sizeof(int32_t) * (size_t)N * d);
+  int64_t *c = (int64_t *)malloc(sizeof(int64_t) * (size_t)C * d);
+  int64_t *cc = (int64_t *)malloc(sizeof(int64_t) * (size_t)C);
   int64_t *sum = (int64_t *)malloc(sizeof(int64_t) * (size_t)C * d);
   int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * (size_t)C);
 
+  for (size_t i = 0; i < (size_t)N * d; ++i) u[i] = (int32_t)llrintf(ldexpf(v[i], sh));
   oc_kmeans_init_indices(P->seed, head, N, C, init);
   for (int k = 0; k < C; ++k)
-    for (int c = 0; c < d; ++c) cent[(size_t)k * d + c] = v[(size_t)init[k] * d + c];
+    for (int ch = 0; ch < d; ++ch) c[(size_t)k * d + ch] = u[(size_t)init[k] * d + ch];
 
   for (int it = 0; it < P->T; ++it) {
-    /* assignment step: argmin_k ||c_k||^2 - 2 v.c_k */
+    /* assignment step: argmin_k ||c_k||^2 - 2 u.c_k, exact integers */
     for (int k = 0; k < C; ++k) {
-      float s = 0.0f;
-      for (int c = 0; c < d; ++c) s = fmaf(cent[(size_t)k * d + c], cent[(size_t)k * d + c], s);
+      int64_t s = 0;
+      for (int ch = 0; ch < d; ++ch) s += c[(size_t)k * d + ch] * c[(size_t)k * d + ch];
       cc[k] = s;
     }
     for (int j = 0; j < N; ++j) {
-      const float *vj = v + (size_t)j * d;
+      const int32_t *uj = u + (size_t)j * d;
       int best = 0;
-      float bestD = 0.0f;
+      int64_t bestD = 0;
       for (int k = 0; k < C; ++k) {
-        float dot = 0.0f, D;
-        for (int c = 0; c < d; ++c) dot = fmaf(vj[c], cent[(size_t)k * d + c], dot);
-        D = fmaf(-2.0f, dot, cc[k]);
+        int64_t dot = 0, D;
+        for (int ch = 0; ch < d; ++ch) dot += (int64_t)uj[ch] * c[(size_t)k * d + ch];
+        D = cc[k] - 2 * dot;
         if (k == 0 || D < bestD) {
           best = k;
           bestD = D;
@@ -247,19 +266,24 @@ static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d
       }
       labels[j] = best;
     }
-    /* update step: each non-empty cluster moves to the mean of its members */
+    /* update step: each non-empty cluster moves to the rounded mean of its members */
     memset(sum, 0, sizeof(int64_t) * (size_t)C * d);
     memset(cnt, 0, sizeof(int64_t) * (size_t)C);
     for (int j = 0; j < N; ++j) {
       int k = labels[j];
       cnt[k] += 1;
-      for (int c = 0; c < d; ++c) sum[(size_t)k * d + c] += fx24(v[(size_t)j * d + c]);
+      for (int ch = 0; ch < d; ++ch) sum[(size_t)k * d + ch] += u[(size_t)j * d + ch];
     }
     for (int k = 0; k < C; ++k)
       if (cnt[k] > 0)
-        for (int c = 0; c < d; ++c) cent[(size_t)k * d + c] = fixed_mean(sum[(size_t)k * d + c], cnt[k]);
+        for (int ch = 0; ch < d; ++ch) /* |sum| < 2^34: the quotient rounds once, exactly */
+          c[(size_t)k * d + ch] = llrint((double)sum[(size_t)k * d + ch] / (double)cnt[k]);
   }
+  for (int k = 0; k < C; ++k)
+    for (int ch = 0; ch < d; ++ch) cent[(size_t)k * d + ch] = ldexpf((float)c[(size_t)k * d + ch], -sh);
   free(init);
+  free(u);
+  free(c);
   free(cc);
   free(sum);
   free(cnt);

@@ -152,14 +152,34 @@ def _lloyd_fp64(v, init_idx, T):
         for kk in range(cent.shape[0]):
             if np.any(lab == kk):
                 cent[kk] = v[lab == kk].mean(0)
-        if margin < 1e-3:
+        if margin < 1e-2 * max(1.0, np.abs(v).max() ** 2):
             return None, None
     return lab, cent
 
 
+def _lloyd_fixed_numpy(v, init_idx, T):
+    """Independent integer Lloyd: values scaled by the largest power of two
+    keeping max|v| below 2^13, exact int64 distances, ties to the lowest id,
+    rounded (half to even) integer means."""
+    a = np.abs(v).max()
+    sh = 13 - int(np.frexp(a)[1]) if a > 0 else 0
+    u = np.rint(v * 2.0 ** sh).astype(np.int64)
+    c = u[init_idx].copy()
+    lab = None
+    for _ in range(T):
+        d = (c * c).sum(1)[None, :] - 2 * (u @ c.T)
+        lab = np.argmin(d, axis=1)  # first minimum = lowest id
+        for kk in range(c.shape[0]):
+            sel = lab == kk
+            if sel.any():
+                c[kk] = np.rint(u[sel].sum(0) / sel.sum()).astype(np.int64)
+    return lab, c.astype(np.float64) * 2.0 ** -sh
+
+
 def test_kmeans_tiny_brute_force():
-    """Labels of the oracle's fp32 Lloyd equal an independent fp64 Lloyd from the
-    same initial indices on tiny inputs without near ties."""
+    """Labels and centroids equal an independent integer Lloyd from the same
+    initial indices; where no assignment is near a tie they also equal the
+    real-valued fp64 Lloyd (the fixed-point grid is 2^-13 of max|v|)."""
     checked = 0
     for seed in range(40):
         N = 4 + seed % 7
@@ -169,13 +189,29 @@ def test_kmeans_tiny_brute_force():
         P = orc.make_params(1, 1, N, C_=C_, T=T, seed=seed, rho=0.0)
         pr = orc.prepare(P, q, k, v)
         vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
-        lab, cent = _lloyd_fp64(vf, orc.kmeans_init_indices(seed, 0, N, C_), T)
+        init = orc.kmeans_init_indices(seed, 0, N, C_)
+        lab_i, cent_i = _lloyd_fixed_numpy(vf, init, T)
+        assert np.array_equal(pr["labels"][0], lab_i)
+        assert np.array_equal(pr["centroids"][0].astype(np.float64), cent_i)
+        lab, cent = _lloyd_fp64(vf, init, T)
         if lab is None:
             continue
         checked += 1
         assert np.array_equal(pr["labels"][0], lab)
-        np.testing.assert_allclose(pr["centroids"][0], cent, rtol=1e-6, atol=1e-6)
-    assert checked >= 25
+        np.testing.assert_allclose(pr["centroids"][0], cent, rtol=0, atol=2.0 ** -12 * np.abs(vf).max())
+    assert checked >= 20
+
+
+def test_kmeans_fixed_point_larger_head():
+    """Exact agreement with the independent integer Lloyd on a head with
+    outliers (many clusters, several iterations)."""
+    q, k, v = inputs.make_custom(1, 1, 900, seed=31, rate=0.02, sigma=30.0)
+    P = orc.make_params(1, 1, 900, C_=12, T=6, seed=4, rho=0.0)
+    pr = orc.prepare(P, q, k, v)
+    vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+    lab, cent = _lloyd_fixed_numpy(vf, orc.kmeans_init_indices(4, 0, 900, 12), 6)
+    assert np.array_equal(pr["labels"][0], lab)
+    assert np.array_equal(pr["centroids"][0].astype(np.float64), cent)
 
 
 def test_kmeans_recovers_planted_blobs():

@@ -104,6 +104,8 @@ typedef struct {
   size_t iperm;      /* i32 [BH][N] original token -> position                   */
   size_t q8;         /* u8  [BH][Npad][128] Q codes, position order               */
   size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order      */
+  size_t k16;        /* bf16 [BH][Npad][128] the same codes decoded (exact in bf16),
+                        operand of the exactly-accumulated score MFMA             */
   size_t sq;         /* f32 [BH][nblk] Q block scales                            */
   size_t sk;         /* f32 [BH][nblk] K block scales                            */
   size_t mu;         /* f32 [BH][nblk][128] V block means (real units)           */

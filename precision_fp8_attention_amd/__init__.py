@@ -29,7 +29,7 @@ class Params(C.Structure):
 
 
 LAYOUT_FIELDS = ("total", "header", "kbar", "ksum", "init_idx", "centroids", "labels", "perm",
-                 "iperm", "q8", "k8", "sq", "sk", "mu", "bamax", "mup", "mupt", "sv", "inv", "v8t", "err",
+                 "iperm", "q8", "k8", "k16", "sq", "sk", "mu", "bamax", "mup", "mupt", "sv", "inv", "v8t", "err",
                  "rep_pos", "rep_dt")
 
 

@@ -65,13 +65,19 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.ksum = take(BH * (size_t)s.nkc * D * 8);
   L.init_idx = take(BH * C * 4);
   L.centroids = take(BH * C * D * 4);
-  out->kmpart = take(BH * (size_t)s.nkm * C * D * 8);
+  out->kmpart = take(BH * (size_t)s.nkm * C * D * 4);
   out->kmcnt = take(BH * (size_t)s.nkm * C * 4);
+  out->vmaxp = take(BH * (size_t)s.nkc * 4);
+  out->kmsh = take(BH * 4);
+  out->uhi = take(BH * N * D);
+  out->ulo = take(BH * N * D);
+  out->centfix = take(BH * C * D * 4);
   L.labels = take(BH * N * 4);
   L.perm = take(BH * N * 4);
   L.iperm = take(BH * N * 4);
   L.q8 = take(BH * Np * D);
   L.k8 = take(BH * Np * D);
+  L.k16 = take(BH * Np * D * 2);
   L.sq = take(BH * nb * 4);
   L.sk = take(BH * nb * 4);
   L.mu = take(BH * nb * D * 4);
@@ -116,13 +122,19 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.ksum = reinterpret_cast<long long*>(b + L.ksum);
   a.init_idx = reinterpret_cast<int*>(b + L.init_idx);
   a.cent = reinterpret_cast<float*>(b + L.centroids);
-  a.kmpart = reinterpret_cast<long long*>(b + FL.kmpart);
+  a.kmpart = reinterpret_cast<int*>(b + FL.kmpart);
   a.kmcnt = reinterpret_cast<int*>(b + FL.kmcnt);
+  a.vmaxp = reinterpret_cast<float*>(b + FL.vmaxp);
+  a.kmsh = reinterpret_cast<int*>(b + FL.kmsh);
+  a.uhi = reinterpret_cast<int8_t*>(b + FL.uhi);
+  a.ulo = reinterpret_cast<int8_t*>(b + FL.ulo);
+  a.centfix = reinterpret_cast<int*>(b + FL.centfix);
   a.labels = reinterpret_cast<int*>(b + L.labels);
   a.perm = reinterpret_cast<int*>(b + L.perm);
   a.iperm = reinterpret_cast<int*>(b + L.iperm);
   a.q8 = b + L.q8;
   a.k8 = b + L.k8;
+  a.k16 = reinterpret_cast<uint16_t*>(b + L.k16);
   a.sq = reinterpret_cast<float*>(b + L.sq);
   a.sk = reinterpret_cast<float*>(b + L.sk);
   a.mu = reinterpret_cast<float*>(b + L.mu);

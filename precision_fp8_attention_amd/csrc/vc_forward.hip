@@ -3,7 +3,7 @@
 // Method (noticiai.com.br VC-Attention article, sections "V-Smooth" (Restore) and
 // "ExpCast-FP8"; ip73.fr article, section "Le compromis entre vitesse et
 // fidelite" (repair)):
-//   S_raw = Q8 . K8^T                       FP8 MFMA, fp32 accumulate
+//   S_raw = Q8 . K8^T   exact products of the E4M3 codes, fp32 accumulation
 //   M     = running row maximum in ExpCast code units, moved once per 128-key
 //           block (only when the block maximum exceeds it by more than tau)
 //   code  = clamp(rne(fma(S_raw, alpha, 56 + 8k - M)), 0, 126)   -- the E4M3 byte
@@ -13,14 +13,22 @@
 //   after the loop the repaired tokens add P(final M) . delta (bf16 MFMA), and
 //   O = sV * acc / l, written as bf16 to the token's original row.
 //
-// Layout.  A workgroup of 4 waves owns one 128-row query block; wave w owns rows
-// 32w..32w+31 as two 16-row subtiles.  Scores are computed transposed
-// (S^T = K8 . Q8^T on v_mfma_f32_16x16x128_f8f6f4) so each lane holds 32 keys of
-// one query: key 16t+4g+v of the block in S[t][v], g = lane/16.  Those 32 ExpCast
-// bytes are exactly the lane's B operand of O^T = V8^T . P^T because prepare
-// stores V8 channel-major with the same key interleave, so P never touches LDS.
+// Layout.  A workgroup of 8 waves owns two 128-row query blocks; wave w owns
+// rows 32w..32w+31 as two 16-row subtiles.  Scores are computed transposed
+// (S^T = K . Q^T) so each lane holds 32 keys of one query: key 16t+4g+v of the
+// block in S[t][v], g = lane/16.  Those 32 ExpCast bytes are exactly the lane's
+// B operand of O^T = V8^T . P^T on v_mfma_f32_16x16x128_f8f6f4, because prepare
+// stores V8 channel-major with the same key interleave: P never touches LDS.
 // v_cvt_pk_u8_f32 rounds to nearest even, saturates to [0, 255] and inserts the
 // byte, so one fma and one convert produce each packed code.
+//
+// Scores.  The codes are decisions, so S must be the exact dot product rounded
+// once: gfx950's FP8 MFMA accumulates 128 products with about 11 bits relative to
+// the largest one, which moves ExpCast codes across rounding boundaries.  The
+// E4M3 codes are therefore multiplied as bf16 (every E4M3 value is exact in
+// bf16) on v_mfma_f32_16x16x32_bf16, whose fp32 accumulation is accurate to the
+// last bits; PV, whose error only perturbs the accumulator by ~1e-5, stays on
+// the FP8 MFMA.
 //
 // Row sums and restore.  One more MFMA per block multiplies P by a ones row:
 // block b of a 16-block group puts its ones in A row b%16, so the group's row
@@ -29,8 +37,8 @@
 // MFMA group adds sum_b l_b * mu'_b to the accumulator: the restore costs no
 // per-element VALU work and no second pass over the keys.
 //
-// K/V tiles (16 KB each) are double-buffered in LDS and filled by direct
-// global->LDS loads while the previous block is computed.
+// K tiles (bf16 codes, 32 KB) and V tiles (E4M3, 16 KB) are double-buffered in
+// LDS and filled by direct global->LDS loads while the previous block runs.
 #include "vc_internal.h"
 
 namespace vc {
@@ -64,6 +72,21 @@ __device__ __forceinline__ v8i lds_row32(const uint8_t* tile, int row, int g) {
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
   return r;
+}
+
+// 8 bf16 (16 bytes) of row `row` of a 128x128 bf16 tile: K positions
+// 32kc+8g..32kc+8g+7, i.e. 16-byte chunk 4kc+g, XOR-swizzled by row%16.
+__device__ __forceinline__ v8bf lds_k16(const uint8_t* tile, int row, int kc, int g) {
+  const uint4 x = *reinterpret_cast<const uint4*>(tile + row * 256 + (((4 * kc + g) ^ (row & 15)) << 4));
+  return __builtin_bit_cast(v8bf, x);
+}
+
+// S^T tile (16 keys x 16 queries) from bf16 K rows and the query operand.
+__device__ __forceinline__ v4f score_tile(const uint8_t* Kt, int row, int g, const v8bf (&qop)[4]) {
+  v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) s = mfma_bf16_k32(lds_k16(Kt, row, kc, g), qop[kc], s);
+  return s;
 }
 
 __device__ __forceinline__ uint32_t expcast_byte(float s, float alpha, float beta) {
@@ -186,41 +209,64 @@ __device__ __forceinline__ void restore_group(RowState& st, const uint16_t* mupt
   st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-__global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
-  __shared__ __align__(1024) uint8_t smem[2][2][BLK * D];  // [stage][K, V]
-  __shared__ float alpha_s[BLK];
+__global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
+  __shared__ __align__(1024) uint8_t ksm[2][BLK * D * 2];  // [stage] bf16 K rows
+  __shared__ __align__(1024) uint8_t vsm[2][D * BLK];      // [stage] V^T codes
+  __shared__ float alpha_s[2][BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  const int npair = (a.nblk + 1) / 2;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.nblk, qb = logical % a.nblk;
+  const int bh = logical / npair, qb = 2 * (logical % npair) + (w >> 2);
+  const bool active = qb < a.nblk;  // the second block of an odd count is empty
+  const int qbv = active ? qb : qb - 1;
+  const int wq = w & 3;             // wave within its query block
 
-  const uint8_t* q8 = a.q8 + ((size_t)bh * a.Npad + (size_t)qb * BLK) * D;
-  const uint8_t* k8 = a.k8 + (size_t)bh * a.Npad * D;
+  const uint8_t* q8 = a.q8 + ((size_t)bh * a.Npad + (size_t)qbv * BLK) * D;
+  const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D);
   const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
   const float* sk = a.sk + (size_t)bh * a.nblk;
   const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
-  const float sQa = a.sq[(size_t)bh * a.nblk + qb];
+  const float sQa = a.sq[(size_t)bh * a.nblk + qbv];
 
-  // direct global->LDS loads of one block's K rows and V^T columns: wave w,
-  // instruction i fills 1 KB region r = 4i+w (8 rows); lane l lands at byte 16l,
-  // i.e. row 8r + l/8, stored chunk l%8, which holds source chunk (l%8)^(row%8)
+  // direct global->LDS loads of one key block: K (32 KB) as 32 regions of 4 rows,
+  // V^T (16 KB) as 16 regions of 8 rows; a lane lands at byte 16*lane of its
+  // region, i.e. in stored chunk lane%16 (K) or lane%8 (V) of its row, which
+  // holds the source chunk XOR the row's swizzle
   auto issue = [&](int kb, int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * i + w;
+      const int r = 8 * i + w;
+      const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
+      __builtin_amdgcn_global_load_lds(k16 + ((size_t)kb * BLK + row) * 256 + cc * 16,
+                                       &ksm[st][r * 1024], 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * i + w;
       const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ (row & 7);
-      __builtin_amdgcn_global_load_lds(k8 + ((size_t)kb * BLK + row) * D + cc * 16,
-                                       &smem[st][0][r * 1024], 16, 0, 0);
       __builtin_amdgcn_global_load_lds(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16,
-                                       &smem[st][1][r * 1024], 16, 0, 0);
+                                       &vsm[st][r * 1024], 16, 0, 0);
     }
   };
 
-  v8i qop[2];
+  // query operand: bf16 of the Q codes, lane (g, q) holds d = 32kc+8g..+7
+  v8bf qop[2][4];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
-    qop[qs] = *reinterpret_cast<const v8i*>(q8 + (size_t)(w * 32 + qs * 16 + l16) * D + 32 * g);
+  for (int qs = 0; qs < 2; ++qs) {
+    const uint8_t* qrow = q8 + (size_t)(wq * 32 + qs * 16 + l16) * D;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint2 b = *reinterpret_cast<const uint2*>(qrow + 32 * kc + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = ((i < 4 ? b.x : b.y) >> (8 * (i & 3))) & 0xffu;
+        qop[qs][kc][i] = __builtin_bit_cast(
+            __bf16, (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0)) >> 16));
+      }
+    }
+  }
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   RowState rs[2];
@@ -240,16 +286,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
   for (int kb = 0; kb < a.nblk; ++kb) {
     const int st = kb & 1;
     if (kb + 1 < a.nblk) issue(kb + 1, st ^ 1);
-    const uint8_t* Ks = smem[st][0];
-    const uint8_t* Vs = smem[st][1];
+    const uint8_t* Ks = ksm[st];
+    const uint8_t* Vs = vsm[st];
     const float alpha = (sQa * sk[kb]) * a.c0;
 
     v4f S[2][8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const v8i kop = lds_row32(Ks, 16 * t + l16, g);
-      S[0][t] = mfma_f8(kop, qop[0], zero);
-      S[1][t] = mfma_f8(kop, qop[1], zero);
+      S[0][t] = zero;
+      S[1][t] = zero;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const v8bf kop = lds_k16(Ks, 16 * t + l16, kc, g);
+        S[0][t] = mfma_bf16_k32(kop, qop[0][kc], S[0][t]);
+        S[1][t] = mfma_bf16_k32(kop, qop[1][kc], S[1][t]);
+      }
     }
     const int nvalid = a.N - kb * BLK;
     if (nvalid < BLK) {
@@ -293,20 +344,24 @@ __global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
   // Repair: the selected tokens' residual error, weighted by codes formed with
   // the final row maximum and each token's own K block scale; l is unchanged.
   for (int grp = 0; grp < a.mpad / BLK; ++grp) {
-    uint8_t* Ks = smem[0][0];
+    uint8_t* Ks = ksm[0];
     const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, cc = ch & 7;
+      const int ch = tid + 512 * i, row = ch >> 4, cc = ch & 15;
       const int pos = rp[row];
-      const uint4 kv = *reinterpret_cast<const uint4*>(k8 + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
-      *reinterpret_cast<uint4*>(Ks + row * D + ((cc ^ (row & 7)) << 4)) = kv;
+      const uint4 kv = *reinterpret_cast<const uint4*>(k16 + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
+      *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
     }
     if (tid < BLK) {
       const int pos = rp[tid];
-      alpha_s[tid] = (sQa * sk[pos < 0 ? 0 : pos / BLK]) * a.c0;
+      const float sk_pos = sk[pos < 0 ? 0 : pos / BLK];
+      alpha_s[0][tid] = (a.sq[(size_t)bh * a.nblk + 2 * (logical % npair)] * sk_pos) * a.c0;
+      const int qb1 = min(2 * (logical % npair) + 1, a.nblk - 1);
+      alpha_s[1][tid] = (a.sq[(size_t)bh * a.nblk + qb1] * sk_pos) * a.c0;
     }
     __syncthreads();
+    const float* al = alpha_s[w >> 2];
     const uint16_t* dt = a.rep_dt + (size_t)bh * D * a.mpad + (size_t)grp * BLK;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -319,10 +374,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           const int t = 2 * u + tp;
-          const v4f S = mfma_f8(lds_row32(Ks, 16 * t + l16, g), qop[qs], zero);
+          const v4f S = score_tile(Ks, 16 * t + l16, g, qop[qs]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t code = expcast_byte(S[v], alpha_s[16 * t + 4 * g + v], beta);
+            const uint32_t code = expcast_byte(S[v], al[16 * t + 4 * g + v], beta);
             // E4M3 values are exact in bf16
             bop[4 * tp + v] = __builtin_bit_cast(__bf16, f2bf_rne(__builtin_amdgcn_cvt_f32_fp8((int)code, 0)));
           }
@@ -341,8 +396,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
   const float* sv = a.sv + (size_t)bh * D;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    const int p = qb * BLK + w * 32 + qs * 16 + l16;
-    if (p < a.N) {
+    const int p = qb * BLK + wq * 32 + qs * 16 + l16;
+    if (active && p < a.N) {
       const int orig = (a.flags & VC_PERMUTE_Q) ? a.perm[(size_t)bh * a.N + p] : p;
       const float il = 1.0f / rs[qs].ell;
       uint16_t* orow = a.o + ((size_t)bh * a.N + orig) * D;
@@ -364,8 +419,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(Args a) {
 }  // namespace
 
 hipError_t launch_forward(const Args& a, hipStream_t st) {
-  const unsigned tiles = (unsigned)a.BH * (unsigned)a.nblk;
-  hipLaunchKernelGGL(k_fwd, dim3(tiles), dim3(256), 0, st, a);
+  const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
+  hipLaunchKernelGGL(k_fwd, dim3(tiles), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

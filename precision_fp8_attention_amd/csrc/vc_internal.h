@@ -47,13 +47,19 @@ struct Args {
   long long* ksum;
   int* init_idx;
   float* cent;
-  long long* kmpart;  // [BH][nkm][C][128] fixed-point partial sums of members
+  int* kmpart;        // [BH][nkm][C][128] partial sums of members (fixed point)
   int* kmcnt;         // [BH][nkm][C] member counts
+  float* vmaxp;       // [BH][nkc] partial max |V|
+  int* kmsh;          // [BH] fixed-point exponent of the head
+  int8_t* uhi;        // [BH][N][128] high part (u >> 7) of the fixed-point V
+  int8_t* ulo;        // [BH][N][128] low part (u & 127)
+  int* centfix;       // [BH][C][128] fixed-point centroids
   int* labels;
   int* perm;
   int* iperm;
   uint8_t* q8;
   uint8_t* k8;
+  uint16_t* k16;  // [BH][Npad][128] bf16 of the K codes
   float* sq;
   float* sk;
   float* mu;
@@ -71,7 +77,7 @@ struct Args {
 // Private extension of the public layout (partial k-means sums).
 struct FullLayout {
   vc_attn_ws_layout pub;
-  size_t kmpart, kmcnt;
+  size_t kmpart, kmcnt, vmaxp, kmsh, uhi, ulo, centfix;
 };
 
 bool shape_of(const vc_attn_params* p, Shape* s);

@@ -82,19 +82,24 @@ __device__ __forceinline__ int rep_col(int s) {
 }
 
 // ---------------------------------------------------------------------------
-// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens.
+// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; the same
+// workgroup records max|V| of the chunk (the k-means fixed-point scale).
 // grid (nkc, BH), 256 threads: thread = (row r = t/16, 8-channel group t%16).
 __global__ __launch_bounds__(256) void k_ksum(Args a) {
   __shared__ long long red[16][D];
+  __shared__ float wm[4];
   const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
   const int cg = t & 15, r = t >> 4;
   const int j0 = ch * KSUM_CHUNK, j1 = min(j0 + KSUM_CHUNK, a.N);
   const uint16_t* kh = a.k + (size_t)bh * a.N * D;
+  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
   long long s[8];
+  float vm = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = 0;
   for (int j = j0 + r; j < j1; j += 16) {
     const uint4 u = *reinterpret_cast<const uint4*>(kh + (size_t)j * D + cg * 8);
+    const uint4 w = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + cg * 8);
     s[0] += fx24(bf2f(u.x));
     s[1] += fx24(bf2f(u.x >> 16));
     s[2] += fx24(bf2f(u.y));
@@ -103,15 +108,22 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
     s[5] += fx24(bf2f(u.z >> 16));
     s[6] += fx24(bf2f(u.w));
     s[7] += fx24(bf2f(u.w >> 16));
+    vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
+                         fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
+    vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
+                         fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = s[i];
+  vm = wave_max(vm);
+  if ((t & 63) == 0) wm[t >> 6] = vm;
   __syncthreads();
   if (t < D) {
     long long tot = 0;
     for (int rr = 0; rr < 16; ++rr) tot += red[rr][t];
     a.ksum[((size_t)bh * a.nkc + ch) * D + t] = tot;
   }
+  if (t == 0) a.vmaxp[(size_t)bh * a.nkc + ch] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
 }
 
 // K channel mean.  grid BH, 128 threads.
@@ -123,8 +135,61 @@ __global__ __launch_bounds__(128) void k_kbar(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// k-means initialisation (Forgy): seeded partial Fisher-Yates over [0, N).
-// grid BH, 128 threads.
+// k-means on fixed-point values ("lightweight" clustering): per head every V
+// value is scaled by 2^sh, the largest power of two keeping max|V| * 2^sh below
+// 2^13, and rounded to an integer u; u = 128 * (u >> 7) + (u & 127) with both
+// parts in int8, so u.c is exact on int8 MFMA (four products, int32 partial
+// sums, combined in int64).  Distances ||c||^2 - 2 u.c are exact integers, so
+// the cluster ids do not depend on the order of any accumulation.
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Fixed-point exponent of the head and the int8 planes of u (token order).
+// grid (ceil(N/256), BH), 256 threads: one token per thread.
+__global__ __launch_bounds__(256) void k_vfix(Args a) {
+  __shared__ float wm[4];
+  const int bh = blockIdx.y, t = threadIdx.x;
+  float am = 0.0f;
+  for (int i = t; i < a.nkc; i += 256) am = fmaxf(am, a.vmaxp[(size_t)bh * a.nkc + i]);
+  am = wave_max(am);
+  if ((t & 63) == 0) wm[t >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  int e = 0;
+  if (am > 0.0f) frexpf(am, &e);
+  const int sh = am > 0.0f ? 13 - e : 0;
+  if (blockIdx.x == 0 && t == 0) a.kmsh[bh] = sh;
+  const int j = blockIdx.x * 256 + t;
+  if (j >= a.N) return;
+  const uint16_t* row = a.v + ((size_t)bh * a.N + j) * D;
+  int8_t* hi = a.uhi + ((size_t)bh * a.N + j) * D;
+  int8_t* lo = a.ulo + ((size_t)bh * a.N + j) * D;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(row + 16 * i);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(row + 16 * i + 8);
+    const uint32_t h[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t wh = 0, wl = 0;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t bits = (e2 & 1) ? (h[2 * q + (e2 >> 1)] >> 16) : h[2 * q + (e2 >> 1)];
+        const int u = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
+        wh |= (uint32_t)((u >> 7) & 0xff) << (8 * e2);
+        wl |= (uint32_t)(u & 127) << (8 * e2);
+      }
+      ph[q] = wh;
+      pl[q] = wl;
+    }
+    *reinterpret_cast<uint4*>(hi + 16 * i) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    *reinterpret_cast<uint4*>(lo + 16 * i) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+  }
+}
+
+// Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
+// fixed-point value of token idx[k].  grid BH, 128 threads.
 __global__ __launch_bounds__(128) void k_km_init(Args a) {
   __shared__ int key[2 * MAX_CLUSTERS], val[2 * MAX_CLUSTERS];
   __shared__ int idx[MAX_CLUSTERS];
@@ -148,112 +213,122 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
     }
   }
   __syncthreads();
-  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
-  for (int e = threadIdx.x; e < C * D; e += blockDim.x) {
-    const int kk = e / D, c = e % D;
-    a.cent[(size_t)bh * C * D + e] = bf2f(vh[(size_t)idx[kk] * D + c]);
+  const int sh = a.kmsh[bh];
+  const int c = threadIdx.x;
+  for (int kk = 0; kk < C; ++kk) {
+    const size_t src = ((size_t)bh * a.N + idx[kk]) * D + c;
+    const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
+    a.centfix[((size_t)bh * C + kk) * D + c] = u;
+    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -sh);
   }
-  for (int kk = threadIdx.x; kk < C; kk += blockDim.x) a.init_idx[(size_t)bh * C + kk] = idx[kk];
+  if (c < C) a.init_idx[(size_t)bh * C + c] = idx[c];
 }
 
-// Assignment step plus per-workgroup member sums.
-// grid (nkm, BH), 512 threads, KM_CHUNK tokens per workgroup (2 per thread).
-__global__ __launch_bounds__(512) void k_km_assign(Args a) {
-  __shared__ __align__(16) float cs[MAX_CLUSTERS * D];
-  __shared__ float cn[MAX_CLUSTERS];
-  __shared__ unsigned long long bins[MAX_CLUSTERS * D];
+// Assignment step on int8 MFMA plus per-workgroup member sums.
+// grid (nkm, BH), 256 threads (4 waves x 64 tokens per 256-token pass),
+// KM_CHUNK tokens per workgroup.
+constexpr int CROW = D + 16;  // padded LDS row of a centroid operand (bytes)
+
+__global__ __launch_bounds__(256) void k_km_assign(Args a) {
+  __shared__ __align__(16) int8_t chi[MAX_CLUSTERS * CROW];
+  __shared__ __align__(16) int8_t clo[MAX_CLUSTERS * CROW];
+  __shared__ long long cc[MAX_CLUSTERS];
+  __shared__ int bins[MAX_CLUSTERS * D];
   __shared__ int cnt[MAX_CLUSTERS];
+  __shared__ int slab[256];
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, C = a.C;
-  const float* cent = a.cent + (size_t)bh * C * D;
-  for (int e = t; e < C * D; e += 512) {
-    cs[e] = cent[e];
-    bins[e] = 0ull;
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
+  const int* cf = a.centfix + (size_t)bh * C * D;
+  for (int e = t; e < C * D; e += 256) {
+    const int u = cf[e];
+    chi[(e / D) * CROW + (e % D)] = (int8_t)(u >> 7);
+    clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
+    bins[e] = 0;
   }
-  if (t < C) cnt[t] = 0;
-  __syncthreads();
   if (t < C) {
-    float s = 0.0f;
-    for (int c = 0; c < D; ++c) s = __builtin_fmaf(cs[t * D + c], cs[t * D + c], s);
-    cn[t] = s;
+    long long s = 0;
+    for (int c = 0; c < D; ++c) s += (long long)cf[t * D + c] * cf[t * D + c];
+    cc[t] = s;
+    cnt[t] = 0;
   }
   __syncthreads();
-  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
-  for (int rep = 0; rep < KM_CHUNK / 512; ++rep) {
-    const int j = chunk * KM_CHUNK + rep * 512 + t;
-    if (j < a.N) {
-      float v[D];
+  const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
+  const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
+  const int ntile = (C + 15) / 16;
+  for (int pass = 0; pass < KM_CHUNK / 256; ++pass) {
+    const int base = chunk * KM_CHUNK + pass * 256;
+    if (base >= a.N) break;  // uniform across the workgroup
+#pragma unroll 1
+    for (int ts = 0; ts < 4; ++ts) {
+      const int loc = w * 64 + ts * 16 + l16;  // token within the pass
+      const int j = base + loc;
+      const int jj = j < a.N ? j : a.N - 1;    // tail lanes compute on a valid row
+      v4i bh0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
+      v4i bh1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
+      v4i bl0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
+      v4i bl1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+      long long bestD = 0x7fffffffffffffffll;  // lanes with no valid centroid never win
+      int best = 0x7fffffff;
+      for (int kt = 0; kt < ntile; ++kt) {
+        const int kr = 16 * kt + l16;
+        const int krow = kr < C ? kr : 0;
+        const v4i ah0 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 16 * g);
+        const v4i ah1 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 64 + 16 * g);
+        const v4i al0 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 16 * g);
+        const v4i al1 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 64 + 16 * g);
+        const v4i z = {0, 0, 0, 0};
+        v4i HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bh0, z, 0, 0, 0);
+        HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bh1, HH, 0, 0, 0);
+        v4i HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bl0, z, 0, 0, 0);
+        HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bl1, HL, 0, 0, 0);
+        v4i LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bh0, z, 0, 0, 0);
+        LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, LH, 0, 0, 0);
+        v4i LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bl0, z, 0, 0, 0);
+        LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bl1, LL, 0, 0, 0);
+        // lane (g, token l16) holds centroids 16kt + 4g + v
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const uint4 u = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + i * 8);
-        v[i * 8 + 0] = bf2f(u.x);
-        v[i * 8 + 1] = bf2f(u.x >> 16);
-        v[i * 8 + 2] = bf2f(u.y);
-        v[i * 8 + 3] = bf2f(u.y >> 16);
-        v[i * 8 + 4] = bf2f(u.z);
-        v[i * 8 + 5] = bf2f(u.z >> 16);
-        v[i * 8 + 6] = bf2f(u.w);
-        v[i * 8 + 7] = bf2f(u.w >> 16);
-      }
-      int best = 0;
-      float bestD = 0.0f;
-      int kk = 0;
-      // four independent channel-ordered fma chains at a time
-      for (; kk + 4 <= C; kk += 4) {
-        const float* c0p = cs + kk * D;
-        float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < D; c += 4) {
-          const float4 x0 = *reinterpret_cast<const float4*>(c0p + c);
-          const float4 x1 = *reinterpret_cast<const float4*>(c0p + D + c);
-          const float4 x2 = *reinterpret_cast<const float4*>(c0p + 2 * D + c);
-          const float4 x3 = *reinterpret_cast<const float4*>(c0p + 3 * D + c);
-          d0 = __builtin_fmaf(v[c], x0.x, d0);
-          d1 = __builtin_fmaf(v[c], x1.x, d1);
-          d2 = __builtin_fmaf(v[c], x2.x, d2);
-          d3 = __builtin_fmaf(v[c], x3.x, d3);
-          d0 = __builtin_fmaf(v[c + 1], x0.y, d0);
-          d1 = __builtin_fmaf(v[c + 1], x1.y, d1);
-          d2 = __builtin_fmaf(v[c + 1], x2.y, d2);
-          d3 = __builtin_fmaf(v[c + 1], x3.y, d3);
-          d0 = __builtin_fmaf(v[c + 2], x0.z, d0);
-          d1 = __builtin_fmaf(v[c + 2], x1.z, d1);
-          d2 = __builtin_fmaf(v[c + 2], x2.z, d2);
-          d3 = __builtin_fmaf(v[c + 2], x3.z, d3);
-          d0 = __builtin_fmaf(v[c + 3], x0.w, d0);
-          d1 = __builtin_fmaf(v[c + 3], x1.w, d1);
-          d2 = __builtin_fmaf(v[c + 3], x2.w, d2);
-          d3 = __builtin_fmaf(v[c + 3], x3.w, d3);
+        for (int v = 0; v < 4; ++v) {
+          const int k = 16 * kt + 4 * g + v;
+          if (k < C) {
+            const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
+            const long long Dk = cc[k] - 2 * dot;
+            if (Dk < bestD) { bestD = Dk; best = k; }
+          }
         }
-        const float e0 = __builtin_fmaf(-2.0f, d0, cn[kk]);
-        const float e1 = __builtin_fmaf(-2.0f, d1, cn[kk + 1]);
-        const float e2 = __builtin_fmaf(-2.0f, d2, cn[kk + 2]);
-        const float e3 = __builtin_fmaf(-2.0f, d3, cn[kk + 3]);
-        if (kk == 0 || e0 < bestD) { best = kk; bestD = e0; }
-        if (e1 < bestD) { best = kk + 1; bestD = e1; }
-        if (e2 < bestD) { best = kk + 2; bestD = e2; }
-        if (e3 < bestD) { best = kk + 3; bestD = e3; }
       }
-      for (; kk < C; ++kk) {
-        float d0 = 0.0f;
+      // argmin across the four lane groups; ties go to the lower id
 #pragma unroll
-        for (int c = 0; c < D; ++c) d0 = __builtin_fmaf(v[c], cs[kk * D + c], d0);
-        const float e0 = __builtin_fmaf(-2.0f, d0, cn[kk]);
-        if (kk == 0 || e0 < bestD) { best = kk; bestD = e0; }
+      for (int off = 16; off <= 32; off <<= 1) {
+        const long long oD = __shfl_xor(bestD, off, 64);
+        const int ob = __shfl_xor(best, off, 64);
+        if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
       }
-      a.labels[(size_t)bh * a.N + j] = best;
-      atomicAdd(&cnt[best], 1);
-#pragma unroll
-      for (int c = 0; c < D; ++c)
-        atomicAdd(&bins[best * D + c], (unsigned long long)fx24(v[c]));
+      if (g == 0) {
+        slab[loc] = best;
+        if (j < a.N) a.labels[(size_t)bh * a.N + j] = best;
+      }
     }
+    __syncthreads();
+    // member sums: thread = (channel t%128, token parity t/128)
+    {
+      const int c = t & 127, par = t >> 7;
+      const int n = min(256, a.N - base);
+#pragma unroll 4
+      for (int i = par; i < n; i += 2) {
+        const size_t o = (size_t)(base + i) * D + c;
+        atomicAdd(&bins[slab[i] * D + c], 128 * (int)uhi[o] + (int)ulo[o]);
+      }
+      if (t < n) atomicAdd(&cnt[slab[t]], 1);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  long long* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
-  for (int e = t; e < C * D; e += 512) part[e] = (long long)bins[e];
+  int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
+  for (int e = t; e < C * D; e += 256) part[e] = bins[e];
   if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
 }
 
-// Update step: centroid = exact mean of its members (empty clusters stay).
+// Update step: centroid = member mean rounded to the nearest integer (ties to
+// even; |sum| < 2^34 so the fp64 quotient rounds once), empty clusters stay.
 // grid (C, BH), 128 threads.
 __global__ __launch_bounds__(128) void k_km_update(Args a) {
   const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
@@ -262,7 +337,11 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
     s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
     n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
   }
-  if (n > 0) a.cent[((size_t)bh * C + kk) * D + c] = fixed_mean(s, n);
+  if (n > 0) {
+    const int u = (int)__builtin_rint((double)s / (double)n);
+    a.centfix[((size_t)bh * C + kk) * D + c] = u;
+    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -a.kmsh[bh]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -378,6 +457,21 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  if (isk) {
+    // the K codes decoded to bf16 (E4M3 values are exact in bf16)
+    uint16_t* d16 = a.k16 + ((size_t)bh * a.Npad + p) * D + hf * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wd = w[2 * i + (e >> 1)];
+        const uint32_t b0 = (wd >> (16 * (e & 1))) & 0xff, b1 = (wd >> (16 * (e & 1) + 8)) & 0xff;
+        h[e] = (__float_as_uint(e4m3_val(b0)) >> 16) | (__float_as_uint(e4m3_val(b1)) & 0xffff0000u);
+      }
+      *reinterpret_cast<uint4*>(d16 + 8 * i) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+  }
   if (t == 0) (isk ? a.sk : a.sq)[(size_t)bh * a.nblk + blk] = s;
 }
 
@@ -646,9 +740,10 @@ hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
   hipLaunchKernelGGL(k_kbar, dim3(BH), dim3(128), 0, st, a);
   if (vs) {
     if (recluster) {
+      hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
       hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
       for (int it = 0; it < a.T; ++it) {
-        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(512), 0, st, a);
+        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(256), 0, st, a);
         hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
       }
       hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);

@@ -99,7 +99,7 @@ def test_layout_aligned_and_disjoint(B, H, N, C_, rho):
     mpad = -(-m // 128) * 128
     sizes = dict(header=256, kbar=BH * 512, ksum=BH * (-(-N // 512)) * 1024, init_idx=BH * C_ * 4,
                  centroids=BH * C_ * 512, labels=BH * N * 4, perm=BH * N * 4, iperm=BH * N * 4,
-                 q8=BH * npad * 128, k8=BH * npad * 128, sq=BH * nblk * 4, sk=BH * nblk * 4,
+                 q8=BH * npad * 128, k8=BH * npad * 128, k16=BH * npad * 256, sq=BH * nblk * 4, sk=BH * nblk * 4,
                  mu=BH * nblk * 512, bamax=BH * nblk * 512, mup=BH * nblk * 512,
                  mupt=BH * (-(-nblk // 16)) * 8192, sv=BH * 512,
                  inv=BH * 512, v8t=BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,

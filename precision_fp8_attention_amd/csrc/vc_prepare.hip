@@ -145,7 +145,8 @@ __global__ __launch_bounds__(128) void k_kbar(Args a) {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Fixed-point exponent of the head and the int8 planes of u (token order).
-// grid (ceil(N/256), BH), 256 threads: one token per thread.
+// grid (ceil(N/256), BH), 256 threads: 16 threads per token row (8 channels
+// each, 16-byte loads), 16 rows per step.
 __global__ __launch_bounds__(256) void k_vfix(Args a) {
   __shared__ float wm[4];
   const int bh = blockIdx.y, t = threadIdx.x;
@@ -159,75 +160,96 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
   if (am > 0.0f) frexpf(am, &e);
   const int sh = am > 0.0f ? 13 - e : 0;
   if (blockIdx.x == 0 && t == 0) a.kmsh[bh] = sh;
-  const int j = blockIdx.x * 256 + t;
-  if (j >= a.N) return;
-  const uint16_t* row = a.v + ((size_t)bh * a.N + j) * D;
-  int8_t* hi = a.uhi + ((size_t)bh * a.N + j) * D;
-  int8_t* lo = a.ulo + ((size_t)bh * a.N + j) * D;
+  const int cg = t & 15;
+  for (int r = t >> 4; r < 256; r += 16) {
+    const int j = blockIdx.x * 256 + r;
+    if (j >= a.N) break;
+    const size_t o = ((size_t)bh * a.N + j) * D + cg * 8;
+    const uint4 u = *reinterpret_cast<const uint4*>(a.v + o);
+    const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+    uint32_t ph[2] = {0u, 0u}, pl[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(row + 16 * i);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(row + 16 * i + 8);
-    const uint32_t h[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t wh = 0, wl = 0;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t bits = (e2 & 1) ? (h[2 * q + (e2 >> 1)] >> 16) : h[2 * q + (e2 >> 1)];
-        const int u = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
-        wh |= (uint32_t)((u >> 7) & 0xff) << (8 * e2);
-        wl |= (uint32_t)(u & 127) << (8 * e2);
-      }
-      ph[q] = wh;
-      pl[q] = wl;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (i & 1) ? (h[i >> 1] >> 16) : h[i >> 1];
+      const int q = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
+      ph[i >> 2] |= (uint32_t)((q >> 7) & 0xff) << (8 * (i & 3));
+      pl[i >> 2] |= (uint32_t)(q & 127) << (8 * (i & 3));
     }
-    *reinterpret_cast<uint4*>(hi + 16 * i) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-    *reinterpret_cast<uint4*>(lo + 16 * i) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    *reinterpret_cast<uint2*>(a.uhi + o) = make_uint2(ph[0], ph[1]);
+    *reinterpret_cast<uint2*>(a.ulo + o) = make_uint2(pl[0], pl[1]);
   }
 }
 
 // Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
-// fixed-point value of token idx[k].  grid BH, 128 threads.
+// fixed-point value of token idx[k].  The draws do not depend on the swaps, so
+// lane i computes draw i; wave 0 then replays the swaps over a sparse map held
+// one entry per lane.  grid BH, 128 threads.
 __global__ __launch_bounds__(128) void k_km_init(Args a) {
-  __shared__ int key[2 * MAX_CLUSTERS], val[2 * MAX_CLUSTERS];
+  __shared__ int jdraw[MAX_CLUSTERS];
   __shared__ int idx[MAX_CLUSTERS];
-  const int bh = blockIdx.x, C = a.C;
-  if (threadIdx.x == 0) {
-    uint64_t st = a.seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(bh + 1));
-    int n = 0;
+  const int bh = blockIdx.x, C = a.C, t = threadIdx.x;
+  if (t < C) {
+    // state after t+1 steps of splitmix64 from the head's seed
+    uint64_t st = (a.seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(bh + 1))) +
+                  0x9E3779B97F4A7C15ull * (uint64_t)t;
+    const uint64_t r = splitmix(st);
+    jdraw[t] = t + (int)(r % (uint64_t)(a.N - t));
+  }
+  __syncthreads();
+  if (t < 64) {
+    // sparse map: lanes 0..63 hold keys (positions) k0 and k1 with values v0, v1
+    int k0 = -1, v0 = 0, k1 = -1, v1 = 0, n = 0;
     for (int i = 0; i < C; ++i) {
-      const uint64_t r = splitmix(st);
-      const int j = i + (int)(r % (uint64_t)(a.N - i));
-      int vi = i, vj = j, si = -1, sj = -1;
-      for (int e = 0; e < n; ++e) {
-        if (key[e] == i) { vi = val[e]; si = e; }
-        if (key[e] == j) { vj = val[e]; sj = e; }
+      const int j = jdraw[i];
+      const unsigned long long mi0 = __ballot(k0 == i), mi1 = __ballot(k1 == i);
+      const unsigned long long mj0 = __ballot(k0 == j), mj1 = __ballot(k1 == j);
+      int vi = i, vj = j;
+      if (mi0) vi = __shfl(v0, __ffsll((long long)mi0) - 1, 64);
+      else if (mi1) vi = __shfl(v1, __ffsll((long long)mi1) - 1, 64);
+      if (mj0) vj = __shfl(v0, __ffsll((long long)mj0) - 1, 64);
+      else if (mj1) vj = __shfl(v1, __ffsll((long long)mj1) - 1, 64);
+      // map[i] = vj, map[j] = vi (insert when absent)
+      const int li = mi0 ? __ffsll((long long)mi0) - 1 : (mi1 ? 64 + __ffsll((long long)mi1) - 1 : n);
+      if (!(mi0 | mi1)) ++n;
+      const int lj = (j == i) ? li
+                     : (mj0 ? __ffsll((long long)mj0) - 1 : (mj1 ? 64 + __ffsll((long long)mj1) - 1 : n));
+      if (j != i && !(mj0 | mj1)) ++n;
+      if (li < 64) { if (t == li) { k0 = i; v0 = vj; } } else if (t == li - 64) { k1 = i; v1 = vj; }
+      if (j != i) {
+        if (lj < 64) { if (t == lj) { k0 = j; v0 = vi; } } else if (t == lj - 64) { k1 = j; v1 = vi; }
       }
-      if (si < 0) { key[n] = i; si = n++; }
-      if (sj < 0 && j != i) { key[n] = j; sj = n++; }
-      val[si] = vj;
-      if (j != i) val[sj] = vi;
-      idx[i] = vj;
+      if (t == 0) idx[i] = vj;
     }
   }
   __syncthreads();
   const int sh = a.kmsh[bh];
-  const int c = threadIdx.x;
   for (int kk = 0; kk < C; ++kk) {
-    const size_t src = ((size_t)bh * a.N + idx[kk]) * D + c;
+    const size_t src = ((size_t)bh * a.N + idx[kk]) * D + t;
     const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
-    a.centfix[((size_t)bh * C + kk) * D + c] = u;
-    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -sh);
+    a.centfix[((size_t)bh * C + kk) * D + t] = u;
+    a.cent[((size_t)bh * C + kk) * D + t] = ldexpf((float)u, -sh);
   }
-  if (c < C) a.init_idx[(size_t)bh * C + c] = idx[c];
+  if (t < C) a.init_idx[(size_t)bh * C + t] = idx[t];
 }
 
 // Assignment step on int8 MFMA plus per-workgroup member sums.
 // grid (nkm, BH), 256 threads (4 waves x 64 tokens per 256-token pass),
-// KM_CHUNK tokens per workgroup.
-constexpr int CROW = D + 16;  // padded LDS row of a centroid operand (bytes)
+// KM_CHUNK tokens per workgroup.  Lane (g, j) of a 16-token subtile loads the
+// hi/lo bytes of channels 16g..16g+15 and 64+16g..64+16g+15 of token j as its
+// MFMA B operand; after the argmin the same registers are added to the LDS bins
+// of the token's cluster, so the planes are read once per iteration.
+constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
+
+__device__ __forceinline__ void add_bins(int* bins, int base, const v4i& h, const v4i& l) {
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int hv = (int)(signed char)((uint32_t)h[wd] >> (8 * b));
+      const int lv = (int)(((uint32_t)l[wd] >> (8 * b)) & 0xffu);
+      atomicAdd(&bins[base + 4 * wd + b], hv * 128 + lv);
+    }
+}
 
 __global__ __launch_bounds__(256) void k_km_assign(Args a) {
   __shared__ __align__(16) int8_t chi[MAX_CLUSTERS * CROW];
@@ -235,7 +257,6 @@ __global__ __launch_bounds__(256) void k_km_assign(Args a) {
   __shared__ long long cc[MAX_CLUSTERS];
   __shared__ int bins[MAX_CLUSTERS * D];
   __shared__ int cnt[MAX_CLUSTERS];
-  __shared__ int slab[256];
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, C = a.C;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
   const int* cf = a.centfix + (size_t)bh * C * D;
@@ -255,73 +276,71 @@ __global__ __launch_bounds__(256) void k_km_assign(Args a) {
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
   const int ntile = (C + 15) / 16;
-  for (int pass = 0; pass < KM_CHUNK / 256; ++pass) {
-    const int base = chunk * KM_CHUNK + pass * 256;
-    if (base >= a.N) break;  // uniform across the workgroup
+  // wave w takes 16-token subtiles w, w+4, ... of the chunk; the operands of the
+  // next subtile are loaded while the current one is processed
+  const int first = chunk * KM_CHUNK;
+  auto load_sub = [&](int s, v4i& h0, v4i& h1, v4i& l0, v4i& l1) {
+    int jj = first + s * 16 + l16;
+    jj = jj < a.N ? jj : a.N - 1;  // tail lanes read a valid row, add nothing
+    h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
+    h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
+    l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
+    l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+  };
+  v4i nh0, nh1, nl0, nl1;
+  if (first + w * 16 < a.N) load_sub(w, nh0, nh1, nl0, nl1);
 #pragma unroll 1
-    for (int ts = 0; ts < 4; ++ts) {
-      const int loc = w * 64 + ts * 16 + l16;  // token within the pass
-      const int j = base + loc;
-      const int jj = j < a.N ? j : a.N - 1;    // tail lanes compute on a valid row
-      v4i bh0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
-      v4i bh1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
-      v4i bl0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
-      v4i bl1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
-      long long bestD = 0x7fffffffffffffffll;  // lanes with no valid centroid never win
-      int best = 0x7fffffff;
-      for (int kt = 0; kt < ntile; ++kt) {
-        const int kr = 16 * kt + l16;
-        const int krow = kr < C ? kr : 0;
-        const v4i ah0 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 16 * g);
-        const v4i ah1 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 64 + 16 * g);
-        const v4i al0 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 16 * g);
-        const v4i al1 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 64 + 16 * g);
-        const v4i z = {0, 0, 0, 0};
-        v4i HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bh0, z, 0, 0, 0);
-        HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bh1, HH, 0, 0, 0);
-        v4i HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bl0, z, 0, 0, 0);
-        HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bl1, HL, 0, 0, 0);
-        v4i LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bh0, z, 0, 0, 0);
-        LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, LH, 0, 0, 0);
-        v4i LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bl0, z, 0, 0, 0);
-        LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bl1, LL, 0, 0, 0);
-        // lane (g, token l16) holds centroids 16kt + 4g + v
+  for (int sub = w; sub < KM_CHUNK / 16; sub += 4) {
+    if (first + sub * 16 >= a.N) break;  // uniform per wave
+    const v4i bh0 = nh0, bh1 = nh1, bl0 = nl0, bl1 = nl1;
+    if (sub + 4 < KM_CHUNK / 16 && first + (sub + 4) * 16 < a.N) load_sub(sub + 4, nh0, nh1, nl0, nl1);
+    const int j = first + sub * 16 + l16;
+    long long bestD = 0x7fffffffffffffffll;  // lanes with no valid centroid never win
+    int best = 0x7fffffff;
+    for (int kt = 0; kt < ntile; ++kt) {
+      const int kr = 16 * kt + l16;
+      const int krow = kr < C ? kr : 0;
+      const v4i ah0 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 16 * g);
+      const v4i ah1 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 64 + 16 * g);
+      const v4i al0 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 16 * g);
+      const v4i al1 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 64 + 16 * g);
+      const v4i z = {0, 0, 0, 0};
+      v4i HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bh0, z, 0, 0, 0);
+      HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bh1, HH, 0, 0, 0);
+      v4i HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bl0, z, 0, 0, 0);
+      HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bl1, HL, 0, 0, 0);
+      v4i LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bh0, z, 0, 0, 0);
+      LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, LH, 0, 0, 0);
+      v4i LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bl0, z, 0, 0, 0);
+      LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bl1, LL, 0, 0, 0);
+      // lane (g, token l16) holds centroids 16kt + 4g + v
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int k = 16 * kt + 4 * g + v;
-          if (k < C) {
-            const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
-            const long long Dk = cc[k] - 2 * dot;
-            if (Dk < bestD) { bestD = Dk; best = k; }
-          }
+      for (int v = 0; v < 4; ++v) {
+        const int k = 16 * kt + 4 * g + v;
+        if (k < C) {
+          const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
+          const long long Dk = cc[k] - 2 * dot;
+          if (Dk < bestD) { bestD = Dk; best = k; }
         }
       }
-      // argmin across the four lane groups; ties go to the lower id
+    }
+    // argmin across the four lane groups; ties go to the lower id
 #pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const long long oD = __shfl_xor(bestD, off, 64);
-        const int ob = __shfl_xor(best, off, 64);
-        if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
-      }
+    for (int off = 16; off <= 32; off <<= 1) {
+      const long long oD = __shfl_xor(bestD, off, 64);
+      const int ob = __shfl_xor(best, off, 64);
+      if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
+    }
+    if (j < a.N) {
       if (g == 0) {
-        slab[loc] = best;
-        if (j < a.N) a.labels[(size_t)bh * a.N + j] = best;
+        a.labels[(size_t)bh * a.N + j] = best;
+        atomicAdd(&cnt[best], 1);
       }
+      add_bins(bins, best * D + 16 * g, bh0, bl0);
+      add_bins(bins, best * D + 64 + 16 * g, bh1, bl1);
     }
-    __syncthreads();
-    // member sums: thread = (channel t%128, token parity t/128)
-    {
-      const int c = t & 127, par = t >> 7;
-      const int n = min(256, a.N - base);
-#pragma unroll 4
-      for (int i = par; i < n; i += 2) {
-        const size_t o = (size_t)(base + i) * D + c;
-        atomicAdd(&bins[slab[i] * D + c], 128 * (int)uhi[o] + (int)ulo[o]);
-      }
-      if (t < n) atomicAdd(&cnt[slab[t]], 1);
-    }
-    __syncthreads();
   }
+  __syncthreads();
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
   for (int e = t; e < C * D; e += 256) part[e] = bins[e];
   if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
@@ -403,39 +422,38 @@ __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-block E4M3 codes of Q (z = 0) and smoothed K (z = 1).
-// grid (nblk, BH, 2), 256 threads: thread = (row t/2, 64-channel half t%2).
+// Per-block E4M3 codes of Q (z = 0) and smoothed K (z = 1), and for K the bf16
+// copy of the codes.  grid (nblk, BH, 2), 256 threads: thread = (8-channel
+// chunk t%16, rows t/16 + 16i), so 16 threads cover one 256-byte row.
 __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
   __shared__ float wmax[4];
   const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z, t = threadIdx.x;
-  const int r = t >> 1, hf = t & 1, p = blk * BLK + r;
-  const bool real = p < a.N;
+  const int cg = t & 15, r0 = t >> 4;
   const bool follow = isk || (a.flags & VC_PERMUTE_Q);
   const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
-  const float* kbar = a.kbar + (size_t)bh * D + hf * 64;
-  float x[64];
+  float kb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kb[i] = isk ? a.kbar[(size_t)bh * D + cg * 8 + i] : 0.0f;
+  float x[8][8];
   float amax = 0.0f;
-  if (real) {
-    const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
-    const uint16_t* row = src + (size_t)j * D + hf * 64;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
-      x[i * 8 + 0] = bf2f(u.x);
-      x[i * 8 + 1] = bf2f(u.x >> 16);
-      x[i * 8 + 2] = bf2f(u.y);
-      x[i * 8 + 3] = bf2f(u.y >> 16);
-      x[i * 8 + 4] = bf2f(u.z);
-      x[i * 8 + 5] = bf2f(u.z >> 16);
-      x[i * 8 + 6] = bf2f(u.w);
-      x[i * 8 + 7] = bf2f(u.w >> 16);
+  for (int i = 0; i < 8; ++i) {
+    const int p = blk * BLK + r0 + 16 * i;
+    if (p < a.N) {
+      const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
+      const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)j * D + cg * 8);
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float val = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
+        if (isk) val = val - kb[e];
+        x[i][e] = val;
+        amax = fmaxf(amax, fabsf(val));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
     }
-    if (isk) {
-#pragma unroll
-      for (int c = 0; c < 64; ++c) x[c] = x[c] - kbar[c];
-    }
-#pragma unroll
-    for (int c = 0; c < 64; ++c) amax = fmaxf(amax, fabsf(x[c]));
   }
   amax = wave_max(amax);
   if ((t & 63) == 0) wmax[t >> 6] = amax;
@@ -443,33 +461,27 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float s, inv;
   scale_from_amax(amax, &s, &inv);
-  uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + hf * 64;
-  uint32_t w[16];
-  if (real) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      w[i] = e4m3x2(x[4 * i] * inv, x[4 * i + 1] * inv) |
-             (e4m3x2(x[4 * i + 2] * inv, x[4 * i + 3] * inv) << 16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-  if (isk) {
-    // the K codes decoded to bf16 (E4M3 values are exact in bf16)
-    uint16_t* d16 = a.k16 + ((size_t)bh * a.Npad + p) * D + hf * 64;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 8; ++i) {
+    const int p = blk * BLK + r0 + 16 * i;
+    uint32_t w0 = 0u, w1 = 0u;
+    if (p < a.N) {
+      w0 = e4m3x2(x[i][0] * inv, x[i][1] * inv) | (e4m3x2(x[i][2] * inv, x[i][3] * inv) << 16);
+      w1 = e4m3x2(x[i][4] * inv, x[i][5] * inv) | (e4m3x2(x[i][6] * inv, x[i][7] * inv) << 16);
+    }
+    uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + cg * 8;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    if (isk) {
+      // the K codes decoded to bf16 (E4M3 values are exact in bf16)
       uint32_t h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t wd = w[2 * i + (e >> 1)];
+        const uint32_t wd = e < 2 ? w0 : w1;
         const uint32_t b0 = (wd >> (16 * (e & 1))) & 0xff, b1 = (wd >> (16 * (e & 1) + 8)) & 0xff;
         h[e] = (__float_as_uint(e4m3_val(b0)) >> 16) | (__float_as_uint(e4m3_val(b1)) & 0xffff0000u);
       }
-      *reinterpret_cast<uint4*>(d16 + 8 * i) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(a.k16 + ((size_t)bh * a.Npad + p) * D + cg * 8) =
+          make_uint4(h[0], h[1], h[2], h[3]);
     }
   }
   if (t == 0) (isk ? a.sk : a.sq)[(size_t)bh * a.nblk + blk] = s;
@@ -477,43 +489,64 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
 
 // ---------------------------------------------------------------------------
 // V block means and block maxima of |V - mu|.  grid (nblk, BH), 256 threads:
-// thread = (channel t%128, row half t/128).
+// thread = (8-channel chunk t%16, rows t/16 + 16i).
 __global__ __launch_bounds__(256) void k_v_stats(Args a) {
-  __shared__ long long ssum[2][D];
-  __shared__ float smax[2][D];
+  __shared__ long long ssum[16][D];
+  __shared__ float smax[16][D];
   __shared__ float smu[D];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const int c = t & 127, hf = t >> 7;
+  const int cg = t & 15, r0 = t >> 4;
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
   const uint16_t* vh = a.v + (size_t)bh * a.N * D;
   const int* perm = a.perm + (size_t)bh * a.N;
-  float x[64];
-  long long s = 0;
+  float x[8][8];
+  long long s[8];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const int r = hf * 64 + i;
-    x[i] = 0.0f;
+  for (int e = 0; e < 8; ++e) s[e] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + 16 * i;
     if (r < n) {
-      x[i] = bf2f(vh[(size_t)perm[p0 + r] * D + c]);
-      s += fx24(x[i]);
+      const uint4 u = *reinterpret_cast<const uint4*>(vh + (size_t)perm[p0 + r] * D + cg * 8);
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[i][e] = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
+        s[e] += fx24(x[i][e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
     }
   }
-  ssum[hf][c] = s;
-  __syncthreads();
-  if (t < D) smu[c] = vs ? fixed_mean(ssum[0][c] + ssum[1][c], n) : 0.0f;
-  __syncthreads();
-  const float mu = smu[c];
-  float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i)
-    if (hf * 64 + i < n) m = fmaxf(m, fabsf(x[i] - mu));
-  smax[hf][c] = m;
+  for (int e = 0; e < 8; ++e) ssum[r0][cg * 8 + e] = s[e];
   __syncthreads();
   if (t < D) {
-    const size_t o = ((size_t)bh * a.nblk + blk) * D + c;
-    a.mu[o] = mu;
-    a.bamax[o] = fmaxf(smax[0][c], smax[1][c]);
+    long long tot = 0;
+    for (int rr = 0; rr < 16; ++rr) tot += ssum[rr][t];
+    smu[t] = vs ? fixed_mean(tot, n) : 0.0f;
+  }
+  __syncthreads();
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (r0 + 16 * i < n) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[i][e] - smu[cg * 8 + e]));
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) smax[r0][cg * 8 + e] = m[e];
+  __syncthreads();
+  if (t < D) {
+    float mm = 0.0f;
+    for (int rr = 0; rr < 16; ++rr) mm = fmaxf(mm, smax[rr][t]);
+    const size_t o = ((size_t)bh * a.nblk + blk) * D + t;
+    a.mu[o] = smu[t];
+    a.bamax[o] = mm;
   }
 }
 
@@ -572,28 +605,48 @@ __global__ __launch_bounds__(128) void k_v_mup(Args a) {
 }
 
 // Residual codes (channel-major, interleaved) and the repair criterion.
-// grid (nblk, BH), 128 threads: thread = position in the block.
-__global__ __launch_bounds__(128) void k_v_quant(Args a) {
+// grid (nblk, BH), 256 threads.  The block's rows are staged in LDS with
+// coalesced loads (row stride 65 words: a thread per row reads conflict-free);
+// then one thread per row walks its channels in order, because the criterion is
+// an fp32 fma chain over channels 0..127.
+constexpr int VROW = D / 2 + 1;  // words per staged row (2 bf16 per word + pad)
+
+__global__ __launch_bounds__(256) void k_v_quant(Args a) {
   __shared__ float smu[D], sinv[D], ssv[D];
+  __shared__ uint32_t rows[BLK * VROW];
   __shared__ __align__(16) uint8_t tile[D * BLK];
-  const int blk = blockIdx.x, bh = blockIdx.y, r = threadIdx.x;
-  const int p = blk * BLK + r;
-  smu[r] = a.mu[((size_t)bh * a.nblk + blk) * D + r];
-  sinv[r] = a.inv[(size_t)bh * D + r];
-  ssv[r] = a.sv[(size_t)bh * D + r];
-  __syncthreads();
-  const int col = v_col(r);
-  if (p < a.N) {
-    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
-    float e = 0.0f;
-    for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int p0 = blk * BLK, n = min(BLK, a.N - p0);
+  if (t < D) {
+    smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
+    sinv[t] = a.inv[(size_t)bh * D + t];
+    ssv[t] = a.sv[(size_t)bh * D + t];
+  }
+  {
+    const int cg = t & 15, r0 = t >> 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = i * 8 + 2 * j;
-        const float x0 = (bf2f(h[j]) - smu[c]) * sinv[c];
-        const float x1 = (bf2f(h[j] >> 16) - smu[c + 1]) * sinv[c + 1];
+    for (int i = 0; i < 8; ++i) {
+      const int r = r0 + 16 * i;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (r < n) u = *reinterpret_cast<const uint4*>(
+          a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p0 + r]) * D + cg * 8);
+      uint32_t* dst = rows + r * VROW + cg * 4;
+      dst[0] = u.x;
+      dst[1] = u.y;
+      dst[2] = u.z;
+      dst[3] = u.w;
+    }
+  }
+  __syncthreads();
+  if (t < BLK) {
+    const int r = t, col = v_col(r), p = p0 + r;
+    if (r < n) {
+      float e = 0.0f;
+      for (int wd = 0; wd < D / 2; ++wd) {
+        const uint32_t h = rows[r * VROW + wd];
+        const int c = 2 * wd;
+        const float x0 = (bf2f(h) - smu[c]) * sinv[c];
+        const float x1 = (bf2f(h >> 16) - smu[c + 1]) * sinv[c + 1];
         const uint32_t cc = e4m3x2(x0, x1);
         tile[c * BLK + col] = (uint8_t)(cc & 0xff);
         tile[(c + 1) * BLK + col] = (uint8_t)(cc >> 8);
@@ -602,17 +655,20 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
         const float t1 = ssv[c + 1] * (x1 - e4m3_val(cc >> 8));
         e = __builtin_fmaf(t1, t1, e);
       }
+      a.err[(size_t)bh * a.N + p] = e;
+    } else {
+      for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
     }
-    a.err[(size_t)bh * a.N + p] = e;
-  } else {
-    for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
   }
   __syncthreads();
-  // thread r stores channel row r of the tile (128 contiguous bytes)
-  uint8_t* dst = a.v8t + ((size_t)bh * D + r) * a.Npad + (size_t)blk * BLK;
+  // 128 channel rows x 128 bytes: thread t stores half a row
+  {
+    const int c = t >> 1, hf = t & 1;
+    uint8_t* dst = a.v8t + ((size_t)bh * D + c) * a.Npad + (size_t)blk * BLK + hf * 64;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + r * BLK + 16 * i);
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + c * BLK + hf * 64 + 16 * i);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -757,7 +813,7 @@ hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
-  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(256), 0, st, a);
   if (a.m > 0) {
     hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
     hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);

@@ -12,10 +12,11 @@
 //   repair set      the ceil(rho*N) positions whose value codes lose the most.
 //
 // Every decision that yields an integer (cluster id, E4M3 code, selected token)
-// is taken in fixed-order fp32 (explicit fma) or in exact integer arithmetic, so
-// that the result does not depend on the order in which threads run: means are
-// exact int64 sums of values rounded to a 2^-24 grid, divided once in fp64.
-// The library is built with -ffp-contract=off.
+// is taken in exact integer arithmetic or in a fixed sequence of fp32 operations
+// (explicit fma), so that the result does not depend on the order in which
+// threads run: means are exact int64 sums of values rounded to a 2^-24 grid,
+// divided once in fp64; k-means distances are exact integers on fixed-point
+// values.  The library is built with -ffp-contract=off.
 #include "vc_internal.h"
 
 namespace vc {

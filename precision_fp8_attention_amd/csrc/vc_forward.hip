@@ -63,9 +63,10 @@ __device__ __forceinline__ v4f mfma_bf16_k16(v4s a, v4s b, v4f c) {
 }
 
 // 32 bytes of row `row` of a 128x128 byte tile, 16-byte chunks 2g and 2g+1,
-// stored with the chunk index XOR-swizzled by row%8 (LDS bank spreading).
+// stored with the chunk index XOR-swizzled by (row/2)%8: the 16 rows a
+// ds_read_b128 serves together then cover all 64 banks once.
 __device__ __forceinline__ v8i lds_row32(const uint8_t* tile, int row, int g) {
-  const int sw = row & 7;
+  const int sw = (row >> 1) & 7;
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * g) ^ sw) << 4));
   const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * g + 1) ^ sw) << 4));
   v8i r;
@@ -218,7 +219,8 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   const int g = lane >> 4, l16 = lane & 15;
   const int npair = (a.nblk + 1) / 2;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / npair, qb = 2 * (logical % npair) + (w >> 2);
+  const int wg = w >> 2;            // which of the two query blocks
+  const int bh = logical / npair, qb = 2 * (logical % npair) + wg;
   const bool active = qb < a.nblk;  // the second block of an odd count is empty
   const int qbv = active ? qb : qb - 1;
   const int wq = w & 3;             // wave within its query block
@@ -234,20 +236,20 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   // V^T (16 KB) as 16 regions of 8 rows; a lane lands at byte 16*lane of its
   // region, i.e. in stored chunk lane%16 (K) or lane%8 (V) of its row, which
   // holds the source chunk XOR the row's swizzle
-  auto issue = [&](int kb, int st) {
+  auto issue = [&](int kb) {
+    uint8_t* kd = ksm[kb & 1];
+    uint8_t* vd = vsm[kb & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * i + w;
       const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
-      __builtin_amdgcn_global_load_lds(k16 + ((size_t)kb * BLK + row) * 256 + cc * 16,
-                                       &ksm[st][r * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(k16 + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 8 * i + w;
-      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ (row & 7);
-      __builtin_amdgcn_global_load_lds(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16,
-                                       &vsm[st][r * 1024], 16, 0, 0);
+      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ ((row >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024, 16, 0, 0);
     }
   };
 
@@ -279,18 +281,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     for (int ct = 0; ct < 8; ++ct) rs[qs].acc[ct] = zero;
   }
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int kb = 0; kb < a.nblk; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < a.nblk) issue(kb + 1, st ^ 1);
-    const uint8_t* Ks = ksm[st];
-    const uint8_t* Vs = vsm[st];
-    const float alpha = (sQa * sk[kb]) * a.c0;
-
-    v4f S[2][8];
+  // S^T of one key block for both query subtiles (bf16 MFMA, exact products)
+  auto qk = [&](int kb, v4f (&S)[2][8]) {
+    const uint8_t* Ks = ksm[kb & 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       S[0][t] = zero;
@@ -302,6 +295,10 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
         S[1][t] = mfma_bf16_k32(kop, qop[1][kc], S[1][t]);
       }
     }
+  };
+  // masking, row maximum, rescale and ExpCast codes of one key block
+  auto soft = [&](int kb, v4f (&S)[2][8], v8i (&pop)[2]) {
+    const float alpha = (sQa * sk[kb]) * a.c0;
     const int nvalid = a.N - kb * BLK;
     if (nvalid < BLK) {
 #pragma unroll
@@ -312,10 +309,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
           for (int v = 0; v < 4; ++v)
             if (16 * t + 4 * g + v >= nvalid) S[qs][t][v] = -INFINITY;
     }
-    v8i pop[2];
     pop[0] = softmax_codes(S[0], rs[0], alpha, a.bias, a.tau);
     pop[1] = softmax_codes(S[1], rs[1], alpha, a.bias, a.tau);
-
+  };
+  // row sums (ones MFMA), P.V (FP8 MFMA) and the 16-block restore of one block
+  auto pv = [&](int kb, const v8i (&pop)[2]) {
+    const uint8_t* Vs = vsm[kb & 1];
     // ones in A row kb%16: the block's row sum accumulates in L element v of
     // lane group g where 4g+v = kb%16
     const int onesrow = kb & 15;
@@ -325,7 +324,6 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     for (int i = 0; i < 8; ++i) onesop[i] = o;
     rs[0].L = mfma_f8(onesop, pop[0], rs[0].L);
     rs[1].L = mfma_f8(onesop, pop[1], rs[1].L);
-
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const v8i vop = lds_row32(Vs, 16 * ct + l16, g);
@@ -337,6 +335,22 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
       restore_group(rs[0], grp, l16, g);
       restore_group(rs[1], grp, l16, g);
     }
+  };
+
+  // Every wave runs QK(kb), softmax(kb), PV(kb) per key block; block kb+1 lands
+  // in the other LDS stage meanwhile.  (Offsetting half of the waves by half a
+  // block, so that one wave per SIMD is on VALU work while the other feeds the
+  // matrix core, measured slower on gfx950.)
+  issue(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kb = 0; kb < a.nblk; ++kb) {
+    if (kb + 1 < a.nblk) issue(kb + 1);
+    v4f S[2][8];
+    v8i pop[2];
+    qk(kb, S);
+    soft(kb, S, pop);
+    pv(kb, pop);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }

@@ -240,6 +240,9 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
 // MFMA B operand; after the argmin the same registers are added to the LDS bins
 // of the token's cluster, so the planes are read once per iteration.
 constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
+constexpr int BROW = D + 1;   // LDS row of the member-sum bins (ints): lanes adding
+                              // the same channel of different clusters hit
+                              // different banks
 
 __device__ __forceinline__ void add_bins(int* bins, int base, const v4i& h, const v4i& l) {
 #pragma unroll
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256) void k_km_assign(Args a) {
   __shared__ __align__(16) int8_t chi[MAX_CLUSTERS * CROW];
   __shared__ __align__(16) int8_t clo[MAX_CLUSTERS * CROW];
   __shared__ long long cc[MAX_CLUSTERS];
-  __shared__ int bins[MAX_CLUSTERS * D];
+  __shared__ int bins[MAX_CLUSTERS * BROW];
   __shared__ int cnt[MAX_CLUSTERS];
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, C = a.C;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(256) void k_km_assign(Args a) {
     const int u = cf[e];
     chi[(e / D) * CROW + (e % D)] = (int8_t)(u >> 7);
     clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
-    bins[e] = 0;
+    bins[(e / D) * BROW + (e % D)] = 0;
   }
   if (t < C) {
     long long s = 0;
@@ -337,13 +340,13 @@ __global__ __launch_bounds__(256) void k_km_assign(Args a) {
         a.labels[(size_t)bh * a.N + j] = best;
         atomicAdd(&cnt[best], 1);
       }
-      add_bins(bins, best * D + 16 * g, bh0, bl0);
-      add_bins(bins, best * D + 64 + 16 * g, bh1, bl1);
+      add_bins(bins, best * BROW + 16 * g, bh0, bl0);
+      add_bins(bins, best * BROW + 64 + 16 * g, bh1, bl1);
     }
   }
   __syncthreads();
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
-  for (int e = t; e < C * D; e += 256) part[e] = bins[e];
+  for (int e = t; e < C * D; e += 256) part[e] = bins[(e / D) * BROW + (e % D)];
   if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
 }
 
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(256) void k_v_quant(Args a) {
 __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   __shared__ int hist[256];
   __shared__ unsigned long long s_prefix, s_mask;
-  __shared__ int s_kth, s_base;
+  __shared__ int s_kth, s_kth_next, s_base;
   __shared__ int wtot[16];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const float* err = a.err + (size_t)bh * a.N;
@@ -698,16 +701,33 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
       if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255], 1);
     }
     __syncthreads();
-    if (t == 0) {
-      int kth = s_kth, cum = 0, dg = 0;
-      for (dg = 0; dg < 256; ++dg) {
-        if (cum + hist[dg] >= kth) break;
-        cum += hist[dg];
+    // parallel exclusive scan of the 256 bins (threads 0..255, 4 waves); the one
+    // bin where the running count crosses kth fixes the next digit
+    int h = 0, incl = 0;
+    if (t < 256) {
+      h = hist[t];
+      incl = h;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
       }
-      s_kth = kth - cum;
-      s_prefix = pre | ((unsigned long long)dg << shift);
-      s_mask = msk | (255ull << shift);
+      if (lane == 63) wtot[w] = incl;
     }
+    __syncthreads();
+    if (t < 256) {
+      int before = 0;
+      for (int ww = 0; ww < w; ++ww) before += wtot[ww];
+      const int cum = before + incl - h;  // count of smaller digits
+      const int kth = s_kth;
+      if (h > 0 && cum < kth && kth <= cum + h) {
+        s_kth_next = kth - cum;
+        s_prefix = pre | ((unsigned long long)t << shift);
+        s_mask = msk | (255ull << shift);
+      }
+    }
+    __syncthreads();
+    if (t == 0) s_kth = s_kth_next;
     __syncthreads();
   }
   const unsigned long long thr = s_prefix;  // the m-th smallest key

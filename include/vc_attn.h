@@ -68,9 +68,14 @@ enum {
   VC_REPAIR = 2u,        /* correct the ceil(rho*N) worst-quantised value tokens */
   VC_PERMUTE_Q = 4u,     /* queries follow the cluster permutation too (output is
                             scattered back to original order either way) */
-  VC_REUSE_CLUSTERS = 8u /* prepare skips k-means and reuses labels/permutation
+  VC_REUSE_CLUSTERS = 8u, /* prepare skips k-means and reuses labels/permutation
                             already in the workspace (clustering runs only in the
                             early denoising steps, as the V-Smooth section says) */
+  VC_EXACT_SCORES = 16u  /* QK^T as the exact dot product of the E4M3 codes (bf16
+                            MFMA, twice the matrix-core time) instead of the FP8
+                            MFMA, whose accumulation cuts each product 13 bits below
+                            the largest exponent of its 8-channel group; set the
+                            same flag on prepare and forward */
 };
 
 typedef struct {
@@ -105,7 +110,8 @@ typedef struct {
   size_t q8;         /* u8  [BH][Npad][128] Q codes, position order               */
   size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order      */
   size_t k16;        /* bf16 [BH][Npad][128] the same codes decoded (exact in bf16),
-                        operand of the exactly-accumulated score MFMA             */
+                        operand of the exact score MFMA; written only with
+                        VC_EXACT_SCORES                                          */
   size_t sq;         /* f32 [BH][nblk] Q block scales                            */
   size_t sk;         /* f32 [BH][nblk] K block scales                            */
   size_t mu;         /* f32 [BH][nblk][128] V block means (real units)           */

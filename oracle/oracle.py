@@ -26,6 +26,7 @@ LIB = os.path.join(HERE, "libvcoracle.so")
 VSMOOTH = 1
 REPAIR = 2
 PERMUTE_Q = 4
+EXACT_SCORES = 16
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 
@@ -69,6 +70,7 @@ def lib():
         L.oc_e4m3_encode_array.argtypes = [vp, vp, i64]
         L.oc_expcast_array.argtypes = [vp, C.c_float, C.c_float, vp, i64]
         L.oc_splitmix64_array.argtypes = [C.c_uint64, vp, i64]
+        L.oc_score_array.argtypes = [vp, vp, i64, i32, i32, vp]
         L.oc_kmeans_init_indices.argtypes = [C.c_uint64, i64, i32, i32, vp]
         L.oc_repair_count.argtypes = [C.POINTER(Params)]
         L.oc_repair_count.restype = i32
@@ -172,6 +174,17 @@ def expcast(s, alpha: float, beta: float) -> np.ndarray:
     sf = np.ascontiguousarray(s, np.float32)
     out = np.zeros(sf.shape, np.uint8)
     lib().oc_expcast_array(_ptr(sf), float(alpha), float(beta), _ptr(out), sf.size)
+    return out
+
+
+def scores(a, b, exact: bool = False) -> np.ndarray:
+    """Raw scores of code rows a[i] . b[i] (uint8 [n, d]): the FP8 matrix-
+    instruction accumulation, or the exact dot product rounded to fp32."""
+    a = np.ascontiguousarray(a, np.uint8)
+    b = np.ascontiguousarray(b, np.uint8)
+    assert a.shape == b.shape and a.ndim == 2 and a.shape[1] % 8 == 0
+    out = np.zeros(a.shape[0], np.float32)
+    lib().oc_score_array(_ptr(a), _ptr(b), a.shape[0], a.shape[1], int(exact), _ptr(out))
     return out
 
 

@@ -27,7 +27,8 @@ static vc_status check(const vc_attn_params* p) {
   if (!(p->rho >= 0.0f && p->rho <= 1.0f)) return VC_ERR_INVALID_ARG;  // also rejects NaN
   if (!std::isfinite(p->sm_scale)) return VC_ERR_INVALID_ARG;
   if (!(p->tau >= 0.0f) || 56.0f + 8.0f * p->expcast_k + p->tau > 126.0f) return VC_ERR_INVALID_ARG;
-  if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS))
+  if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS |
+                         VC_EXACT_SCORES))
     return VC_ERR_INVALID_ARG;
   return VC_OK;
 }

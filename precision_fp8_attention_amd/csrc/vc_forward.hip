@@ -3,7 +3,8 @@
 // Method (noticiai.com.br VC-Attention article, sections "V-Smooth" (Restore) and
 // "ExpCast-FP8"; ip73.fr article, section "Le compromis entre vitesse et
 // fidelite" (repair)):
-//   S_raw = Q8 . K8^T   exact products of the E4M3 codes, fp32 accumulation
+//   S_raw = Q8 . K8^T   E4M3 codes on the FP8 MFMA (or, with VC_EXACT_SCORES,
+//           the exact dot product through bf16 MFMA), fp32 result
 //   M     = running row maximum in ExpCast code units, moved once per 128-key
 //           block (only when the block maximum exceeds it by more than tau)
 //   code  = clamp(rne(fma(S_raw, alpha, 56 + 8k - M)), 0, 126)   -- the E4M3 byte
@@ -22,13 +23,14 @@
 // v_cvt_pk_u8_f32 rounds to nearest even, saturates to [0, 255] and inserts the
 // byte, so one fma and one convert produce each packed code.
 //
-// Scores.  The codes are decisions, so S must be the exact dot product rounded
-// once: gfx950's FP8 MFMA accumulates 128 products with about 11 bits relative to
-// the largest one, which moves ExpCast codes across rounding boundaries.  The
-// E4M3 codes are therefore multiplied as bf16 (every E4M3 value is exact in
-// bf16) on v_mfma_f32_16x16x32_bf16, whose fp32 accumulation is accurate to the
-// last bits; PV, whose error only perturbs the accumulator by ~1e-5, stays on
-// the FP8 MFMA.
+// Scores.  By default QK^T runs on v_mfma_f32_16x16x128_f8f6f4 like PV.  Its
+// accumulation is not exact: inside each group of 8 consecutive channels the
+// products are cut toward zero 13 bits below the group's largest exponent sum
+// before the group sums are added, and that is the precision in which the
+// ExpCast codes are decided (the CPU simulation follows the same rule).  With
+// VC_EXACT_SCORES the E4M3 codes are multiplied as bf16 instead (every E4M3
+// value is exact in bf16) on v_mfma_f32_16x16x32_bf16, whose fp32 accumulation
+// is accurate to the last bits, at twice the matrix-core time of the FP8 path.
 //
 // Row sums and restore.  One more MFMA per block multiplies P by a ones row:
 // block b of a 16-block group puts its ones in A row b%16, so the group's row
@@ -37,8 +39,9 @@
 // MFMA group adds sum_b l_b * mu'_b to the accumulator: the restore costs no
 // per-element VALU work and no second pass over the keys.
 //
-// K tiles (bf16 codes, 32 KB) and V tiles (E4M3, 16 KB) are double-buffered in
-// LDS and filled by direct global->LDS loads while the previous block runs.
+// K tiles (E4M3 codes, 16 KB; bf16 codes, 32 KB, for exact scores) and V tiles
+// (E4M3, 16 KB) are double-buffered in LDS and filled by direct global->LDS
+// loads while the previous block runs.
 #include "vc_internal.h"
 
 namespace vc {
@@ -88,6 +91,12 @@ __device__ __forceinline__ v4f score_tile(const uint8_t* Kt, int row, int g, con
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) s = mfma_bf16_k32(lds_k16(Kt, row, kc, g), qop[kc], s);
   return s;
+}
+
+// S^T tile (16 keys x 16 queries) from E4M3 K rows and the query operand.
+__device__ __forceinline__ v4f score_tile8(const uint8_t* Kt, int row, int g, v8i qop) {
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return mfma_f8(lds_row32(Kt, row, g), qop, z);
 }
 
 __device__ __forceinline__ uint32_t expcast_byte(float s, float alpha, float beta) {
@@ -210,8 +219,15 @@ __device__ __forceinline__ void restore_group(RowState& st, const uint16_t* mupt
   st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// Query operands of one wave: bf16 codes (exact scores) or E4M3 bytes.
+template <bool EXACT> struct QOp;
+template <> struct QOp<true> { v8bf v[2][4]; };
+template <> struct QOp<false> { v8i v[2]; };
+
+template <bool EXACT>
 __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
-  __shared__ __align__(1024) uint8_t ksm[2][BLK * D * 2];  // [stage] bf16 K rows
+  constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
+  __shared__ __align__(1024) uint8_t ksm[2][BLK * KROW];   // [stage] K rows
   __shared__ __align__(1024) uint8_t vsm[2][D * BLK];      // [stage] V^T codes
   __shared__ float alpha_s[2][BLK];
 
@@ -226,24 +242,35 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   const int wq = w & 3;             // wave within its query block
 
   const uint8_t* q8 = a.q8 + ((size_t)bh * a.Npad + (size_t)qbv * BLK) * D;
-  const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D);
+  const uint8_t* kg = EXACT ? reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D)
+                            : a.k8 + (size_t)bh * a.Npad * D;
   const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
   const float* sk = a.sk + (size_t)bh * a.nblk;
   const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
   const float sQa = a.sq[(size_t)bh * a.nblk + qbv];
 
-  // direct global->LDS loads of one key block: K (32 KB) as 32 regions of 4 rows,
-  // V^T (16 KB) as 16 regions of 8 rows; a lane lands at byte 16*lane of its
-  // region, i.e. in stored chunk lane%16 (K) or lane%8 (V) of its row, which
-  // holds the source chunk XOR the row's swizzle
+  // direct global->LDS loads of one key block: K as 1 KB regions of 4 bf16 rows
+  // (exact scores, 32 KB) or 8 E4M3 rows (16 KB), V^T (16 KB) as 16 regions of 8
+  // rows; a lane lands at byte 16*lane of its region, i.e. in stored chunk
+  // lane%16 (bf16 K) or lane%8 (E4M3 K, V) of its row, which holds the source
+  // chunk XOR the row's swizzle
   auto issue = [&](int kb) {
     uint8_t* kd = ksm[kb & 1];
     uint8_t* vd = vsm[kb & 1];
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * i + w;
-      const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
-      __builtin_amdgcn_global_load_lds(k16 + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024, 16, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + w;
+        const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
+        __builtin_amdgcn_global_load_lds(kg + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024, 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + w;
+        const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024, 16, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -253,20 +280,25 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     }
   };
 
-  // query operand: bf16 of the Q codes, lane (g, q) holds d = 32kc+8g..+7
-  v8bf qop[2][4];
+  // query operand, lane (g, q) holding d = 32g..32g+31: E4M3 bytes, or (exact
+  // scores) bf16 of the codes with chunk kc holding d = 32kc+8g..+7
+  QOp<EXACT> qop;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const uint8_t* qrow = q8 + (size_t)(wq * 32 + qs * 16 + l16) * D;
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const uint2 b = *reinterpret_cast<const uint2*>(qrow + 32 * kc + 8 * g);
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint2 b = *reinterpret_cast<const uint2*>(qrow + 32 * kc + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t byte = ((i < 4 ? b.x : b.y) >> (8 * (i & 3))) & 0xffu;
-        qop[qs][kc][i] = __builtin_bit_cast(
-            __bf16, (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0)) >> 16));
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t byte = ((i < 4 ? b.x : b.y) >> (8 * (i & 3))) & 0xffu;
+          qop.v[qs][kc][i] = __builtin_bit_cast(
+              __bf16, (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0)) >> 16));
+        }
       }
+    } else {
+      qop.v[qs] = *reinterpret_cast<const v8i*>(qrow + 32 * g);
     }
   }
 
@@ -281,18 +313,24 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     for (int ct = 0; ct < 8; ++ct) rs[qs].acc[ct] = zero;
   }
 
-  // S^T of one key block for both query subtiles (bf16 MFMA, exact products)
+  // S^T of one key block for both query subtiles
   auto qk = [&](int kb, v4f (&S)[2][8]) {
     const uint8_t* Ks = ksm[kb & 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      S[0][t] = zero;
-      S[1][t] = zero;
+      if constexpr (EXACT) {
+        S[0][t] = zero;
+        S[1][t] = zero;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const v8bf kop = lds_k16(Ks, 16 * t + l16, kc, g);
-        S[0][t] = mfma_bf16_k32(kop, qop[0][kc], S[0][t]);
-        S[1][t] = mfma_bf16_k32(kop, qop[1][kc], S[1][t]);
+        for (int kc = 0; kc < 4; ++kc) {
+          const v8bf kop = lds_k16(Ks, 16 * t + l16, kc, g);
+          S[0][t] = mfma_bf16_k32(kop, qop.v[0][kc], S[0][t]);
+          S[1][t] = mfma_bf16_k32(kop, qop.v[1][kc], S[1][t]);
+        }
+      } else {
+        const v8i kop = lds_row32(Ks, 16 * t + l16, g);
+        S[0][t] = mfma_f8(kop, qop.v[0], zero);
+        S[1][t] = mfma_f8(kop, qop.v[1], zero);
       }
     }
   };
@@ -360,12 +398,22 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   for (int grp = 0; grp < a.mpad / BLK; ++grp) {
     uint8_t* Ks = ksm[0];
     const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 512 * i, row = ch >> 4, cc = ch & 15;
-      const int pos = rp[row];
-      const uint4 kv = *reinterpret_cast<const uint4*>(k16 + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
-      *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
+      for (int i = 0; i < 4; ++i) {
+        const int ch = tid + 512 * i, row = ch >> 4, cc = ch & 15;
+        const int pos = rp[row];
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
+        *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ch = tid + 512 * i, row = ch >> 3, cc = ch & 7;
+        const int pos = rp[row];
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
+        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ ((row >> 1) & 7)) << 4)) = kv;
+      }
     }
     if (tid < BLK) {
       const int pos = rp[tid];
@@ -388,7 +436,11 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           const int t = 2 * u + tp;
-          const v4f S = score_tile(Ks, 16 * t + l16, g, qop[qs]);
+          v4f S;
+          if constexpr (EXACT)
+            S = score_tile(Ks, 16 * t + l16, g, qop.v[qs]);
+          else
+            S = score_tile8(Ks, 16 * t + l16, g, qop.v[qs]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const uint32_t code = expcast_byte(S[v], al[16 * t + 4 * g + v], beta);
@@ -434,7 +486,10 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
 
 hipError_t launch_forward(const Args& a, hipStream_t st) {
   const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
-  hipLaunchKernelGGL(k_fwd, dim3(tiles), dim3(512), 0, st, a);
+  if (a.flags & VC_EXACT_SCORES)
+    hipLaunchKernelGGL(k_fwd<true>, dim3(tiles), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_fwd<false>, dim3(tiles), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

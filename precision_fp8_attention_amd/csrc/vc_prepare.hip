@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
     }
     uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + cg * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-    if (isk) {
+    if (isk && (a.flags & VC_EXACT_SCORES)) {
       // the K codes decoded to bf16 (E4M3 values are exact in bf16)
       uint32_t h[4];
 #pragma unroll

@@ -28,7 +28,8 @@ def lib_params(B, H, N, C_, T=10, seed=0, rho=0.005, expcast_k=8, tau=0.0, flags
 def oracle_params(p) -> orc.Params:
     return orc.make_params(p.B, p.H, p.N, C_=p.n_clusters, T=p.kmeans_iters, seed=p.seed,
                            rho=p.rho, sm_scale=p.sm_scale, expcast_k=p.expcast_k, tau=p.tau,
-                           flags=p.flags & 7)
+                           flags=p.flags & (vc.VSMOOTH | vc.REPAIR | vc.PERMUTE_Q |
+                                            vc.EXACT_SCORES))
 
 
 def to_device(q, k, v):

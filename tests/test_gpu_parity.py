@@ -57,6 +57,8 @@ SMALL = [
     ("literal_56", 1, 2, 700, 4, dict(expcast_k=0)),
     ("repair_all", 1, 1, 260, 3, dict(rho=1.0)),
     ("custom_scale_seed", 1, 2, 513, 6, dict(sm_scale=0.05, seed=12345, T=3)),
+    ("exact_scores", 2, 2, 300, 5, dict(flags=1 | 2 | 4 | 16)),
+    ("exact_scores_one_token", 1, 1, 1, 1, dict(flags=1 | 2 | 4 | 16)),
 ]
 
 
@@ -70,11 +72,26 @@ def test_small_cases(label, B, H, N, C_, kw):
     _full_case(p, q, k, v, heads, np.arange(N, dtype=np.int32), label)
 
 
-def test_workload0_all_rows():
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_scores", "exact_scores"])
+def test_workload0_all_rows(exact):
+    import precision_fp8_attention_amd as vc
     q, k, v = inputs.make_inputs(0)
     wl = inputs.WORKLOADS[0]
-    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
-    _full_case(p, q, k, v, [0, 1], np.arange(wl["N"], dtype=np.int32), "workload0")
+    flags = vc.DEFAULT_FLAGS | (vc.EXACT_SCORES if exact else 0)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"], flags=flags)
+    _full_case(p, q, k, v, [0, 1], np.arange(wl["N"], dtype=np.int32),
+               "workload0" + ("_exact" if exact else ""))
+
+
+def test_workload3_exact_scores_sampled():
+    """The benchmark workload with exact scores (bf16 score MFMA), one head."""
+    import precision_fp8_attention_amd as vc
+    wl = inputs.WORKLOADS[3]
+    q, k, v = inputs.make_inputs(3)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"],
+                     flags=vc.DEFAULT_FLAGS | vc.EXACT_SCORES)
+    rows = G.sample_rows(wl["N"], 128, seed=33)
+    _full_case(p, q, k, v, [30], rows, "workload3_exact")
 
 
 @pytest.mark.parametrize("cfg,heads,nrows", [(1, [0, 23], 160), (2, [5, 17], 160),

@@ -66,10 +66,17 @@ __device__ __forceinline__ v4f mfma_bf16_k16(v4s a, v4s b, v4f c) {
 }
 
 // 32 bytes of row `row` of a 128x128 byte tile, 16-byte chunks 2g and 2g+1,
-// stored with the chunk index XOR-swizzled by (row/2)%8: the 16 rows a
-// ds_read_b128 serves together then cover all 64 banks once.
+// stored with the chunk index XOR-swizzled by row_swz(row).
+// Chunk swizzle of 128-byte tile rows.  ds_read_b128 on gfx950 reads a wave's
+// 64 x 16 bytes in four passes; with x = (row/2) % 8 and its two low bits
+// swapped, the lanes of every pass hit 16 distinct 16-byte bank groups for both
+// halves of the operand (measured: full LDS rate, where x itself halves it).
+__device__ __forceinline__ int row_swz(int row) {
+  const int x = (row >> 1) & 7;
+  return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+}
 __device__ __forceinline__ v8i lds_row32(const uint8_t* tile, int row, int g) {
-  const int sw = (row >> 1) & 7;
+  const int sw = row_swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * g) ^ sw) << 4));
   const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * g + 1) ^ sw) << 4));
   v8i r;
@@ -97,6 +104,31 @@ __device__ __forceinline__ v4f score_tile(const uint8_t* Kt, int row, int g, con
 __device__ __forceinline__ v4f score_tile8(const uint8_t* Kt, int row, int g, v8i qop) {
   const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
   return mfma_f8(lds_row32(Kt, row, g), qop, z);
+}
+
+// 16 bytes per lane from global memory into LDS at lds_dst + 16 * lane (the
+// wave's 1 KB region).  Written as inline assembly: with the builtin the compiler
+// cannot tell that the next tile does not alias the current one and waits for
+// the copy before every LDS read of the block.  The instruction writes no
+// registers; the kernel waits for it explicitly (vmcnt(0)) before the barrier
+// that publishes the tile.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "memory", "m0");
+#else
+  (void)src;
+  (void)lds_dst;
+#endif
+}
+
+// Makes the compiler complete the load of x at this point (an empty asm that
+// reads it), so that no wait for it lands inside a later loop.
+__device__ __forceinline__ void keep_loaded(v8i x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
 }
 
 __device__ __forceinline__ uint32_t expcast_byte(float s, float alpha, float beta) {
@@ -231,7 +263,10 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   __shared__ __align__(1024) uint8_t vsm[2][D * BLK];      // [stage] V^T codes
   __shared__ float alpha_s[2][BLK];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // block scales are read-only here: constant address space -> scalar loads
+  typedef __attribute__((address_space(4))) const float cfloat;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g = lane >> 4, l16 = lane & 15;
   const int npair = (a.nblk + 1) / 2;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -245,9 +280,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   const uint8_t* kg = EXACT ? reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D)
                             : a.k8 + (size_t)bh * a.Npad * D;
   const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
-  const float* sk = a.sk + (size_t)bh * a.nblk;
+  const cfloat* sk = reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sk + (size_t)bh * a.nblk));
   const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
-  const float sQa = a.sq[(size_t)bh * a.nblk + qbv];
+  const float sQa = *reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sq + (size_t)bh * a.nblk + qbv));
 
   // direct global->LDS loads of one key block: K as 1 KB regions of 4 bf16 rows
   // (exact scores, 32 KB) or 8 E4M3 rows (16 KB), V^T (16 KB) as 16 regions of 8
@@ -262,21 +297,21 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
       for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + w;
         const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
-        __builtin_amdgcn_global_load_lds(kg + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024, 16, 0, 0);
+        dma16(kg + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = 8 * i + w;
-        const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_global_load_lds(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024, 16, 0, 0);
+        const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
+        dma16(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024);
       }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 8 * i + w;
-      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ ((row >> 1) & 7);
-      __builtin_amdgcn_global_load_lds(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024, 16, 0, 0);
+      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
+      dma16(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024);
     }
   };
 
@@ -300,6 +335,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     } else {
       qop.v[qs] = *reinterpret_cast<const v8i*>(qrow + 32 * g);
     }
+  }
+
+  // complete the query loads here, not inside the key loop
+  if constexpr (!EXACT) {
+    keep_loaded(qop.v[0]);
+    keep_loaded(qop.v[1]);
   }
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -412,7 +453,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
         const int ch = tid + 512 * i, row = ch >> 3, cc = ch & 7;
         const int pos = rp[row];
         const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
-        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ ((row >> 1) & 7)) << 4)) = kv;
+        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv;
       }
     }
     if (tid < BLK) {

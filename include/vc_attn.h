@@ -157,6 +157,18 @@ vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
 vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
                           void* o, void* stream);
 
+/* vc_attn_forward that also writes every ExpCast probability byte of the main
+ * loop (the codes of P the article's ExpCast-FP8 section describes), for
+ * checking them code by code.  pcodes: device buffer of B*H*Npad*Npad bytes,
+ * [b*H+h][query position][key position], both positions in the order the kernel
+ * processes them (cluster order when VC_PERMUTE_Q, else original order for the
+ * queries; cluster order for the keys).  Keys >= N hold 0; rows >= N are
+ * written with the codes of a padding query.  The repaired tokens' final-M
+ * codes are not included.  Same errors as vc_attn_forward, plus
+ * VC_ERR_INVALID_ARG for a null pcodes.  Asynchronous. */
+vc_status vc_attn_forward_pcodes(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
+                                 void* o, void* pcodes, void* stream);
+
 /* Static description of a status code. */
 const char* vc_attn_status_string(vc_status s);
 

@@ -17,8 +17,8 @@ VSMOOTH, REPAIR, PERMUTE_Q, REUSE_CLUSTERS, EXACT_SCORES = 1, 2, 4, 8, 16
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 EXPORTS = ("vc_attn_default_params", "vc_attn_workspace_size", "vc_attn_workspace_layout",
-           "vc_attn_check_params", "vc_attn_prepare", "vc_attn_forward", "vc_attn_status_string",
-           "vc_attn_version")
+           "vc_attn_check_params", "vc_attn_prepare", "vc_attn_forward", "vc_attn_forward_pcodes",
+           "vc_attn_status_string", "vc_attn_version")
 
 
 class Params(C.Structure):
@@ -64,11 +64,13 @@ def lib() -> C.CDLL:
         L.vc_attn_prepare.argtypes = [P, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_size_t, C.c_void_p]
         L.vc_attn_forward.argtypes = [P, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+        L.vc_attn_forward_pcodes.argtypes = [P, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]
         L.vc_attn_status_string.argtypes = [C.c_int]
         L.vc_attn_status_string.restype = C.c_char_p
         L.vc_attn_version.restype = C.c_int32
         for f in ("vc_attn_workspace_layout", "vc_attn_check_params", "vc_attn_prepare",
-                  "vc_attn_forward"):
+                  "vc_attn_forward", "vc_attn_forward_pcodes"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -135,6 +137,16 @@ def forward(p: Params, workspace, o, stream=None) -> None:
                                _stream(stream))
     if st != OK:
         raise VCError(st, "vc_attn_forward")
+
+
+def forward_pcodes(p: Params, workspace, o, pcodes, stream=None) -> None:
+    """vc_attn_forward_pcodes: forward plus every ExpCast byte of the main loop in
+    pcodes (uint8 [B*H, Npad, Npad], processing order)."""
+    st = lib().vc_attn_forward_pcodes(C.byref(p), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _ptr(o),
+                                      _ptr(pcodes), _stream(stream))
+    if st != OK:
+        raise VCError(st, "vc_attn_forward_pcodes")
 
 
 def alloc_workspace(p: Params, device="cuda"):

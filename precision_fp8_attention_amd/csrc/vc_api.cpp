@@ -226,8 +226,8 @@ vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
   return launch_prepare(a, !reuse, hs) == hipSuccess ? VC_OK : VC_ERR_HIP;
 }
 
-vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t ws_bytes, void* o,
-                          void* stream) {
+static vc_status forward_impl(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
+                              void* o, uint8_t* pcodes, void* stream) {
   const vc_status st = check(p);
   if (st != VC_OK) return st;
   if (!o || !aligned(o, 16)) return VC_ERR_INVALID_ARG;
@@ -238,7 +238,22 @@ vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t
   if (!workspace || !aligned(workspace, 256) || ws_bytes < L.pub.total) return VC_ERR_WORKSPACE;
   Args a = make_args(p, s, L, const_cast<void*>(workspace));
   a.o = static_cast<uint16_t*>(o);
+  a.pcodes = pcodes;
   return launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? VC_OK : VC_ERR_HIP;
+}
+
+vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t ws_bytes, void* o,
+                          void* stream) {
+  return forward_impl(p, workspace, ws_bytes, o, nullptr, stream);
+}
+
+vc_status vc_attn_forward_pcodes(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
+                                 void* o, void* pcodes, void* stream) {
+  if (!pcodes || !aligned(pcodes, 16)) {
+    const vc_status st = check(p);
+    return st != VC_OK ? st : VC_ERR_INVALID_ARG;
+  }
+  return forward_impl(p, workspace, ws_bytes, o, static_cast<uint8_t*>(pcodes), stream);
 }
 
 const char* vc_attn_status_string(vc_status s) {

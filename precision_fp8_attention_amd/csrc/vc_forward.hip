@@ -390,6 +390,18 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     }
     pop[0] = softmax_codes(S[0], rs[0], alpha, a.bias, a.tau);
     pop[1] = softmax_codes(S[1], rs[1], alpha, a.bias, a.tau);
+    if (a.pcodes) {
+      // lane (g, q) holds keys 16t+4g..16t+4g+3 of query row q: one dword each
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        uint8_t* prow = a.pcodes + ((size_t)bh * a.Npad + (size_t)qb * BLK + wq * 32 + qs * 16 + l16) * a.Npad +
+                        (size_t)kb * BLK + 4 * g;
+        if (active) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) *reinterpret_cast<int*>(prow + 16 * t) = pop[qs][t];
+        }
+      }
+    }
   };
   // row sums (ones MFMA), P.V (FP8 MFMA) and the 16-block restore of one block
   auto pv = [&](int kb, const v8i (&pop)[2]) {

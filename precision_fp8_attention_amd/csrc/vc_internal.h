@@ -72,6 +72,7 @@ struct Args {
   float* err;
   int* rep_pos;
   uint16_t* rep_dt;
+  uint8_t* pcodes;  // optional [BH][Npad][Npad] ExpCast bytes of the main loop
 };
 
 // Private extension of the public layout (partial k-means sums).

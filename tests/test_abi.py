@@ -85,6 +85,10 @@ def test_pointer_and_workspace_errors_before_device_work():
     assert L.vc_attn_forward(None, fake, need, fake, None) == vc.ERR_INVALID_ARG
     bad = vc.default_params(1, 2, 1024, d=64)
     assert L.vc_attn_forward(C.byref(bad), fake, need, fake, None) == vc.ERR_UNSUPPORTED
+    assert L.vc_attn_forward_pcodes(P, fake, need, fake, None, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_forward_pcodes(P, fake, need, fake, mis, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_forward_pcodes(P, fake, need - 1, fake, fake, None) == vc.ERR_WORKSPACE
+    assert L.vc_attn_forward_pcodes(C.byref(bad), fake, need, fake, None, None) == vc.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("B,H,N,C_,rho", [(1, 2, 1024, 8, 0.005), (2, 24, 16544, 32, 0.005),

@@ -175,3 +175,66 @@ def test_output_in_original_order_when_inputs_permuted():
         ws, o = G.run(p, qd, kd, vd)
         res = G.check_output(p, qq, kk, vv, o, [0], rows, label=lab)
         assert res["rel_l2_exact"] < 0.1
+
+
+# ------------------------------------------------------------------ P codes
+
+PCODE_CASES = [
+    # (label, B, H, N, C, kwargs)
+    ("ragged", 1, 2, 300, 5, {}),
+    ("exact_scores", 1, 2, 300, 5, dict(flags=1 | 2 | 4 | 16)),
+    ("q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2)),
+    ("lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0)),
+    ("literal_56", 1, 1, 520, 4, dict(expcast_k=0)),
+]
+
+
+def _pcodes_case(p, q, k, v, heads, rows, label):
+    """Every ExpCast byte the GPU main loop wrote for the given rows equals the
+    oracle's code (the scores' accumulation rule included)."""
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    G.log(f"[case] pcodes {label}: B={p.B} H={p.H} N={p.N} flags={p.flags} tau={p.tau} k={p.expcast_k}")
+    npad = ((p.N + 127) // 128) * 128
+    qd, kd, vd = G.to_device(q, k, v)
+    ws = vc.alloc_workspace(p)
+    o = torch.empty_like(qd)
+    pc = torch.zeros(p.B * p.H * npad * npad, dtype=torch.uint8, device=qd.device)
+    vc.prepare(p, qd, kd, vd, ws)
+    vc.forward_pcodes(p, ws, o, pc)
+    o2 = torch.empty_like(qd)
+    vc.forward(p, ws, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "forward_pcodes changed the output"
+    P = G.oracle_params(p)
+    prep = orc.prepare(P, q, k, v, heads=heads)
+    gpc = pc.view(p.B * p.H, npad, npad).cpu().numpy()
+    total = bad = 0
+    for slot, hd in enumerate(heads):
+        _, opc = orc.forward_rows(P, prep, np.full(len(rows), slot, np.int32), rows, want_pcodes=True)
+        pos = prep["iperm"][slot][rows] if (p.flags & vc.PERMUTE_Q) else rows
+        got = gpc[hd][pos]
+        bad += int(np.sum(got != opc))
+        total += got.size
+    G.log(f"pcodes {label}: {bad} of {total} codes differ")
+    assert bad == 0, f"{label}: {bad} of {total} P codes differ from the oracle"
+
+
+@pytest.mark.parametrize("label,B,H,N,C_,kw", PCODE_CASES, ids=[c[0] for c in PCODE_CASES])
+def test_pcodes_match_oracle(label, B, H, N, C_, kw):
+    q, k, v = inputs.make_custom(B, H, N, seed=100 + len(label), rate=0.01, sigma=20.0)
+    p = G.lib_params(B, H, N, C_, **kw)
+    _pcodes_case(p, q, k, v, list(range(B * H)), np.arange(N, dtype=np.int32), label)
+
+
+def test_pcodes_workloads_0_and_1():
+    """All codes of workload 0, and sampled rows of two heads of workload 1
+    (4256 keys, text and image tokens)."""
+    for cfg, heads, nrows in ((0, [0, 1], None), (1, [3, 20], 96)):
+        wl = inputs.WORKLOADS[cfg]
+        q, k, v = inputs.make_inputs(cfg, heads=heads)
+        p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+        rows = (np.arange(wl["N"], dtype=np.int32) if nrows is None
+                else G.sample_rows(wl["N"], nrows, seed=7))
+        _pcodes_case(p, q, k, v, heads, rows, f"workload{cfg}")

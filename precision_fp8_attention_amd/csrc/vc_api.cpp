@@ -73,6 +73,7 @@ void layout_of(const Shape& s, FullLayout* out) {
   out->uhi = take(BH * N * D);
   out->ulo = take(BH * N * D);
   out->centfix = take(BH * C * D * 4);
+  out->kmcc = take(BH * C * 8);
   L.labels = take(BH * N * 4);
   L.perm = take(BH * N * 4);
   L.iperm = take(BH * N * 4);
@@ -130,6 +131,7 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.uhi = reinterpret_cast<int8_t*>(b + FL.uhi);
   a.ulo = reinterpret_cast<int8_t*>(b + FL.ulo);
   a.centfix = reinterpret_cast<int*>(b + FL.centfix);
+  a.kmcc = reinterpret_cast<long long*>(b + FL.kmcc);
   a.labels = reinterpret_cast<int*>(b + L.labels);
   a.perm = reinterpret_cast<int*>(b + L.perm);
   a.iperm = reinterpret_cast<int*>(b + L.iperm);

@@ -259,8 +259,11 @@ template <> struct QOp<false> { v8i v[2]; };
 template <bool EXACT>
 __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
-  __shared__ __align__(1024) uint8_t ksm[2][BLK * KROW];   // [stage] K rows
-  __shared__ __align__(1024) uint8_t vsm[2][D * BLK];      // [stage] V^T codes
+  // LDS stages: FP8 mode holds four key blocks (two computed per barrier while
+  // the next two land), exact-score mode two (its bf16 K tiles are twice as big)
+  constexpr int NST = EXACT ? 2 : 4;
+  __shared__ __align__(1024) uint8_t ksm[NST][BLK * KROW];   // [stage] K rows
+  __shared__ __align__(1024) uint8_t vsm[NST][D * BLK];      // [stage] V^T codes
   __shared__ float alpha_s[2][BLK];
 
   // block scales are read-only here: constant address space -> scalar loads
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   // lane%16 (bf16 K) or lane%8 (E4M3 K, V) of its row, which holds the source
   // chunk XOR the row's swizzle
   auto issue = [&](int kb) {
-    uint8_t* kd = ksm[kb & 1];
-    uint8_t* vd = vsm[kb & 1];
+    uint8_t* kd = ksm[kb % NST];
+    uint8_t* vd = vsm[kb % NST];
     if constexpr (EXACT) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
 
   // S^T of one key block for both query subtiles
   auto qk = [&](int kb, v4f (&S)[2][8]) {
-    const uint8_t* Ks = ksm[kb & 1];
+    const uint8_t* Ks = ksm[kb % NST];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if constexpr (EXACT) {
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   };
   // row sums (ones MFMA), P.V (FP8 MFMA) and the 16-block restore of one block
   auto pv = [&](int kb, const v8i (&pop)[2]) {
-    const uint8_t* Vs = vsm[kb & 1];
+    const uint8_t* Vs = vsm[kb % NST];
     // ones in A row kb%16: the block's row sum accumulates in L element v of
     // lane group g where 4g+v = kb%16
     const int onesrow = kb & 15;
@@ -428,22 +431,52 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     }
   };
 
-  // Every wave runs QK(kb), softmax(kb), PV(kb) per key block; block kb+1 lands
-  // in the other LDS stage meanwhile.  (Offsetting half of the waves by half a
+  // Every wave runs QK(kb), softmax(kb), PV(kb) per key block while the next
+  // blocks land in the other LDS stages.  (Offsetting half of the waves by half a
   // block, so that one wave per SIMD is on VALU work while the other feeds the
-  // matrix core, measured slower on gfx950.)
-  issue(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kb = 0; kb < a.nblk; ++kb) {
-    if (kb + 1 < a.nblk) issue(kb + 1);
-    v4f S[2][8];
-    v8i pop[2];
-    qk(kb, S);
-    soft(kb, S, pop);
-    pv(kb, pop);
+  // matrix core, measured slower on gfx950: VALU and MFMA work of one SIMD barely
+  // overlap there, whichever waves issue them.)
+  if constexpr (NST == 4) {
+    // two key blocks per barrier (half the barrier waits of one): blocks kb,
+    // kb+1 run while kb+2, kb+3 land
+    issue(0);
+    if (a.nblk > 1) issue(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    for (int kb = 0; kb < a.nblk; kb += 2) {
+      if (kb + 2 < a.nblk) issue(kb + 2);
+      if (kb + 3 < a.nblk) issue(kb + 3);
+      {
+        v4f S[2][8];
+        v8i pop[2];
+        qk(kb, S);
+        soft(kb, S, pop);
+        pv(kb, pop);
+      }
+      if (kb + 1 < a.nblk) {
+        v4f S[2][8];
+        v8i pop[2];
+        qk(kb + 1, S);
+        soft(kb + 1, S, pop);
+        pv(kb + 1, pop);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  } else {
+    issue(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kb = 0; kb < a.nblk; ++kb) {
+      if (kb + 1 < a.nblk) issue(kb + 1);
+      v4f S[2][8];
+      v8i pop[2];
+      qk(kb, S);
+      soft(kb, S, pop);
+      pv(kb, pop);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
 
   // Repair: the selected tokens' residual error, weighted by codes formed with

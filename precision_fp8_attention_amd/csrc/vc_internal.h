@@ -54,6 +54,7 @@ struct Args {
   int8_t* uhi;        // [BH][N][128] high part (u >> 7) of the fixed-point V
   int8_t* ulo;        // [BH][N][128] low part (u & 127)
   int* centfix;       // [BH][C][128] fixed-point centroids
+  long long* kmcc;    // [BH][C] squared norms of the fixed-point centroids
   int* labels;
   int* perm;
   int* iperm;
@@ -78,7 +79,7 @@ struct Args {
 // Private extension of the public layout (partial k-means sums).
 struct FullLayout {
   vc_attn_ws_layout pub;
-  size_t kmpart, kmcnt, vmaxp, kmsh, uhi, ulo, centfix;
+  size_t kmpart, kmcnt, vmaxp, kmsh, uhi, ulo, centfix, kmcc;
 };
 
 bool shape_of(const vc_attn_params* p, Shape* s);

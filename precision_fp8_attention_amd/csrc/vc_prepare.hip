@@ -185,6 +185,17 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
 // fixed-point value of token idx[k].  The draws do not depend on the swaps, so
 // lane i computes draw i; wave 0 then replays the swaps over a sparse map held
 // one entry per lane.  grid BH, 128 threads.
+// Sum of one int64 per thread over a 128-thread block (exact).  red: 2 slots of
+// shared memory.  Every thread gets the total.
+__device__ __forceinline__ long long sum128_i64(long long x, long long* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return red[0] + red[1];
+}
+
 __global__ __launch_bounds__(128) void k_km_init(Args a) {
   __shared__ int jdraw[MAX_CLUSTERS];
   __shared__ int idx[MAX_CLUSTERS];
@@ -224,11 +235,14 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
   }
   __syncthreads();
   const int sh = a.kmsh[bh];
+  __shared__ long long red[2];
   for (int kk = 0; kk < C; ++kk) {
     const size_t src = ((size_t)bh * a.N + idx[kk]) * D + t;
     const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
     a.centfix[((size_t)bh * C + kk) * D + t] = u;
     a.cent[((size_t)bh * C + kk) * D + t] = ldexpf((float)u, -sh);
+    const long long cc = sum128_i64((long long)u * u, red);
+    if (t == 0) a.kmcc[(size_t)bh * C + kk] = cc;
   }
   if (t < C) a.init_idx[(size_t)bh * C + t] = idx[t];
 }
@@ -257,13 +271,19 @@ __device__ __forceinline__ void add_bins(int* bins, int base, const v4i& h, cons
 
 constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measured 13 us
                              // less per Lloyd iteration at N=16544, 48 heads)
+// Shared memory of k_km_assign for C clusters (sized at launch, so that with 32
+// clusters four workgroups fit on a CU instead of three).
+constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 + 4 * BROW + 4); }
+
 __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
-  __shared__ __align__(16) int8_t chi[MAX_CLUSTERS * CROW];
-  __shared__ __align__(16) int8_t clo[MAX_CLUSTERS * CROW];
-  __shared__ long long cc[MAX_CLUSTERS];
-  __shared__ int bins[MAX_CLUSTERS * BROW];
-  __shared__ int cnt[MAX_CLUSTERS];
-  const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, C = a.C;
+  extern __shared__ __align__(16) unsigned char km_smem[];
+  const int C = a.C;
+  int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                    // [C][CROW]
+  int8_t* clo = chi + C * CROW;                                        // [C][CROW]
+  long long* cc = reinterpret_cast<long long*>(clo + C * CROW);        // [C]
+  int* bins = reinterpret_cast<int*>(cc + C);                          // [C][BROW]
+  int* cnt = bins + C * BROW;                                          // [C]
+  const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
   const int* cf = a.centfix + (size_t)bh * C * D;
   for (int e = t; e < C * D; e += 64 * KM_WAVES) {
@@ -273,9 +293,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
     bins[(e / D) * BROW + (e % D)] = 0;
   }
   if (t < C) {
-    long long s = 0;
-    for (int c = 0; c < D; ++c) s += (long long)cf[t * D + c] * cf[t * D + c];
-    cc[t] = s;
+    cc[t] = a.kmcc[(size_t)bh * C + t];
     cnt[t] = 0;
   }
   __syncthreads();
@@ -324,11 +342,11 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int k = 16 * kt + 4 * g + v;
-        if (k < C) {
-          const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
-          const long long Dk = cc[k] - 2 * dot;
-          if (Dk < bestD) { bestD = Dk; best = k; }
-        }
+        const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
+        const long long ck = cc[k < C ? k : 0];
+        const long long Dk = k < C ? ck - 2 * dot : 0x7fffffffffffffffll;
+        best = Dk < bestD ? k : best;
+        bestD = Dk < bestD ? Dk : bestD;
       }
     }
     // argmin across the four lane groups; ties go to the lower id
@@ -363,11 +381,17 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
     s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
     n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
   }
+  int u;
   if (n > 0) {
-    const int u = (int)__builtin_rint((double)s / (double)n);
+    u = (int)__builtin_rint((double)s / (double)n);
     a.centfix[((size_t)bh * C + kk) * D + c] = u;
     a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -a.kmsh[bh]);
+  } else {
+    u = a.centfix[((size_t)bh * C + kk) * D + c];
   }
+  __shared__ long long red[2];
+  const long long cc = sum128_i64((long long)u * u, red);
+  if (c == 0) a.kmcc[(size_t)bh * C + kk] = cc;
 }
 
 // ---------------------------------------------------------------------------
@@ -823,7 +847,7 @@ hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
       hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
       hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
       for (int it = 0; it < a.T; ++it) {
-        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(64 * KM_WAVES), 0, st, a);
+        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(64 * KM_WAVES), km_smem_bytes(a.C), st, a);
         hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
       }
       hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);

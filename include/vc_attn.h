@@ -30,9 +30,9 @@
  * Ownership.  The caller allocates Q, K, V, O and the workspace on the device and
  * keeps them alive until the stream has finished the calls.  The library never
  * allocates or frees device memory and never synchronises the stream, except
- * vc_attn_prepare with VC_REUSE_CLUSTERS, which reads 64 bytes of the workspace
- * header back to the host (one stream synchronisation) to check that clusters
- * exist for the same shape.  The library has no global mutable state; calls on
+ * vc_attn_prepare with VC_REUSE_CLUSTERS or VC_WARM_START, which reads 64 bytes
+ * of the workspace header back to the host (one stream synchronisation) to check
+ * that clusters exist for the same shape.  The library has no global mutable state; calls on
  * different streams with different workspaces may run concurrently.  Two calls
  * that share a workspace must be ordered by the caller.
  *
@@ -57,7 +57,8 @@ typedef enum {
   VC_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, out-of-range parameter */
   VC_ERR_UNSUPPORTED = 2,  /* d != 128 or block != 128 */
   VC_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
-  VC_ERR_NOT_PREPARED = 4, /* VC_REUSE_CLUSTERS without clusters for this shape */
+  VC_ERR_NOT_PREPARED = 4, /* VC_REUSE_CLUSTERS / VC_WARM_START without clusters
+                              for this shape */
   VC_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
   VC_ERR_INTERNAL = 6
 } vc_status;
@@ -71,6 +72,14 @@ enum {
   VC_REUSE_CLUSTERS = 8u, /* prepare skips k-means and reuses labels/permutation
                             already in the workspace (clustering runs only in the
                             early denoising steps, as the V-Smooth section says) */
+  VC_WARM_START = 32u,   /* k-means starts from the centroids a previous prepare of
+                            the same shape left in the workspace (a denoising step
+                            close to the last one) instead of the seeded Forgy
+                            draw; each is rescaled to the current fixed-point
+                            exponent, rounded and clamped to 14 bits.  Needs
+                            VC_VSMOOTH, excludes VC_REUSE_CLUSTERS; without
+                            clusters of this shape prepare returns
+                            VC_ERR_NOT_PREPARED */
   VC_EXACT_SCORES = 16u  /* QK^T as the exact dot product of the E4M3 codes (bf16
                             MFMA, twice the matrix-core time) instead of the FP8
                             MFMA, whose accumulation cuts each product 13 bits below

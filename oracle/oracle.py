@@ -27,6 +27,7 @@ VSMOOTH = 1
 REPAIR = 2
 PERMUTE_Q = 4
 EXACT_SCORES = 16
+WARM_START = 32
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 
@@ -72,6 +73,8 @@ def lib():
         L.oc_splitmix64_array.argtypes = [C.c_uint64, vp, i64]
         L.oc_score_array.argtypes = [vp, vp, i64, i32, i32, vp]
         L.oc_kmeans_init_indices.argtypes = [C.c_uint64, i64, i32, i32, vp]
+        L.oc_kmeans_shift.argtypes = [vp, i64]
+        L.oc_kmeans_shift.restype = C.c_int
         L.oc_repair_count.argtypes = [C.POINTER(Params)]
         L.oc_repair_count.restype = i32
         for f in (L.oc_prepare, L.oc_forward_rows, L.oc_exact_rows):
@@ -94,11 +97,12 @@ def repair_count(P: Params) -> int:
     return int(lib().oc_repair_count(C.byref(P)))
 
 
-def prepare(P: Params, q, k, v, heads=None) -> dict:
+def prepare(P: Params, q, k, v, heads=None, init_centroids=None) -> dict:
     """Run the prepare stage on the listed global heads (default: all).
 
     q, k, v are uint16 bf16 bit arrays [B, H, N, 128].  Returns a dict of numpy
-    arrays whose first axis is the slot (position in `heads`)."""
+    arrays whose first axis is the slot (position in `heads`).  init_centroids
+    (fp32 [nheads, C, 128]) are the starting centroids when P has WARM_START."""
     B, H, N, d = P.B, P.H, P.N, P.d
     heads = np.arange(B * H, dtype=np.int32) if heads is None else np.asarray(heads, np.int32)
     nh = len(heads)
@@ -116,6 +120,10 @@ def prepare(P: Params, q, k, v, heads=None) -> dict:
         sv=np.zeros((nh, d), np.float32), inv=np.zeros((nh, d), np.float32),
         err=np.zeros((nh, N), np.float32), rep_pos=np.zeros((nh, mcap), np.int32),
         rep_delta=np.zeros((nh, mcap, d), np.uint16))
+    if P.flags & WARM_START:
+        if init_centroids is None:
+            raise ValueError("WARM_START needs init_centroids")
+        out["centroids"][...] = np.asarray(init_centroids, np.float32).reshape(nh, P.C, d)
     pr = _Prep(*[out[n].ctypes.data for n, _ in _Prep._fields_[:-1]], mcap)
     q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
     rc = lib().oc_prepare(C.byref(P), _ptr(q), _ptr(k), _ptr(v), _ptr(heads), nh, C.byref(pr))
@@ -198,6 +206,12 @@ def kmeans_init_indices(seed: int, head: int, N: int, C_: int) -> np.ndarray:
     out = np.zeros(C_, np.int32)
     lib().oc_kmeans_init_indices(seed, head, N, C_, _ptr(out))
     return out
+
+
+def kmeans_shift(v) -> int:
+    """Fixed-point exponent sh of a head's values (max|v| * 2^sh < 2^13)."""
+    vf = np.ascontiguousarray(v, np.float32)
+    return int(lib().oc_kmeans_shift(_ptr(vf), vf.size))
 
 
 def code_gain(sm_scale: float, d: int = 128) -> np.float32:

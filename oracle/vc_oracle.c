@@ -34,6 +34,10 @@
  *     integers; ties go to the lowest cluster id; a non-empty cluster moves to
  *     the mean of its members rounded to the nearest integer (ties to even), an
  *     empty one keeps its centroid; labels are those of the last assignment.
+ *     With OC_WARM_START the Lloyd rounds start instead from the centroids
+ *     passed in the output array (those of a previous denoising step): each is
+ *     scaled by 2^sh of the current values, rounded to the nearest integer (ties
+ *     to even) and clamped to [-2^13, 2^13 - 1].
  *   - means (K channel mean, V block means, centroids) are exact sums of values
  *     rounded to 2^-24 fixed point, divided once in fp64, rounded to fp32.
  *   - the permutation is a stable sort of positions by cluster id; Q follows it
@@ -71,6 +75,7 @@
 #define OC_REPAIR 2u
 #define OC_PERMUTE_Q 4u
 #define OC_EXACT_SCORES 16u
+#define OC_WARM_START 32u
 
 typedef struct {
   int32_t B, H, N, d;     /* d must be 128 */
@@ -250,9 +255,17 @@ static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d
   int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * (size_t)C);
 
   for (size_t i = 0; i < (size_t)N * d; ++i) u[i] = (int32_t)llrintf(ldexpf(v[i], sh));
-  oc_kmeans_init_indices(P->seed, head, N, C, init);
-  for (int k = 0; k < C; ++k)
-    for (int ch = 0; ch < d; ++ch) c[(size_t)k * d + ch] = u[(size_t)init[k] * d + ch];
+  if (P->flags & OC_WARM_START) {
+    /* previous step's centroids, in the current fixed-point scale */
+    for (size_t i = 0; i < (size_t)C * d; ++i) {
+      int64_t x = llrintf(ldexpf(cent[i], sh));
+      c[i] = x < -8192 ? -8192 : (x > 8191 ? 8191 : x);
+    }
+  } else {
+    oc_kmeans_init_indices(P->seed, head, N, C, init);
+    for (int k = 0; k < C; ++k)
+      for (int ch = 0; ch < d; ++ch) c[(size_t)k * d + ch] = u[(size_t)init[k] * d + ch];
+  }
 
   for (int it = 0; it < P->T; ++it) {
     /* assignment step: argmin_k ||c_k||^2 - 2 u.c_k, exact integers */

@@ -28,7 +28,9 @@ static vc_status check(const vc_attn_params* p) {
   if (!std::isfinite(p->sm_scale)) return VC_ERR_INVALID_ARG;
   if (!(p->tau >= 0.0f) || 56.0f + 8.0f * p->expcast_k + p->tau > 126.0f) return VC_ERR_INVALID_ARG;
   if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS |
-                         VC_EXACT_SCORES))
+                         VC_EXACT_SCORES | VC_WARM_START))
+    return VC_ERR_INVALID_ARG;
+  if ((p->flags & VC_WARM_START) && (!(p->flags & VC_VSMOOTH) || (p->flags & VC_REUSE_CLUSTERS)))
     return VC_ERR_INVALID_ARG;
   return VC_OK;
 }
@@ -211,7 +213,8 @@ vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool vs = (p->flags & VC_VSMOOTH) != 0;
   const bool reuse = vs && (p->flags & VC_REUSE_CLUSTERS);
-  if (reuse) {
+  const bool warm = vs && (p->flags & VC_WARM_START);
+  if (reuse || warm) {
     Header h;
     if (hipMemcpyAsync(&h, static_cast<uint8_t*>(workspace) + L.pub.header, sizeof(h),
                        hipMemcpyDeviceToHost, hs) != hipSuccess)
@@ -225,7 +228,8 @@ vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
-  return launch_prepare(a, !reuse, hs) == hipSuccess ? VC_OK : VC_ERR_HIP;
+  const ClusterMode mode = reuse ? ClusterMode::Reuse : (warm ? ClusterMode::Warm : ClusterMode::Cold);
+  return launch_prepare(a, mode, hs) == hipSuccess ? VC_OK : VC_ERR_HIP;
 }
 
 static vc_status forward_impl(const vc_attn_params* p, const void* workspace, size_t ws_bytes,

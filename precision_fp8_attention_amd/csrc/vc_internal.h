@@ -86,7 +86,11 @@ bool shape_of(const vc_attn_params* p, Shape* s);
 void layout_of(const Shape& s, FullLayout* out);
 Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& L, void* ws);
 
-hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st);
+// How prepare obtains the clusters: seeded Forgy start, start from the previous
+// centroids in the workspace, or the previous labels/permutation unchanged.
+enum class ClusterMode { Cold, Warm, Reuse };
+
+hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st);
 hipError_t launch_forward(const Args& a, hipStream_t st);
 
 }  // namespace vc

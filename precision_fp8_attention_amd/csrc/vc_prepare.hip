@@ -185,11 +185,17 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
 // fixed-point value of token idx[k].  The draws do not depend on the swaps, so
 // lane i computes draw i; wave 0 then replays the swaps over a sparse map held
 // one entry per lane.  grid BH, 128 threads.
+// Sum of one int64 per lane over a wave (exact).
+__device__ __forceinline__ long long wave_sum_i64(long long x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 // Sum of one int64 per thread over a 128-thread block (exact).  red: 2 slots of
 // shared memory.  Every thread gets the total.
 __device__ __forceinline__ long long sum128_i64(long long x, long long* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  x = wave_sum_i64(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
@@ -235,16 +241,38 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
   }
   __syncthreads();
   const int sh = a.kmsh[bh];
-  __shared__ long long red[2];
+  __shared__ long long part[2][MAX_CLUSTERS];
   for (int kk = 0; kk < C; ++kk) {
     const size_t src = ((size_t)bh * a.N + idx[kk]) * D + t;
     const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
     a.centfix[((size_t)bh * C + kk) * D + t] = u;
     a.cent[((size_t)bh * C + kk) * D + t] = ldexpf((float)u, -sh);
-    const long long cc = sum128_i64((long long)u * u, red);
-    if (t == 0) a.kmcc[(size_t)bh * C + kk] = cc;
+    const long long s2 = wave_sum_i64((long long)u * u);
+    if ((t & 63) == 0) part[t >> 6][kk] = s2;
   }
+  __syncthreads();
+  if (t < C) a.kmcc[(size_t)bh * C + t] = part[0][t] + part[1][t];
   if (t < C) a.init_idx[(size_t)bh * C + t] = idx[t];
+}
+
+// Warm start: the previous step's centroids (fp32, in the workspace) in the
+// current fixed-point scale, rounded to the nearest integer (ties to even) and
+// clamped to 14 bits.  grid BH, 128 threads (one per channel).
+__global__ __launch_bounds__(128) void k_km_warm(Args a) {
+  __shared__ long long part[2][MAX_CLUSTERS];
+  const int bh = blockIdx.x, C = a.C, t = threadIdx.x;
+  const int sh = a.kmsh[bh];
+  for (int kk = 0; kk < C; ++kk) {
+    const size_t o = ((size_t)bh * C + kk) * D + t;
+    const float x = fminf(fmaxf(__builtin_rintf(ldexpf(a.cent[o], sh)), -8192.0f), 8191.0f);
+    const int u = (int)x;
+    a.centfix[o] = u;
+    a.cent[o] = ldexpf((float)u, -sh);
+    const long long s2 = wave_sum_i64((long long)u * u);
+    if ((t & 63) == 0) part[t >> 6][kk] = s2;
+  }
+  __syncthreads();
+  if (t < C) a.kmcc[(size_t)bh * C + t] = part[0][t] + part[1][t];
 }
 
 // Assignment step on int8 MFMA plus per-workgroup member sums.
@@ -837,15 +865,18 @@ __global__ void k_header(Args a, uint32_t clustered) {
 
 }  // namespace
 
-hipError_t launch_prepare(const Args& a, bool recluster, hipStream_t st) {
+hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
   const unsigned BH = (unsigned)a.BH;
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
   hipLaunchKernelGGL(k_ksum, dim3(a.nkc, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_kbar, dim3(BH), dim3(128), 0, st, a);
   if (vs) {
-    if (recluster) {
+    if (mode != ClusterMode::Reuse) {
       hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
-      hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
+      if (mode == ClusterMode::Warm)
+        hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
+      else
+        hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
       for (int it = 0; it < a.T; ++it) {
         hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(64 * KM_WAVES), km_smem_bytes(a.C), st, a);
         hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);

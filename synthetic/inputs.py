@@ -176,3 +176,13 @@ def make_custom(B: int, H: int, N: int, seed: int = 0, rate: float = 0.01, sigma
                     vv[toks, chans[ci]] += add[:, ci]
             q[b, h], k[b, h], v[b, h] = to_bf16_bits(qq), to_bf16_bits(kk), to_bf16_bits(vv)
     return q, k, v
+
+
+def drift(v: np.ndarray, step: int, seed: int = 0, scale: float = 0.05) -> np.ndarray:
+    """Values of a later denoising step: v (bf16 bits, any shape ending in 128)
+    plus independent N(0, scale) noise per element from a stream seeded by
+    (seed, step), rounded back to bf16.  Small steps keep the clusters close
+    to those of the previous step, as consecutive diffusion steps do."""
+    x = bf16_bits_to_f32(np.ascontiguousarray(v)).astype(np.float64)
+    x = x + normals(subseed(seed, 0xD41F7, step), x.size, 0.0, scale).reshape(x.shape)
+    return to_bf16_bits(x)

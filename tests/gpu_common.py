@@ -29,7 +29,7 @@ def oracle_params(p) -> orc.Params:
     return orc.make_params(p.B, p.H, p.N, C_=p.n_clusters, T=p.kmeans_iters, seed=p.seed,
                            rho=p.rho, sm_scale=p.sm_scale, expcast_k=p.expcast_k, tau=p.tau,
                            flags=p.flags & (vc.VSMOOTH | vc.REPAIR | vc.PERMUTE_Q |
-                                            vc.EXACT_SCORES))
+                                            vc.EXACT_SCORES | vc.WARM_START))
 
 
 def to_device(q, k, v):

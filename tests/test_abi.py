@@ -53,6 +53,8 @@ BAD = [
     (dict(expcast_k=0, tau=71.0), vc.ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), vc.ERR_INVALID_ARG),
     (dict(flags=64), vc.ERR_INVALID_ARG),
+    (dict(flags=vc.WARM_START | vc.REPAIR), vc.ERR_INVALID_ARG),  # warm start needs V-Smooth
+    (dict(flags=vc.DEFAULT_FLAGS | vc.WARM_START | vc.REUSE_CLUSTERS), vc.ERR_INVALID_ARG),
 ]
 
 

@@ -238,3 +238,56 @@ def test_pcodes_workloads_0_and_1():
         rows = (np.arange(wl["N"], dtype=np.int32) if nrows is None
                 else G.sample_rows(wl["N"], nrows, seed=7))
         _pcodes_case(p, q, k, v, heads, rows, f"workload{cfg}")
+
+
+# ------------------------------------------------------------------ warm start
+
+@pytest.mark.parametrize("cfg_or_shape", ["small", "workload0"])
+def test_warm_start_after_drift_matches_oracle(cfg_or_shape):
+    """Denoising-step sequence: cold prepare on V, then a warm-started prepare
+    (3 Lloyd rounds from the previous centroids) on drifted V.  The warm
+    prepare's arrays are bit-identical to the oracle's warm start from its own
+    cold centroids, and the output is within tolerance."""
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    if cfg_or_shape == "small":
+        B, H, N, C_ = 1, 2, 700, 5
+        q, k, v = inputs.make_custom(B, H, N, seed=21, rate=0.01, sigma=20.0)
+    else:
+        wl = inputs.WORKLOADS[0]
+        B, H, N, C_ = wl["B"], wl["H"], wl["N"], wl["C"]
+        q, k, v = inputs.make_inputs(0)
+    v1 = inputs.drift(v, step=1, seed=21)
+    heads = list(range(B * H))
+    pc = G.lib_params(B, H, N, C_)
+    pw = G.lib_params(B, H, N, C_, T=3, flags=vc.DEFAULT_FLAGS | vc.WARM_START)
+    G.log(f"[case] warm start {cfg_or_shape}: B={B} H={H} N={N} C={C_}")
+    qd, kd, vd = G.to_device(q, k, v)
+    vd1 = G.to_device(q, k, v1)[2]
+    ws = vc.alloc_workspace(pc)
+    o = torch.empty_like(qd)
+    vc.prepare(pc, qd, kd, vd, ws)
+    vc.prepare(pw, qd, kd, vd1, ws)
+    vc.forward(pw, ws, o)
+    torch.cuda.synchronize()
+    Pc, Pw = G.oracle_params(pc), G.oracle_params(pw)
+    cold = orc.prepare(Pc, q, k, v, heads=heads)
+    ora = orc.prepare(Pw, q, k, v1, heads=heads, init_centroids=cold["centroids"])
+    gpu = G.read_prepared(pw, ws, heads)
+    bad = G.compare_prepared(gpu, ora, vsmooth=True)
+    assert not bad, f"warm start prepare mismatch: {bad}"
+    G.check_output(pw, q, k, v1, o, heads, np.arange(N, dtype=np.int32), prep_oracle=ora,
+                   label=f"warm_{cfg_or_shape}")
+
+
+def test_warm_start_needs_clusters():
+    import precision_fp8_attention_amd as vc
+    q, k, v = inputs.make_custom(1, 1, 300, seed=22)
+    qd, kd, vd = G.to_device(q, k, v)
+    pw = G.lib_params(1, 1, 300, 4, flags=vc.DEFAULT_FLAGS | vc.WARM_START)
+    ws = vc.alloc_workspace(pw)
+    ws.zero_()
+    with pytest.raises(vc.VCError) as e:
+        vc.prepare(pw, qd, kd, vd, ws)
+    assert e.value.status == vc.ERR_NOT_PREPARED

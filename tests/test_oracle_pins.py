@@ -519,3 +519,76 @@ def test_demean_restore_identity_fp64():
         mu = v[sl].mean(0)
         acc += p[:, sl] @ (v[sl] - mu) + p[:, sl].sum(1, keepdims=True) * mu
     np.testing.assert_allclose(acc / p.sum(1, keepdims=True), ref, rtol=1e-12)
+
+
+# ------------------------------------------------------------------ warm start
+
+def _cold(P, q, k, v):
+    pr = orc.prepare(P, q, k, v)
+    return pr["labels"].copy(), pr["centroids"].copy()
+
+
+def test_warm_start_from_forgy_centroids_equals_cold_start():
+    """Starting the Lloyd rounds from the seeded Forgy draw (given as centroids)
+    reproduces the cold start exactly."""
+    q, k, v = inputs.make_custom(1, 2, 300, seed=11)
+    Pc = orc.make_params(1, 2, 300, C_=5, T=4)
+    lab, cen = _cold(Pc, q, k, v)
+    vf = inputs.bf16_bits_to_f32(v).reshape(2, 300, 128)
+    init = np.stack([vf[h][orc.kmeans_init_indices(0, h, 300, 5)] for h in range(2)])
+    sh = [orc.kmeans_shift(vf[h]) for h in range(2)]
+    # centroids as the oracle stores them: integers at 2^-sh
+    init = np.stack([np.ldexp(np.rint(np.ldexp(init[h].astype(np.float64), sh[h])), -sh[h])
+                     for h in range(2)]).astype(np.float32)
+    Pw = orc.make_params(1, 2, 300, C_=5, T=4, flags=orc.DEFAULT_FLAGS | orc.WARM_START)
+    pr = orc.prepare(Pw, q, k, v, init_centroids=init)
+    np.testing.assert_array_equal(pr["labels"], lab)
+    np.testing.assert_array_equal(pr["centroids"], cen)
+
+
+def test_converged_centroids_are_a_fixed_point_of_warm_start():
+    """Lloyd's fixed point: from converged centroids one more round changes
+    neither labels nor centroids."""
+    q, k, v = inputs.make_custom(1, 1, 400, seed=12)
+    lab60, cen60 = _cold(orc.make_params(1, 1, 400, C_=4, T=60), q, k, v)
+    lab61, cen61 = _cold(orc.make_params(1, 1, 400, C_=4, T=61), q, k, v)
+    np.testing.assert_array_equal(lab60, lab61)   # converged
+    Pw = orc.make_params(1, 1, 400, C_=4, T=1, flags=orc.DEFAULT_FLAGS | orc.WARM_START)
+    pr = orc.prepare(Pw, q, k, v, init_centroids=cen60)
+    np.testing.assert_array_equal(pr["labels"], lab60)
+    np.testing.assert_array_equal(pr["centroids"], cen60)
+
+
+def test_warm_start_after_drift_keeps_sse_low():
+    """After a small drift, three warm rounds reach a within-cluster energy no
+    worse than ten cold rounds from the seeded draw (within 2%)."""
+    q, k, v = inputs.make_custom(1, 1, 600, seed=13)
+    _, cen = _cold(orc.make_params(1, 1, 600, C_=6, T=10), q, k, v)
+    v1 = inputs.drift(v, step=1, seed=13)
+    Pw = orc.make_params(1, 1, 600, C_=6, T=3, flags=orc.DEFAULT_FLAGS | orc.WARM_START)
+    prw = orc.prepare(Pw, q, k, v1, init_centroids=cen)
+    prc = orc.prepare(orc.make_params(1, 1, 600, C_=6, T=10), q, k, v1)
+    vf = inputs.bf16_bits_to_f32(v1).reshape(600, 128).astype(np.float64)
+
+    def sse(pr):
+        c = pr["centroids"][0].astype(np.float64)
+        return float(np.sum((vf - c[pr["labels"][0]]) ** 2))
+    assert sse(prw) <= 1.02 * sse(prc), (sse(prw), sse(prc))
+
+
+def test_warm_start_clamps_to_fourteen_bits():
+    """Centroids far outside the current value range are clamped to the 14-bit
+    fixed-point range instead of wrapping."""
+    q, k, v = inputs.make_custom(1, 1, 200, seed=14)
+    init = np.full((1, 3, 128), 1.0e6, np.float32)
+    init[0, 1] = -1.0e6
+    init[0, 2] = 0.0
+    Pw = orc.make_params(1, 1, 200, C_=3, T=1, flags=orc.DEFAULT_FLAGS | orc.WARM_START)
+    pr = orc.prepare(Pw, q, k, v, init_centroids=init)
+    vf = inputs.bf16_bits_to_f32(v).reshape(200, 128)
+    sh = orc.kmeans_shift(vf)
+    # every token is nearest to the zero centroid or to a clamped corner; the
+    # clamped corners sit at +-(2^13 - 1) or -2^13 in fixed point
+    assert set(np.unique(pr["labels"])) <= {0, 1, 2}
+    assert np.all(np.isfinite(pr["centroids"]))
+    assert np.max(np.abs(np.ldexp(pr["centroids"].astype(np.float64), sh))) <= 8192

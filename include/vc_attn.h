@@ -136,9 +136,8 @@ typedef struct {
   size_t err;        /* f32 [BH][N] repair criterion per position                */
   size_t rep_pos;    /* i32 [BH][mpad] repaired positions ascending, padded with -1 */
   size_t rep_dt;     /* bf16 [BH][128][mpad] residual error of the repaired tokens
-                        in V code units, channel-major, slots in order; with
-                        VC_EXACT_SCORES, inside each 128-slot group slot
-                        32u+16t'+4g+v sits at column 32u+8g+4t'+v instead        */
+                        in V code units, channel-major; inside each 128-slot group
+                        slot 32u+16t'+4g+v sits at column 32u+8g+4t'+v           */
 } vc_attn_ws_layout;
 
 /* Fill *p with the defaults: d = block = 128, C = 16, T = 10, k = 8, seed 0,

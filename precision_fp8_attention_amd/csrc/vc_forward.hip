@@ -1,4 +1,4 @@
-// Fused VC-Attention FP8 forward kernels for gfx950.
+// Fused VC-Attention FP8 forward kernel for gfx950.
 //
 // Method (noticiai.com.br VC-Attention article, sections "V-Smooth" (Restore) and
 // "ExpCast-FP8"; ip73.fr article, section "Le compromis entre vitesse et
@@ -16,37 +16,32 @@
 //
 // Layout.  A workgroup of 8 waves owns two 128-row query blocks; wave w owns
 // rows 32w..32w+31 as two 16-row subtiles.  Scores are computed transposed
-// (S^T = K . Q^T) on 16x16 tiles, so each lane holds 32 keys of one query: key
-// 16t+4g+v of the block in S[t][v], g = lane/16.  Prepare stores V8 channel-major
-// with the key interleave that makes those ExpCast bytes the B operand of
-// O^T = V8^T . P^T directly: P never touches LDS.  v_cvt_pk_u8_f32 rounds to
-// nearest even, saturates to [0, 255] and inserts the byte, so one fma and one
-// convert produce each packed code.
+// (S^T = K . Q^T) so each lane holds 32 keys of one query: key 16t+4g+v of the
+// block in S[t][v], g = lane/16.  Those 32 ExpCast bytes are exactly the lane's
+// B operand of O^T = V8^T . P^T on v_mfma_f32_16x16x128_f8f6f4, because prepare
+// stores V8 channel-major with the same key interleave: P never touches LDS.
+// v_cvt_pk_u8_f32 rounds to nearest even, saturates to [0, 255] and inserts the
+// byte, so one fma and one convert produce each packed code.
 //
-// Two kernels share that layout:
-//  * k_fwd (FP8 scores, the default): QK^T on v_mfma_f32_16x16x128_f8f6f4, P.V
-//    and row sums on v_mfma_scale_f32_32x32x64_f8f6f4 (one permlane16 swap per
-//    dword regroups the two subtiles' bytes into the 32-query operand), restore
-//    every 32 blocks, four LDS stages, two key blocks per barrier.
-//  * k_fwd_exact (VC_EXACT_SCORES): QK^T from bf16 K codes on
-//    v_mfma_f32_16x16x32_bf16 (every E4M3 value is exact in bf16, and its fp32
-//    accumulation is accurate to the last bits), P.V on 16x16x128, restore every
-//    16 blocks, two LDS stages (its K tiles are twice as big).
-//
-// Scores.  The FP8 score MFMA is not exact: inside each group of 8 consecutive
-// channels the products are cut toward zero 13 bits below the group's largest
-// exponent sum before the group sums are added, and that is the precision in
-// which the ExpCast codes are decided (the CPU simulation follows the same rule).
+// Scores.  By default QK^T runs on v_mfma_f32_16x16x128_f8f6f4 like PV.  Its
+// accumulation is not exact: inside each group of 8 consecutive channels the
+// products are cut toward zero 13 bits below the group's largest exponent sum
+// before the group sums are added, and that is the precision in which the
+// ExpCast codes are decided (the CPU simulation follows the same rule).  With
+// VC_EXACT_SCORES the E4M3 codes are multiplied as bf16 instead (every E4M3
+// value is exact in bf16) on v_mfma_f32_16x16x32_bf16, whose fp32 accumulation
+// is accurate to the last bits, at twice the matrix-core time of the FP8 path.
 //
 // Row sums and restore.  One more MFMA per block multiplies P by a ones row:
-// block b of a restore group puts its ones in A row b % (group size), so the
-// group's row sums collect in one accumulator L.  At the end of each group L is
-// split into bf16 high and low parts and bf16 MFMAs add sum_b l_b * mu'_b to the
-// accumulator: the restore costs no per-element VALU work and no second pass
-// over the keys.
+// block b of a 16-block group puts its ones in A row b%16, so the group's row
+// sums collect in a 16x16 accumulator L (lane (g, q), element v = block 4g+v).
+// Every 16 blocks L is split into bf16 high and low parts and one 16x16x16 bf16
+// MFMA group adds sum_b l_b * mu'_b to the accumulator: the restore costs no
+// per-element VALU work and no second pass over the keys.
 //
-// K tiles and V tiles are filled by direct global->LDS loads while earlier
-// blocks run.
+// K tiles (E4M3 codes, 16 KB; bf16 codes, 32 KB, for exact scores) and V tiles
+// (E4M3, 16 KB) are double-buffered in LDS and filled by direct global->LDS
+// loads while the previous block runs.
 #include "vc_internal.h"
 
 namespace vc {
@@ -181,53 +176,20 @@ struct RowState {
   v4f acc[8];   // O^T accumulator: channel 16ct+4g+v, query q
 };
 
-// New running maximum of one subtile for one key block (no side effects): the
-// block maximum in code units replaces it when it is higher by more than tau.
-__device__ __forceinline__ float block_max(const v4f (&S)[8], float Mo, float alpha, float tau) {
+// Softmax of one 16-query subtile for one key block: new maximum, rescale of the
+// running state, ExpCast codes packed as the PV B operand.
+__device__ __forceinline__ v8i softmax_codes(v4f (&S)[8], RowState& st, float alpha, float bias,
+                                             float tau) {
   float mx = S[0][0];
 #pragma unroll
   for (int t = 0; t < 8; ++t) mx = fmaxf(fmaxf(mx, S[t][0]), fmaxf(fmaxf(S[t][1], S[t][2]), S[t][3]));
   mx = xmax32(xmax16(mx));
   const float tmax = mx * alpha;
-  return (Mo == -INFINITY || tmax - Mo > tau) ? tmax : Mo;
-}
-// ExpCast codes of one subtile when |M| < 2^21: |fma - (bias + tau)| then stays
-// below half a code, so the saturating convert needs no upper clamp
-__device__ __forceinline__ v8i codes_fast(const v4f (&S)[8], float alpha, float beta) {
-  v8i pop;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    uint32_t d = 0;
-    d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][0], alpha, beta), 0, d);
-    d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][1], alpha, beta), 1, d);
-    d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][2], alpha, beta), 2, d);
-    d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][3], alpha, beta), 3, d);
-    pop[t] = (int)d;
-  }
-  return pop;
-}
-// ExpCast codes of one subtile with the full clamp (any M)
-__device__ __forceinline__ v8i codes_slow(const v4f (&S)[8], float alpha, float beta) {
-  v8i pop;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    uint32_t d = 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) d |= expcast_byte(S[t][v], alpha, beta) << (8 * v);
-    pop[t] = (int)d;
-  }
-  return pop;
-}
-
-// Softmax of one 16-query subtile for one key block (16x16 accumulator layout):
-// new maximum, rescale of the running state, ExpCast codes packed as the PV B
-// operand.
-__device__ __forceinline__ v8i softmax_codes(v4f (&S)[8], RowState& st, float alpha, float bias,
-                                             float tau) {
   const float Mo = st.M;
-  const float Mn = block_max(S, Mo, alpha, tau);
+  const bool first = Mo == -INFINITY;
+  const float Mn = (first || tmax - Mo > tau) ? tmax : Mo;
   if (Mn != Mo) {
-    const float r = Mo == -INFINITY ? 0.0f : exp2f((Mo - Mn) * 0.125f);
+    const float r = first ? 0.0f : exp2f((Mo - Mn) * 0.125f);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= r;
     st.L *= r;
@@ -235,7 +197,28 @@ __device__ __forceinline__ v8i softmax_codes(v4f (&S)[8], RowState& st, float al
     st.M = Mn;
   }
   const float beta = bias - Mn;
-  return fabsf(Mn) < 0x1p21f ? codes_fast(S, alpha, beta) : codes_slow(S, alpha, beta);
+  v8i pop;
+  if (fabsf(Mn) < 0x1p21f) {
+    // |fma - (bias + tau)| stays below half a code: no upper clamp needed
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t d = 0;
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][0], alpha, beta), 0, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][1], alpha, beta), 1, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][2], alpha, beta), 2, d);
+      d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[t][3], alpha, beta), 3, d);
+      pop[t] = (int)d;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) d |= expcast_byte(S[t][v], alpha, beta) << (8 * v);
+      pop[t] = (int)d;
+    }
+  }
+  return pop;
 }
 
 // Adds sum_b L[b] * mu'[b] of a finished 16-block group (bf16 hi/lo split, three
@@ -268,11 +251,17 @@ __device__ __forceinline__ void restore_group(RowState& st, const uint16_t* mupt
   st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// Exact-score forward (VC_EXACT_SCORES): scores from bf16 K codes on the bf16
-// MFMA, P.V and row sums on the 16x16x128 FP8 MFMA, 16-block restore groups.
-__global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
-  constexpr int KROW = 2 * D;  // bytes per bf16 K row in LDS
-  constexpr int NST = 2;       // LDS stages: one block computed while the next lands
+// Query operands of one wave: bf16 codes (exact scores) or E4M3 bytes.
+template <bool EXACT> struct QOp;
+template <> struct QOp<true> { v8bf v[2][4]; };
+template <> struct QOp<false> { v8i v[2]; };
+
+template <bool EXACT>
+__global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
+  constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
+  // LDS stages: FP8 mode holds four key blocks (two computed per barrier while
+  // the next two land), exact-score mode two (its bf16 K tiles are twice as big)
+  constexpr int NST = EXACT ? 2 : 4;
   __shared__ __align__(1024) uint8_t ksm[NST][BLK * KROW];   // [stage] K rows
   __shared__ __align__(1024) uint8_t vsm[NST][D * BLK];      // [stage] V^T codes
   __shared__ float alpha_s[2][BLK];
@@ -291,24 +280,35 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
   const int wq = w & 3;             // wave within its query block
 
   const uint8_t* q8 = a.q8 + ((size_t)bh * a.Npad + (size_t)qbv * BLK) * D;
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D);
+  const uint8_t* kg = EXACT ? reinterpret_cast<const uint8_t*>(a.k16 + (size_t)bh * a.Npad * D)
+                            : a.k8 + (size_t)bh * a.Npad * D;
   const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
   const cfloat* sk = reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sk + (size_t)bh * a.nblk));
   const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
   const float sQa = *reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sq + (size_t)bh * a.nblk + qbv));
 
   // direct global->LDS loads of one key block: K as 1 KB regions of 4 bf16 rows
-  // (32 KB), V^T (16 KB) as 16 regions of 8 rows; a lane lands at byte 16*lane
-  // of its region, i.e. in stored chunk lane%16 (K) or lane%8 (V) of its row,
-  // which holds the source chunk XOR the row's swizzle
+  // (exact scores, 32 KB) or 8 E4M3 rows (16 KB), V^T (16 KB) as 16 regions of 8
+  // rows; a lane lands at byte 16*lane of its region, i.e. in stored chunk
+  // lane%16 (bf16 K) or lane%8 (E4M3 K, V) of its row, which holds the source
+  // chunk XOR the row's swizzle
   auto issue = [&](int kb) {
     uint8_t* kd = ksm[kb % NST];
     uint8_t* vd = vsm[kb % NST];
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * i + w;
-      const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
-      dma16(kg + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + w;
+        const int row = 4 * r + (lane >> 4), cc = (lane & 15) ^ (row & 15);
+        dma16(kg + ((size_t)kb * BLK + row) * 256 + cc * 16, kd + r * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + w;
+        const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
+        dma16(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -318,21 +318,32 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
     }
   };
 
-  // query operand, lane (g, q): bf16 of the codes, chunk kc holding d = 32kc+8g..+7
-  v8bf qop[2][4];
+  // query operand, lane (g, q) holding d = 32g..32g+31: E4M3 bytes, or (exact
+  // scores) bf16 of the codes with chunk kc holding d = 32kc+8g..+7
+  QOp<EXACT> qop;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const uint8_t* qrow = q8 + (size_t)(wq * 32 + qs * 16 + l16) * D;
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const uint2 b = *reinterpret_cast<const uint2*>(qrow + 32 * kc + 8 * g);
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint2 b = *reinterpret_cast<const uint2*>(qrow + 32 * kc + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t byte = ((i < 4 ? b.x : b.y) >> (8 * (i & 3))) & 0xffu;
-        qop[qs][kc][i] = __builtin_bit_cast(
-            __bf16, (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0)) >> 16));
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t byte = ((i < 4 ? b.x : b.y) >> (8 * (i & 3))) & 0xffu;
+          qop.v[qs][kc][i] = __builtin_bit_cast(
+              __bf16, (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0)) >> 16));
+        }
       }
+    } else {
+      qop.v[qs] = *reinterpret_cast<const v8i*>(qrow + 32 * g);
     }
+  }
+
+  // complete the query loads here, not inside the key loop
+  if constexpr (!EXACT) {
+    keep_loaded(qop.v[0]);
+    keep_loaded(qop.v[1]);
   }
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -351,13 +362,19 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
     const uint8_t* Ks = ksm[kb % NST];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      S[0][t] = zero;
-      S[1][t] = zero;
+      if constexpr (EXACT) {
+        S[0][t] = zero;
+        S[1][t] = zero;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const v8bf kop = lds_k16(Ks, 16 * t + l16, kc, g);
-        S[0][t] = mfma_bf16_k32(kop, qop[0][kc], S[0][t]);
-        S[1][t] = mfma_bf16_k32(kop, qop[1][kc], S[1][t]);
+        for (int kc = 0; kc < 4; ++kc) {
+          const v8bf kop = lds_k16(Ks, 16 * t + l16, kc, g);
+          S[0][t] = mfma_bf16_k32(kop, qop.v[0][kc], S[0][t]);
+          S[1][t] = mfma_bf16_k32(kop, qop.v[1][kc], S[1][t]);
+        }
+      } else {
+        const v8i kop = lds_row32(Ks, 16 * t + l16, g);
+        S[0][t] = mfma_f8(kop, qop.v[0], zero);
+        S[1][t] = mfma_f8(kop, qop.v[1], zero);
       }
     }
   };
@@ -415,22 +432,51 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
   };
 
   // Every wave runs QK(kb), softmax(kb), PV(kb) per key block while the next
-  // block lands in the other LDS stage.  (Offsetting half of the waves by half a
+  // blocks land in the other LDS stages.  (Offsetting half of the waves by half a
   // block, so that one wave per SIMD is on VALU work while the other feeds the
   // matrix core, measured slower on gfx950: VALU and MFMA work of one SIMD barely
   // overlap there, whichever waves issue them.)
-  issue(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kb = 0; kb < a.nblk; ++kb) {
-    if (kb + 1 < a.nblk) issue(kb + 1);
-    v4f S[2][8];
-    v8i pop[2];
-    qk(kb, S);
-    soft(kb, S, pop);
-    pv(kb, pop);
+  if constexpr (NST == 4) {
+    // two key blocks per barrier (half the barrier waits of one): blocks kb,
+    // kb+1 run while kb+2, kb+3 land
+    issue(0);
+    if (a.nblk > 1) issue(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    for (int kb = 0; kb < a.nblk; kb += 2) {
+      if (kb + 2 < a.nblk) issue(kb + 2);
+      if (kb + 3 < a.nblk) issue(kb + 3);
+      {
+        v4f S[2][8];
+        v8i pop[2];
+        qk(kb, S);
+        soft(kb, S, pop);
+        pv(kb, pop);
+      }
+      if (kb + 1 < a.nblk) {
+        v4f S[2][8];
+        v8i pop[2];
+        qk(kb + 1, S);
+        soft(kb + 1, S, pop);
+        pv(kb + 1, pop);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  } else {
+    issue(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kb = 0; kb < a.nblk; ++kb) {
+      if (kb + 1 < a.nblk) issue(kb + 1);
+      v4f S[2][8];
+      v8i pop[2];
+      qk(kb, S);
+      soft(kb, S, pop);
+      pv(kb, pop);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
 
   // Repair: the selected tokens' residual error, weighted by codes formed with
@@ -438,12 +484,22 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
   for (int grp = 0; grp < a.mpad / BLK; ++grp) {
     uint8_t* Ks = ksm[0];
     const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 512 * i, row = ch >> 4, cc = ch & 15;
-      const int pos = rp[row];
-      const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
-      *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
+      for (int i = 0; i < 4; ++i) {
+        const int ch = tid + 512 * i, row = ch >> 4, cc = ch & 15;
+        const int pos = rp[row];
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
+        *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ch = tid + 512 * i, row = ch >> 3, cc = ch & 7;
+        const int pos = rp[row];
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
+        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv;
+      }
     }
     if (tid < BLK) {
       const int pos = rp[tid];
@@ -466,7 +522,11 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           const int t = 2 * u + tp;
-          const v4f S = score_tile(Ks, 16 * t + l16, g, qop[qs]);
+          v4f S;
+          if constexpr (EXACT)
+            S = score_tile(Ks, 16 * t + l16, g, qop.v[qs]);
+          else
+            S = score_tile8(Ks, 16 * t + l16, g, qop.v[qs]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const uint32_t code = expcast_byte(S[v], al[16 * t + 4 * g + v], beta);
@@ -508,288 +568,14 @@ __global__ __launch_bounds__(512, 1) void k_fwd_exact(Args a) {
   }
 }
 
-
-// ---------------------------------------------------------------------------
-// FP8-score forward with P.V on 32x32x64 MFMAs.
-//
-// Scores, maxima and ExpCast codes come from 16x16x128 score tiles, two 16-query
-// subtiles per wave, exactly as in k_fwd_exact but with E4M3 K.  One permlane16
-// swap per dword then turns the two subtiles' P bytes into the B operand of the
-// 32x32x64 MFMA for all 32 queries of the wave: a lane of row r (16 lanes) keeps
-// the keys of its own key class r and takes class r^1 from lane ^ 16, which
-// holds the same query.  K position 32h + 4t + v of key chunk c is then key
-// 16t + 4(c + 2h) + v, which is what 32-byte column group c + 2h of the stored
-// V^T rows holds: the V^T layout is shared with k_fwd_exact.  The 32x32 shape
-// halves the MFMA issue count of P.V and leaves more room for VALU work beside
-// each (64-cycle) instruction.
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ v16f mfma32_f8(v8i a, v8i b, v16f c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-__device__ __forceinline__ v16f mfma32_bf16(v8bf a, v8bf b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
-  __shared__ __align__(1024) uint8_t ksm[4][BLK * D];   // [stage] K codes
-  __shared__ __align__(1024) uint8_t vsm[4][D * BLK];   // [stage] V^T codes
-  typedef __attribute__((address_space(4))) const float cfloat;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, l16 = lane & 15;
-  const int h = lane >> 5, n = lane & 31;  // 32x32 coordinates: query n, K half h
-  const int npair = (a.nblk + 1) / 2;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int wg = w >> 2;
-  const int bh = logical / npair, qb = 2 * (logical % npair) + wg;
-  const bool active = qb < a.nblk;
-  const int qbv = active ? qb : qb - 1;
-  const int wq = w & 3;
-
-  const uint8_t* q8 = a.q8 + ((size_t)bh * a.Npad + (size_t)qbv * BLK) * D;
-  const uint8_t* kg = a.k8 + (size_t)bh * a.Npad * D;
-  const uint8_t* v8t = a.v8t + (size_t)bh * D * a.Npad;
-  const cfloat* sk = reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sk + (size_t)bh * a.nblk));
-  const uint16_t* mupt = a.mupt + (size_t)bh * a.nch16 * 2 * D * 16;
-  const float sQa = *reinterpret_cast<const cfloat*>(reinterpret_cast<uintptr_t>(a.sq + (size_t)bh * a.nblk + qbv));
-
-  auto issue = [&](int kb) {
-    uint8_t* kd = ksm[kb & 3];
-    uint8_t* vd = vsm[kb & 3];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * i + w;
-      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
-      dma16(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024);
-      dma16(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024);
-    }
-  };
-
-  v8i qop[2];
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
-    qop[qs] = *reinterpret_cast<const v8i*>(q8 + (size_t)(wq * 32 + qs * 16 + l16) * D + 32 * g);
-  keep_loaded(qop[0]);
-  keep_loaded(qop[1]);
-
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  v16f z16;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z16[i] = 0.0f;
-  float M[2] = {-INFINITY, -INFINITY};  // running maxima of the two subtiles (16x16 layout)
-  v16f acc[4], L = z16;                 // O^T (channels 32ct+8j+4h+v, query n), row sums
-  float ell = 0.0f;                     // flushed row sum of query n
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = z16;
-
-  // adds sum_b L[b] * mu'[b] of the 32-block group G and moves L into ell
-  auto restore = [&](int G) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += L[i];
-    ell += xsum32(s);
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int ch16 = 2 * G + cc;
-      if (ch16 < a.nch16) {
-        v8bf bh_, bl_;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = L[8 * cc + e];
-          const uint16_t hb = f2bf_rne(x);
-          bh_[e] = __builtin_bit_cast(__bf16, hb);
-          bl_[e] = __builtin_bit_cast(__bf16, f2bf_rne(x - __uint_as_float((uint32_t)hb << 16)));
-        }
-        const uint16_t* hip = mupt + (size_t)ch16 * 2 * D * 16;
-        const uint16_t* lop = hip + D * 16;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int c = 32 * ct + n;
-          const uint2 h0 = *reinterpret_cast<const uint2*>(hip + c * 16 + 4 * h);
-          const uint2 h1 = *reinterpret_cast<const uint2*>(hip + c * 16 + 8 + 4 * h);
-          const uint2 l0 = *reinterpret_cast<const uint2*>(lop + c * 16 + 4 * h);
-          const uint2 l1 = *reinterpret_cast<const uint2*>(lop + c * 16 + 8 + 4 * h);
-          const v8bf ah = __builtin_bit_cast(v8bf, make_uint4(h0.x, h0.y, h1.x, h1.y));
-          const v8bf al = __builtin_bit_cast(v8bf, make_uint4(l0.x, l0.y, l1.x, l1.y));
-          v16f x = acc[ct];
-          x = mfma32_bf16(ah, bh_, x);
-          x = mfma32_bf16(ah, bl_, x);
-          x = mfma32_bf16(al, bh_, x);
-          acc[ct] = x;
-        }
-      }
-    }
-    L = z16;
-  };
-
-  auto block = [&](int kb) {
-    const uint8_t* Ks = ksm[kb & 3];
-    const uint8_t* Vs = vsm[kb & 3];
-    const float alpha = (sQa * sk[kb]) * a.c0;
-    v4f S[2][8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const v8i kop = lds_row32(Ks, 16 * t + l16, g);
-      S[0][t] = mfma_f8(kop, qop[0], zero);
-      S[1][t] = mfma_f8(kop, qop[1], zero);
-    }
-    const int nvalid = a.N - kb * BLK;
-    if (nvalid < BLK) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (16 * t + 4 * g + v >= nvalid) S[qs][t][v] = -INFINITY;
-    }
-    float Mn[2];
-    v8i pop[2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      Mn[qs] = block_max(S[qs], M[qs], alpha, a.tau);
-      pop[qs] = codes_fast(S[qs], alpha, a.bias - Mn[qs]);
-    }
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-      if (!(fabsf(Mn[qs]) < 0x1p21f)) pop[qs] = codes_slow(S[qs], alpha, a.bias - Mn[qs]);
-    if (a.pcodes && active) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        uint8_t* prow = a.pcodes + ((size_t)bh * a.Npad + (size_t)qb * BLK + wq * 32 + qs * 16 + l16) * a.Npad +
-                        (size_t)kb * BLK + 4 * g;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) *reinterpret_cast<int*>(prow + 16 * t) = pop[qs][t];
-      }
-    }
-    // rescale the running state of every query whose maximum moved
-    const bool ch0 = Mn[0] != M[0], ch1 = Mn[1] != M[1];
-    if (__builtin_amdgcn_ballot_w64(ch0 || ch1)) {
-      const float r0 = ch0 ? (M[0] == -INFINITY ? 0.0f : exp2f((M[0] - Mn[0]) * 0.125f)) : 1.0f;
-      const float r1 = ch1 ? (M[1] == -INFINITY ? 0.0f : exp2f((M[1] - Mn[1]) * 0.125f)) : 1.0f;
-      const float r = (g & 1) ? r1 : r0;  // this lane's 32x32 query is 16*(g&1) + l16
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[ct] *= r;
-      L *= r;
-      ell *= r;
-    }
-    M[0] = Mn[0];
-    M[1] = Mn[1];
-    // 16x16 P bytes -> 32x32x64 B operands of the two 64-key chunks
-    v8i B0, B1;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)pop[0][t], (uint32_t)pop[1][t], false, false);
-      B0[t] = (int)sw[0];
-      B1[t] = (int)sw[1];
-    }
-    const int o = (n == (kb & 31)) ? 0x38383838 : 0;
-    v8i onesop;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) onesop[i] = o;
-    L = mfma32_f8(onesop, B0, L);
-    L = mfma32_f8(onesop, B1, L);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      acc[ct] = mfma32_f8(lds_row32(Vs, 32 * ct + n, 2 * h), B0, acc[ct]);
-      acc[ct] = mfma32_f8(lds_row32(Vs, 32 * ct + n, 1 + 2 * h), B1, acc[ct]);
-    }
-    if ((kb & 31) == 31 || kb + 1 == a.nblk) restore(kb >> 5);
-  };
-
-  issue(0);
-  if (a.nblk > 1) issue(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kb = 0; kb < a.nblk; kb += 2) {
-    if (kb + 2 < a.nblk) issue(kb + 2);
-    if (kb + 3 < a.nblk) issue(kb + 3);
-    block(kb);
-    if (kb + 1 < a.nblk) block(kb + 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  // Repair: codes of the selected tokens with the final maxima and each token's
-  // own K block scale, times their residual error (bf16, natural slot order).
-  // one alpha table per query block: the two blocks have their own Q scale
-  float* alpha_s = reinterpret_cast<float*>(ksm[1]) + wg * BLK;
-  for (int grp = 0; grp < a.mpad / BLK; ++grp) {
-    uint8_t* Ks = ksm[0];
-    const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int chk = tid + 512 * i, row = chk >> 3, cc = chk & 7;
-      const int pos = rp[row];
-      const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
-      *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv;
-    }
-    if ((tid & 255) < BLK) {  // waves 0-1 for query block 0, waves 4-5 for block 1
-      const int j = tid & 127, pos = rp[j];
-      alpha_s[j] = (sQa * a.sk[(size_t)bh * a.nblk + (pos < 0 ? 0 : pos / BLK)]) * a.c0;
-    }
-    __syncthreads();
-    const uint16_t* dt = a.rep_dt + (size_t)bh * D * a.mpad + (size_t)grp * BLK;
-#pragma unroll 1
-    for (int t = 0; t < 8; ++t) {
-      uint32_t bp[2][2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const v4f S = score_tile8(Ks, 16 * t + l16, g, qop[qs]);
-        const float beta = a.bias - M[qs];
-        uint16_t hv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t code = expcast_byte(S[v], alpha_s[16 * t + 4 * g + v], beta);
-          hv[v] = f2bf_rne(__builtin_amdgcn_cvt_f32_fp8((int)code, 0));  // exact in bf16
-        }
-        bp[qs][0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-        bp[qs][1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-      }
-      const auto s0 = __builtin_amdgcn_permlane16_swap(bp[0][0], bp[1][0], false, false);
-      const auto s1 = __builtin_amdgcn_permlane16_swap(bp[0][1], bp[1][1], false, false);
-      const v8bf bop = __builtin_bit_cast(v8bf, make_uint4(s0[0], s1[0], s0[1], s1[1]));
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const uint4 av = *reinterpret_cast<const uint4*>(dt + (size_t)(32 * ct + n) * a.mpad + 16 * t + 8 * h);
-        acc[ct] = mfma32_bf16(__builtin_bit_cast(v8bf, av), bop, acc[ct]);
-      }
-    }
-    __syncthreads();
-  }
-
-  // Epilogue: O = sV * acc / l, bf16, scattered back to the original row.
-  const float* sv = a.sv + (size_t)bh * D;
-  const int p = qb * BLK + wq * 32 + n;
-  if (active && p < a.N) {
-    const int orig = (a.flags & VC_PERMUTE_Q) ? a.perm[(size_t)bh * a.N + p] : p;
-    const float il = 1.0f / ell;
-    uint16_t* orow = a.o + ((size_t)bh * a.N + orig) * D;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = 32 * ct + 8 * j + 4 * h;
-        const float4 s4 = *reinterpret_cast<const float4*>(sv + c);
-        uint2 pk;
-        pk.x = (uint32_t)f2bf_rne(s4.x * acc[ct][4 * j + 0] * il) |
-               ((uint32_t)f2bf_rne(s4.y * acc[ct][4 * j + 1] * il) << 16);
-        pk.y = (uint32_t)f2bf_rne(s4.z * acc[ct][4 * j + 2] * il) |
-               ((uint32_t)f2bf_rne(s4.w * acc[ct][4 * j + 3] * il) << 16);
-        *reinterpret_cast<uint2*>(orow + c) = pk;
-      }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_forward(const Args& a, hipStream_t st) {
   const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
   if (a.flags & VC_EXACT_SCORES)
-    hipLaunchKernelGGL(k_fwd_exact, dim3(tiles), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(k_fwd<true>, dim3(tiles), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL(k_fwd, dim3(tiles), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(k_fwd<false>, dim3(tiles), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -816,14 +816,13 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
 }
 
-// Residual error (code units, bf16) of the repaired positions, channel-major;
-// slots in order for the FP8-score kernel (32x32 operand), with the repair-slot
-// interleave for the exact-score one.  grid (mpad/128, BH), 128 threads = slots.
+// Residual error (code units, bf16) of the repaired positions, channel-major
+// with the repair-slot interleave.  grid (mpad/128, BH), 128 threads = slots.
 __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
   __shared__ __align__(16) uint16_t tile[D * BLK];
   const int grp = blockIdx.x, bh = blockIdx.y, s = threadIdx.x;
   const int gs = grp * BLK + s;
-  const int col = (a.flags & VC_EXACT_SCORES) ? rep_col(s) : s;
+  const int col = rep_col(s);
   const int p = gs < a.m ? a.rep_pos[(size_t)bh * a.mpad + gs] : -1;
   if (p >= 0) {
     const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;

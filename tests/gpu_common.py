@@ -93,8 +93,7 @@ def read_prepared(p, ws, heads) -> dict:
         out["rep_pos"] = arr("rep_pos", np.int32, (BH, mpad))[:, :m]
         dt = arr("rep_dt", np.uint16, (BH, 128, mpad))
         s = np.arange(m)
-        # the exact-score kernel reads the slots interleaved, the FP8 one in order
-        rc = (s // 128) * 128 + _rep_col(s % 128) if p.flags & vc.EXACT_SCORES else s
+        rc = (s // 128) * 128 + _rep_col(s % 128)
         out["rep_delta"] = np.ascontiguousarray(dt[:, :, rc].transpose(0, 2, 1))
     out["m"] = m
     return out

@@ -282,35 +282,39 @@ __global__ __launch_bounds__(128) void k_km_warm(Args a) {
 // MFMA B operand; after the argmin the same registers are added to the LDS bins
 // of the token's cluster, so the planes are read once per iteration.
 constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
-constexpr int BROW = D + 1;   // LDS row of the member-sum bins (ints): lanes adding
-                              // the same channel of different clusters hit
-                              // different banks
-
-__device__ __forceinline__ void add_bins(int* bins, int base, const v4i& h, const v4i& l) {
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int hv = (int)(signed char)((uint32_t)h[wd] >> (8 * b));
-      const int lv = (int)(((uint32_t)l[wd] >> (8 * b)) & 0xffu);
-      atomicAdd(&bins[base + 4 * wd + b], hv * 128 + lv);
-    }
-}
 
 constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measured 13 us
                              // less per Lloyd iteration at N=16544, 48 heads)
-// Shared memory of k_km_assign for C clusters (sized at launch, so that with 32
-// clusters four workgroups fit on a CU instead of three).
-constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 + 4 * BROW + 4); }
+// Member sums: two channels per 64-bit LDS add.  Each half holds u + 16384 (in
+// [8192, 24575]) summed over at most KM_CHUNK = 1024 tokens (< 2^25), so the low
+// half never carries into the high one; the bias is removed with the count.
+constexpr int BROW2 = D / 2 + 1;  // LDS row of the packed bins (8-byte words)
+constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 * BROW2 + 4); }
 
+__device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, const v4i& h, const v4i& l) {
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t hb = (uint32_t)h[wd] ^ 0x80808080u;  // signed hi byte + 128, as unsigned
+    const uint32_t lb = (uint32_t)l[wd];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
+      const uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
+      atomicAdd(&bins[base + 2 * wd + pr], (unsigned long long)ua | ((unsigned long long)ub << 32));
+    }
+  }
+}
+
+// NT = number of 16-centroid tiles (C <= 16 NT).  Centroids beyond C get a norm
+// of 2^62, so their distance never wins and no lane needs a predicate.
+template <int NT>
 __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
   extern __shared__ __align__(16) unsigned char km_smem[];
   const int C = a.C;
-  int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                    // [C][CROW]
-  int8_t* clo = chi + C * CROW;                                        // [C][CROW]
-  long long* cc = reinterpret_cast<long long*>(clo + C * CROW);        // [C]
-  int* bins = reinterpret_cast<int*>(cc + C);                          // [C][BROW]
-  int* cnt = bins + C * BROW;                                          // [C]
+  int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                       // [C][CROW]
+  int8_t* clo = chi + C * CROW;                                           // [C][CROW]
+  unsigned long long* bins = reinterpret_cast<unsigned long long*>(clo + C * CROW);  // [C][BROW2]
+  int* cnt = reinterpret_cast<int*>(bins + C * BROW2);                    // [C]
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
   const int* cf = a.centfix + (size_t)bh * C * D;
@@ -318,18 +322,23 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
     const int u = cf[e];
     chi[(e / D) * CROW + (e % D)] = (int8_t)(u >> 7);
     clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
-    bins[(e / D) * BROW + (e % D)] = 0;
   }
-  if (t < C) {
-    cc[t] = a.kmcc[(size_t)bh * C + t];
-    cnt[t] = 0;
-  }
+  for (int e = t; e < C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
+  if (t < C) cnt[t] = 0;
+  // this lane's centroid norms: centroid 16kt + 4g + v
+  long long ccr[NT][4];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = 16 * kt + 4 * g + v;
+      ccr[kt][v] = k < C ? a.kmcc[(size_t)bh * C + k] : (1ll << 62);
+    }
   __syncthreads();
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
-  const int ntile = (C + 15) / 16;
-  // wave w takes 16-token subtiles w, w+4, ... of the chunk; the operands of the
-  // next subtile are loaded while the current one is processed
+  // wave w takes 16-token subtiles w, w+KM_WAVES, ... of the chunk; the operands
+  // of the next subtile are loaded while the current one is processed
   const int first = chunk * KM_CHUNK;
   auto load_sub = [&](int s, v4i& h0, v4i& h1, v4i& l0, v4i& l1) {
     int jj = first + s * 16 + l16;
@@ -348,9 +357,10 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
     if (sub + KM_WAVES < KM_CHUNK / 16 && first + (sub + KM_WAVES) * 16 < a.N)
       load_sub(sub + KM_WAVES, nh0, nh1, nl0, nl1);
     const int j = first + sub * 16 + l16;
-    long long bestD = 0x7fffffffffffffffll;  // lanes with no valid centroid never win
-    int best = 0x7fffffff;
-    for (int kt = 0; kt < ntile; ++kt) {
+    long long bestD = 0x7fffffffffffffffll;
+    int best = 0;
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) {
       const int kr = 16 * kt + l16;
       const int krow = kr < C ? kr : 0;
       const v4i ah0 = *reinterpret_cast<const v4i*>(chi + krow * CROW + 16 * g);
@@ -366,13 +376,13 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
       LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, LH, 0, 0, 0);
       v4i LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bl0, z, 0, 0, 0);
       LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bl1, LL, 0, 0, 0);
-      // lane (g, token l16) holds centroids 16kt + 4g + v
+      // lane (g, token l16) holds centroids 16kt + 4g + v; ||c||^2 - 2 u.c with
+      // u.c = 2^14 HH + 2^7 (HL + LH) + LL, exact in int64
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
+        const long long Dk = ccr[kt][v] - (long long)HH[v] * 32768 - (long long)(HL[v] + LH[v]) * 256 -
+                             (long long)LL[v] * 2;
         const int k = 16 * kt + 4 * g + v;
-        const long long dot = (long long)HH[v] * 16384 + (long long)(HL[v] + LH[v]) * 128 + LL[v];
-        const long long ck = cc[k < C ? k : 0];
-        const long long Dk = k < C ? ck - 2 * dot : 0x7fffffffffffffffll;
         best = Dk < bestD ? k : best;
         bestD = Dk < bestD ? Dk : bestD;
       }
@@ -389,13 +399,18 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
         a.labels[(size_t)bh * a.N + j] = best;
         atomicAdd(&cnt[best], 1);
       }
-      add_bins(bins, best * BROW + 16 * g, bh0, bl0);
-      add_bins(bins, best * BROW + 64 + 16 * g, bh1, bl1);
+      add_bins2(bins, best * BROW2 + 8 * g, bh0, bl0);
+      add_bins2(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
     }
   }
   __syncthreads();
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
-  for (int e = t; e < C * D; e += 64 * KM_WAVES) part[e] = bins[(e / D) * BROW + (e % D)];
+  for (int e = t; e < C * D; e += 64 * KM_WAVES) {
+    const int c = e / D, ch = e % D;
+    const unsigned long long wv = bins[c * BROW2 + (ch >> 1)];
+    const uint32_t half = (ch & 1) ? (uint32_t)(wv >> 32) : (uint32_t)wv;
+    part[e] = (int)half - 16384 * cnt[c];
+  }
   if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
 }
 
@@ -878,7 +893,16 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
       else
         hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
       for (int it = 0; it < a.T; ++it) {
-        hipLaunchKernelGGL(k_km_assign, dim3(a.nkm, BH), dim3(64 * KM_WAVES), km_smem_bytes(a.C), st, a);
+        const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
+        const size_t sm = km_smem_bytes(a.C);
+        if (a.C <= 16)
+          hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a);
+        else if (a.C <= 32)
+          hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a);
+        else if (a.C <= 48)
+          hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a);
+        else
+          hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a);
         hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
       }
       hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);

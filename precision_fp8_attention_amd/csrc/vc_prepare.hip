@@ -24,8 +24,13 @@ namespace {
 
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float((h & 0xffffu) << 16); }
 
-__device__ __forceinline__ long long fx24(float x) {
-  return (long long)__builtin_rintf(x * 16777216.0f);
+// x rounded to the 2^-24 grid, in units of 2^-24, as a double (exact: an
+// integer-valued float).  Sums of up to 2^7 such values stay below 2^53 for
+// inputs |x| < 2^22, so fp64 adds of them are exact and equal integer sums;
+// gfx950 has no float -> int64 convert, so this costs 4 instructions per value
+// instead of about 15.
+__device__ __forceinline__ double fx24d(float x) {
+  return (double)__builtin_rintf(x * 16777216.0f);
 }
 
 __device__ __forceinline__ float fixed_mean(long long s, long long n) {
@@ -94,28 +99,29 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
   const int j0 = ch * KSUM_CHUNK, j1 = min(j0 + KSUM_CHUNK, a.N);
   const uint16_t* kh = a.k + (size_t)bh * a.N * D;
   const uint16_t* vh = a.v + (size_t)bh * a.N * D;
-  long long s[8];
+  // a thread sums at most KSUM_CHUNK/16 = 32 rows: exact in fp64 (see fx24d)
+  double s[8];
   float vm = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = 0;
+  for (int i = 0; i < 8; ++i) s[i] = 0.0;
   for (int j = j0 + r; j < j1; j += 16) {
     const uint4 u = *reinterpret_cast<const uint4*>(kh + (size_t)j * D + cg * 8);
     const uint4 w = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + cg * 8);
-    s[0] += fx24(bf2f(u.x));
-    s[1] += fx24(bf2f(u.x >> 16));
-    s[2] += fx24(bf2f(u.y));
-    s[3] += fx24(bf2f(u.y >> 16));
-    s[4] += fx24(bf2f(u.z));
-    s[5] += fx24(bf2f(u.z >> 16));
-    s[6] += fx24(bf2f(u.w));
-    s[7] += fx24(bf2f(u.w >> 16));
+    s[0] += fx24d(bf2f(u.x));
+    s[1] += fx24d(bf2f(u.x >> 16));
+    s[2] += fx24d(bf2f(u.y));
+    s[3] += fx24d(bf2f(u.y >> 16));
+    s[4] += fx24d(bf2f(u.z));
+    s[5] += fx24d(bf2f(u.z >> 16));
+    s[6] += fx24d(bf2f(u.w));
+    s[7] += fx24d(bf2f(u.w >> 16));
     vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
                          fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
     vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
                          fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = s[i];
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = (long long)s[i];
   vm = wave_max(vm);
   if ((t & 63) == 0) wm[t >> 6] = vm;
   __syncthreads();
@@ -575,9 +581,9 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
   const uint16_t* vh = a.v + (size_t)bh * a.N * D;
   const int* perm = a.perm + (size_t)bh * a.N;
   float x[8][8];
-  long long s[8];
+  double s[8];  // 8 rows per thread: exact in fp64 (see fx24d)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = 0;
+  for (int e = 0; e < 8; ++e) s[e] = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r0 + 16 * i;
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[i][e] = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
-        s[e] += fx24(x[i][e]);
+        s[e] += fx24d(x[i][e]);
       }
     } else {
 #pragma unroll
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ssum[r0][cg * 8 + e] = s[e];
+  for (int e = 0; e < 8; ++e) ssum[r0][cg * 8 + e] = (long long)s[e];
   __syncthreads();
   if (t < D) {
     long long tot = 0;

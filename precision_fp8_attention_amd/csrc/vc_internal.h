@@ -13,7 +13,7 @@ namespace vc {
 constexpr int D = 128;              // head dimension
 constexpr int BLK = 128;            // quantisation block (tokens)
 constexpr int KSUM_CHUNK = 512;     // tokens per partial K-sum workgroup
-constexpr int KM_CHUNK = 1024;      // tokens per k-means assignment workgroup
+constexpr int KM_CHUNK = 2048;      // tokens per k-means assignment workgroup
 constexpr int MAX_CLUSTERS = 64;    // centroids and bins live in LDS
 constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 

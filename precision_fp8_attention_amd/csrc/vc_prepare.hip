@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
 
 // Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
 // fixed-point value of token idx[k].  The draws do not depend on the swaps, so
-// lane i computes draw i; wave 0 then replays the swaps over a sparse map held
-// one entry per lane.  grid BH, 128 threads.
+// lane i computes draw i and then resolves, on its own, which value the swaps
+// leave at position i.  grid BH, 128 threads.
 // Sum of one int64 per lane over a wave (exact).
 __device__ __forceinline__ long long wave_sum_i64(long long x) {
 #pragma unroll
@@ -220,30 +220,22 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
     jdraw[t] = t + (int)(r % (uint64_t)(a.N - t));
   }
   __syncthreads();
-  if (t < 64) {
-    // sparse map: lanes 0..63 hold keys (positions) k0 and k1 with values v0, v1
-    int k0 = -1, v0 = 0, k1 = -1, v1 = 0, n = 0;
-    for (int i = 0; i < C; ++i) {
-      const int j = jdraw[i];
-      const unsigned long long mi0 = __ballot(k0 == i), mi1 = __ballot(k1 == i);
-      const unsigned long long mj0 = __ballot(k0 == j), mj1 = __ballot(k1 == j);
-      int vi = i, vj = j;
-      if (mi0) vi = __shfl(v0, __ffsll((long long)mi0) - 1, 64);
-      else if (mi1) vi = __shfl(v1, __ffsll((long long)mi1) - 1, 64);
-      if (mj0) vj = __shfl(v0, __ffsll((long long)mj0) - 1, 64);
-      else if (mj1) vj = __shfl(v1, __ffsll((long long)mj1) - 1, 64);
-      // map[i] = vj, map[j] = vi (insert when absent)
-      const int li = mi0 ? __ffsll((long long)mi0) - 1 : (mi1 ? 64 + __ffsll((long long)mi1) - 1 : n);
-      if (!(mi0 | mi1)) ++n;
-      const int lj = (j == i) ? li
-                     : (mj0 ? __ffsll((long long)mj0) - 1 : (mj1 ? 64 + __ffsll((long long)mj1) - 1 : n));
-      if (j != i && !(mj0 | mj1)) ++n;
-      if (li < 64) { if (t == li) { k0 = i; v0 = vj; } } else if (t == li - 64) { k1 = i; v1 = vj; }
-      if (j != i) {
-        if (lj < 64) { if (t == lj) { k0 = j; v0 = vi; } } else if (t == lj - 64) { k1 = j; v1 = vi; }
-      }
-      if (t == 0) idx[i] = vj;
+  if (t < C) {
+    // Position t is final after step t (later steps only touch positions >= their
+    // own index), so idx[t] is the value at position jdraw[t] just before step t.
+    // A position q holds q until the last earlier step k with jdraw[k] == q,
+    // after which it holds what position k held just before step k; follow that
+    // chain (each link lowers the step index) to an untouched position.
+    int pos = jdraw[t], step = t;
+    for (;;) {
+      int last = -1;
+      for (int k = 0; k < step; ++k)
+        if (jdraw[k] == pos) last = k;
+      if (last < 0) break;
+      pos = last;
+      step = last;
     }
+    idx[t] = pos;
   }
   __syncthreads();
   const int sh = a.kmsh[bh];
@@ -292,9 +284,10 @@ constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
 constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measured 13 us
                              // less per Lloyd iteration at N=16544, 48 heads)
 // Member sums: two channels per 64-bit LDS add.  Each half holds u + 16384 (in
-// [8192, 24575]) summed over at most KM_CHUNK = 1024 tokens (< 2^25), so the low
+// [8192, 24575]) summed over at most KM_CHUNK = 2048 tokens (< 2^26), so the low
 // half never carries into the high one; the bias is removed with the count.
 constexpr int BROW2 = D / 2 + 1;  // LDS row of the packed bins (8-byte words)
+static_assert(KM_CHUNK * 24575ll < (1ll << 32), "packed member sums would carry");
 constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 * BROW2 + 4); }
 
 __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, const v4i& h, const v4i& l) {

@@ -678,46 +678,35 @@ __global__ __launch_bounds__(128) void k_v_mup(Args a) {
 }
 
 // Residual codes (channel-major, interleaved) and the repair criterion.
-// grid (nblk, BH), 256 threads.  The block's rows are staged in LDS with
-// coalesced loads (row stride 65 words: a thread per row reads conflict-free);
-// then one thread per row walks its channels in order, because the criterion is
-// an fp32 fma chain over channels 0..127.
-constexpr int VROW = D / 2 + 1;  // words per staged row (2 bf16 per word + pad)
-
-__global__ __launch_bounds__(256) void k_v_quant(Args a) {
+// One thread per row: the thread loads its own row (256 bytes) into registers
+// and walks its channels in order (the criterion is an fp32 fma chain over
+// channels 0..127).  LDS holds only the transposed code tile, so many
+// workgroups share a CU.  grid (nblk, BH), 128 threads.
+__global__ __launch_bounds__(128) void k_v_quant(Args a) {
   __shared__ float smu[D], sinv[D], ssv[D];
-  __shared__ uint32_t rows[BLK * VROW];
   __shared__ __align__(16) uint8_t tile[D * BLK];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
-  if (t < D) {
-    smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
-    sinv[t] = a.inv[(size_t)bh * D + t];
-    ssv[t] = a.sv[(size_t)bh * D + t];
-  }
-  {
-    const int cg = t & 15, r0 = t >> 4;
+  smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
+  sinv[t] = a.inv[(size_t)bh * D + t];
+  ssv[t] = a.sv[(size_t)bh * D + t];
+  const int r = t, col = v_col(r), p = p0 + r;
+  uint4 row[16];
+  if (r < n) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = r0 + 16 * i;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (r < n) u = *reinterpret_cast<const uint4*>(
-          a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p0 + r]) * D + cg * 8);
-      uint32_t* dst = rows + r * VROW + cg * 4;
-      dst[0] = u.x;
-      dst[1] = u.y;
-      dst[2] = u.z;
-      dst[3] = u.w;
-    }
+    for (int i = 0; i < 16; ++i) row[i] = src[i];
   }
   __syncthreads();
-  if (t < BLK) {
-    const int r = t, col = v_col(r), p = p0 + r;
-    if (r < n) {
-      float e = 0.0f;
-      for (int wd = 0; wd < D / 2; ++wd) {
-        const uint32_t h = rows[r * VROW + wd];
-        const int c = 2 * wd;
+  if (r < n) {
+    float e = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t hw[4] = {row[i].x, row[i].y, row[i].z, row[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h = hw[q];
+        const int c = 8 * i + 2 * q;
         const float x0 = (bf2f(h) - smu[c]) * sinv[c];
         const float x1 = (bf2f(h >> 16) - smu[c + 1]) * sinv[c + 1];
         const uint32_t cc = e4m3x2(x0, x1);
@@ -728,20 +717,17 @@ __global__ __launch_bounds__(256) void k_v_quant(Args a) {
         const float t1 = ssv[c + 1] * (x1 - e4m3_val(cc >> 8));
         e = __builtin_fmaf(t1, t1, e);
       }
-      a.err[(size_t)bh * a.N + p] = e;
-    } else {
-      for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
     }
+    a.err[(size_t)bh * a.N + p] = e;
+  } else {
+    for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
   }
   __syncthreads();
-  // 128 channel rows x 128 bytes: thread t stores half a row
-  {
-    const int c = t >> 1, hf = t & 1;
-    uint8_t* dst = a.v8t + ((size_t)bh * D + c) * a.Npad + (size_t)blk * BLK + hf * 64;
+  // 128 channel rows x 128 bytes: thread t stores row t
+  uint8_t* dst = a.v8t + ((size_t)bh * D + t) * a.Npad + (size_t)blk * BLK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + c * BLK + hf * 64 + 16 * i);
-  }
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + t * BLK + 16 * i);
 }
 
 // ---------------------------------------------------------------------------
@@ -751,7 +737,7 @@ __global__ __launch_bounds__(256) void k_v_quant(Args a) {
 __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   __shared__ int hist[256];
   __shared__ unsigned long long s_prefix, s_mask;
-  __shared__ int s_kth, s_kth_next, s_base;
+  __shared__ int s_kth, s_kth_next, s_base, s_hsel;
   __shared__ int wtot[16];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const float* err = a.err + (size_t)bh * a.N;
@@ -791,6 +777,7 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
       const int kth = s_kth;
       if (h > 0 && cum < kth && kth <= cum + h) {
         s_kth_next = kth - cum;
+        s_hsel = h;
         s_prefix = pre | ((unsigned long long)t << shift);
         s_mask = msk | (255ull << shift);
       }
@@ -798,8 +785,16 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
     __syncthreads();
     if (t == 0) s_kth = s_kth_next;
     __syncthreads();
+    // if every key with the digits fixed so far is taken, the lower digits
+    // cannot change the selected set: any threshold with this prefix works
+    if (s_hsel == s_kth) {
+      if (t == 0) s_prefix |= (1ull << shift) - 1ull;
+      __syncthreads();
+      break;
+    }
   }
-  const unsigned long long thr = s_prefix;  // the m-th smallest key
+  const unsigned long long thr = s_prefix;  // the m-th smallest key, or a key
+                                            // above it and below the next one
   int* out = a.rep_pos + (size_t)bh * a.mpad;
   if (t == 0) s_base = 0;
   __syncthreads();
@@ -915,7 +910,7 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
-  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
   if (a.m > 0) {
     hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
     hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);

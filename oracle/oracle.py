@@ -28,6 +28,7 @@ REPAIR = 2
 PERMUTE_Q = 4
 EXACT_SCORES = 16
 WARM_START = 32
+V4 = 64
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 
@@ -52,7 +53,7 @@ class Params(C.Structure):
 class _Prep(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "labels", "perm", "iperm", "centroids", "kbar", "q8", "k8", "sq", "sk", "mu", "mup",
-        "v8", "sv", "inv", "err", "rep_pos", "rep_delta")] + [("mcap", C.c_int32)]
+        "v8", "sv", "inv", "err", "rep_pos", "rep_delta", "vexp")] + [("mcap", C.c_int32)]
 
 
 _lib = None
@@ -71,6 +72,9 @@ def lib():
         L.oc_e4m3_encode_array.argtypes = [vp, vp, i64]
         L.oc_expcast_array.argtypes = [vp, C.c_float, C.c_float, vp, i64]
         L.oc_splitmix64_array.argtypes = [C.c_uint64, vp, i64]
+        L.oc_e2m1_decode_array.argtypes = [vp, vp, i64]
+        L.oc_e2m1_encode_array.argtypes = [vp, vp, i64]
+        L.oc_mx_exponent_array.argtypes = [vp, vp, i64]
         L.oc_score_array.argtypes = [vp, vp, i64, i32, i32, vp]
         L.oc_kmeans_init_indices.argtypes = [C.c_uint64, i64, i32, i32, vp]
         L.oc_kmeans_shift.argtypes = [vp, i64]
@@ -119,7 +123,7 @@ def prepare(P: Params, q, k, v, heads=None, init_centroids=None) -> dict:
         mup=np.zeros((nh, nblk, d), np.float32), v8=np.zeros((nh, npad, d), np.uint8),
         sv=np.zeros((nh, d), np.float32), inv=np.zeros((nh, d), np.float32),
         err=np.zeros((nh, N), np.float32), rep_pos=np.zeros((nh, mcap), np.int32),
-        rep_delta=np.zeros((nh, mcap, d), np.uint16))
+        rep_delta=np.zeros((nh, mcap, d), np.uint16), vexp=np.zeros((nh, nblk, 4, d), np.int8))
     if P.flags & WARM_START:
         if init_centroids is None:
             raise ValueError("WARM_START needs init_centroids")
@@ -176,6 +180,33 @@ def e4m3_encode(x) -> np.ndarray:
     out = np.zeros(xf.shape, np.uint8)
     lib().oc_e4m3_encode_array(_ptr(xf), _ptr(out), xf.size)
     return out
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.zeros(c.shape, np.float64)
+    lib().oc_e2m1_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def e2m1_encode(x) -> np.ndarray:
+    xf = np.ascontiguousarray(x, np.float32)
+    out = np.zeros(xf.shape, np.uint8)
+    lib().oc_e2m1_encode_array(_ptr(xf), _ptr(out), xf.size)
+    return out
+
+
+def mx_exponent(a) -> np.ndarray:
+    af = np.ascontiguousarray(a, np.float32)
+    out = np.zeros(af.shape, np.int32)
+    lib().oc_mx_exponent_array(_ptr(af), _ptr(out), af.size)
+    return out
+
+
+def v4_group(k):
+    """32-key group of key k (0..127) of a block for the 4-bit residual."""
+    k = np.asarray(k)
+    return 2 * (k >> 6) + ((k >> 3) & 1)
 
 
 def expcast(s, alpha: float, beta: float) -> np.ndarray:

@@ -61,7 +61,15 @@
  *   - repair: m = ceil(rho*N) tokens per (batch, head) with the largest
  *     sum_c (sV_c * delta_c)^2, ties to the lower position; their residual error
  *     delta (in V code units, stored as bf16) is added with codes formed from the
- *     final row maximum; the row sum is left unchanged.
+ *     final row maximum; the row sum is left unchanged. *
+ *   - 4-bit residual (OC_V4): the pages also run V-Smooth with the residual in
+ *     NVFP4 [P5 "V-Smooth", Demean]; here in the gfx950-native MX form.  Per
+ *     128-position block, channel and 32-key group (key k of the block is in
+ *     group 2*(k/64) + (k mod 16)/8), X = floor(log2 max|r|) - 2 and the code is
+ *     E2M1(r * 2^-X), nearest with ties to the even code, saturating at 6.  There
+ *     is no per-channel scale (sV = 1, mu' = mu), the repair error and the
+ *     stored repair residuals are in real units, and P stays the ExpCast FP8
+ *     code (the pages apply ExpCast only at 8 bits, so P's format is ours).
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma -shared -fPIC (fp32 operations
  * must not be contracted; fmaf is always an explicit single-rounding fma).
@@ -76,6 +84,7 @@
 #define OC_PERMUTE_Q 4u
 #define OC_EXACT_SCORES 16u
 #define OC_WARM_START 32u
+#define OC_V4 64u
 
 typedef struct {
   int32_t B, H, N, d;     /* d must be 128 */
@@ -105,6 +114,7 @@ typedef struct {
   float *err;        /* [nh][N]  repair criterion per position                   */
   int32_t *rep_pos;  /* [nh][mcap] repaired positions, ascending                 */
   uint16_t *rep_delta; /* [nh][mcap][d] bf16 residual error, V code units        */
+  int8_t *vexp;      /* [nh][nblk][4][d] MX exponents of the 4-bit residual (OC_V4) */
   int32_t mcap;      /* capacity of the repair arrays (>= m)                     */
 } oc_prep;
 
@@ -169,6 +179,45 @@ uint8_t oc_e4m3_encode(float xf) {
 }
 
 /* ExpCast-FP8 [P5 "ExpCast-FP8"]: one fp32 fma from the raw score to the byte. */
+/* OCP FP4 E2M1 (OCP Microscaling Formats v1.0): magnitude codes 0..7 are 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6; bit 3 is the sign.  Used by the 4-bit V residual (OC_V4),
+ * the NVFP4 variant of V-Smooth [P5 "V-Smooth", Demean] in the gfx950-native MX
+ * form. */
+double oc_e2m1_decode(uint8_t c) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double v = mag[c & 7];
+  return (c & 8) ? -v : v;
+}
+
+/* Nearest E2M1 value, ties to the even code, saturating at 6; a result of
+ * magnitude 0 is the code 0 (no negative zero). */
+uint8_t oc_e2m1_encode(float y) {
+  float a = fabsf(y);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double dc = fabs((double)a - oc_e2m1_decode((uint8_t)c));
+    double db = fabs((double)a - oc_e2m1_decode((uint8_t)best));
+    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+  }
+  if (best == 0) return 0;
+  return (uint8_t)(best | (y < 0.0f ? 8 : 0));
+}
+
+/* MX shared exponent of a 32-value group whose largest magnitude is a: the X
+ * with a * 2^-X in [4, 8), i.e. floor(log2 a) - 2 (E2M1's largest binade starts
+ * at 4); -127 (the smallest E8M0 scale) when the group is all zero. */
+int oc_mx_exponent(float a) {
+  if (!(a > 0.0f)) return -127;
+  int e;
+  frexpf(a, &e); /* a = m 2^e with m in [0.5, 1): floor(log2 a) = e - 1 */
+  int x = e - 3;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+/* 32-key groups of a 128-key block for the 4-bit residual: key k (0..127) is in
+ * group 2 * (k / 64) + ((k mod 16) / 8). */
+int oc_v4_group(int k) { return 2 * (k >> 6) + ((k >> 3) & 1); }
+
 uint8_t oc_expcast(float s_raw, float alpha, float beta) {
   float y = rintf(fmaf(s_raw, alpha, beta));
   if (!(y > 0.0f)) return 0; /* also maps -inf (masked keys) to 0 */
@@ -316,11 +365,22 @@ static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d
 /* Prepare: one (batch, head)                                                 */
 /* ------------------------------------------------------------------------- */
 
+/* Value of residual code `code` of position p, channel c, in the units of the
+ * residual x: the E4M3 value (V code units), or with the 4-bit residual the E2M1
+ * value times its group's power of two (real units; exact in fp32). */
+static float vq_value(const oc_prep *o, int slot, int nblk, int d, int v4, int p, int c, uint8_t code) {
+  if (!v4) return (float)oc_e4m3_decode(code);
+  int b = p / 128;
+  int X = o->vexp[(((size_t)slot * nblk + b) * 4 + oc_v4_group(p - b * 128)) * d + c];
+  return ldexpf((float)oc_e2m1_decode(code), X);
+}
+
 static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, const uint16_t *kh,
                          const uint16_t *vh, oc_prep *o, int slot) {
   const int N = P->N, d = P->d, C = P->C;
   const int nblk = (N + 127) / 128, Npad = nblk * 128;
   const int vs = (P->flags & OC_VSMOOTH) != 0;
+  const int v4 = (P->flags & OC_V4) != 0;
   const int m = repair_count(P);
   float *q = (float *)malloc(sizeof(float) * (size_t)N * d);
   float *k = (float *)malloc(sizeof(float) * (size_t)N * d);
@@ -414,22 +474,50 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
       }
     }
   }
-  for (int c = 0; c < d; ++c) {
-    float a = 0.0f;
-    for (int p = 0; p < N; ++p) {
-      float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
-      if (fabsf(r) > a) a = fabsf(r);
-    }
-    scale_from_amax(a, &sv[c], &inv[c]);
-  }
   memset(v8, 0, (size_t)Npad * d);
-  for (int p = 0; p < N; ++p)
+  if (v4) {
+    /* 4-bit residual [P5 "V-Smooth", Demean: NVFP4 at 4 bits], as MXFP4: one
+     * power-of-two scale per 32-key group of a block and channel, E2M1 codes of
+     * the residual in real units; no per-channel scale (sV = 1). */
+    int8_t *vexp = o->vexp + (size_t)slot * nblk * 4 * d;
     for (int c = 0; c < d; ++c) {
-      float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
-      float xx = r * inv[c];
-      x[(size_t)p * d + c] = xx;
-      v8[(size_t)p * d + c] = oc_e4m3_encode(xx);
+      sv[c] = 1.0f;
+      inv[c] = 1.0f;
     }
+    for (int b = 0; b < nblk; ++b)
+      for (int c = 0; c < d; ++c) {
+        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int p = b * 128; p < b * 128 + 128 && p < N; ++p) {
+          float r = v[(size_t)perm[p] * d + c] - mu[(size_t)b * d + c];
+          int g = oc_v4_group(p - b * 128);
+          if (fabsf(r) > a[g]) a[g] = fabsf(r);
+        }
+        for (int g = 0; g < 4; ++g) vexp[((size_t)b * 4 + g) * d + c] = (int8_t)oc_mx_exponent(a[g]);
+      }
+    for (int p = 0; p < N; ++p)
+      for (int c = 0; c < d; ++c) {
+        int b = p / 128, X = vexp[((size_t)b * 4 + oc_v4_group(p - b * 128)) * d + c];
+        float r = v[(size_t)perm[p] * d + c] - mu[(size_t)b * d + c];
+        x[(size_t)p * d + c] = r;
+        v8[(size_t)p * d + c] = oc_e2m1_encode(ldexpf(r, -X));
+      }
+  } else {
+    for (int c = 0; c < d; ++c) {
+      float a = 0.0f;
+      for (int p = 0; p < N; ++p) {
+        float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
+        if (fabsf(r) > a) a = fabsf(r);
+      }
+      scale_from_amax(a, &sv[c], &inv[c]);
+    }
+    for (int p = 0; p < N; ++p)
+      for (int c = 0; c < d; ++c) {
+        float r = v[(size_t)perm[p] * d + c] - mu[(size_t)(p / 128) * d + c];
+        float xx = r * inv[c];
+        x[(size_t)p * d + c] = xx;
+        v8[(size_t)p * d + c] = oc_e4m3_encode(xx);
+      }
+  }
   for (int b = 0; b < nblk; ++b)
     for (int c = 0; c < d; ++c) mup[(size_t)b * d + c] = mu[(size_t)b * d + c] * inv[c];
 
@@ -438,7 +526,7 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
   for (int p = 0; p < N; ++p) {
     float e = 0.0f;
     for (int c = 0; c < d; ++c) {
-      float dl = x[(size_t)p * d + c] - (float)oc_e4m3_decode(v8[(size_t)p * d + c]);
+      float dl = x[(size_t)p * d + c] - vq_value(o, slot, nblk, d, v4, p, c, v8[(size_t)p * d + c]);
       float t = sv[c] * dl;
       e = fmaf(t, t, e);
     }
@@ -463,7 +551,7 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
       if (taken[p]) {
         sel[n] = p;
         for (int c = 0; c < d; ++c) {
-          float de = x[(size_t)p * d + c] - (float)oc_e4m3_decode(v8[(size_t)p * d + c]);
+          float de = x[(size_t)p * d + c] - vq_value(o, slot, nblk, d, v4, p, c, v8[(size_t)p * d + c]);
           dl[(size_t)n * d + c] = f32_to_bf16(de);
         }
         ++n;
@@ -569,6 +657,7 @@ static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t 
   const float *sv = o->sv + (size_t)slot * d;
   const int p = (P->flags & OC_PERMUTE_Q) ? o->iperm[(size_t)slot * N + row] : row;
   const int a = p / 128;
+  const int v4 = (P->flags & OC_V4) != 0;
   const float c0 = code_gain(P);
   const float bias = (float)(56 + 8 * P->expcast_k);
   float M = -INFINITY;
@@ -598,7 +687,11 @@ static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t 
     ell = ell * r + lb;
     for (int c = 0; c < d; ++c) {
       double pv = 0.0;
-      for (int j = j0; j < j1; ++j) pv += DEC[code[j - j0]] * DEC[v8[(size_t)j * d + c]];
+      for (int j = j0; j < j1; ++j) {
+        double vv = v4 ? (double)vq_value(o, slot, nblk, d, 1, j, c, v8[(size_t)j * d + c])
+                       : DEC[v8[(size_t)j * d + c]];
+        pv += DEC[code[j - j0]] * vv;
+      }
       acc[c] = acc[c] * r + lb * (double)mup[(size_t)b * d + c] + pv;
     }
     M = Mn;
@@ -689,4 +782,14 @@ void oc_score_array(const uint8_t *a, const uint8_t *b, int64_t n, int32_t d, in
 }
 void oc_splitmix64_array(uint64_t state, uint64_t *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = sm64_next(&state);
+}
+
+void oc_e2m1_decode_array(const uint8_t *c, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_e2m1_decode(c[i]);
+}
+void oc_e2m1_encode_array(const float *x, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_e2m1_encode(x[i]);
+}
+void oc_mx_exponent_array(const float *a, int32_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oc_mx_exponent(a[i]);
 }

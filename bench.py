@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true",
                     help="time only vc_attn_forward launches (profiling runs)")
+    ap.add_argument("--v4", action="store_true",
+                    help="with --forward-only: the 4-bit value residual variant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -175,12 +177,16 @@ def main():
         vc.forward(p, ws, o)
 
     if args.forward_only:
+        if args.v4:
+            p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                                  flags=vc.DEFAULT_FLAGS | vc.V4)
+            ws = vc.alloc_workspace(p, dev)
         step()
         for _ in range(args.warmup):
             vc.forward(p, ws, o)
         torch.cuda.synchronize()
         ms = _events_ms(lambda: vc.forward(p, ws, o), args.steps)
-        print(json.dumps({"forward_ms": ms, "launches": args.steps + args.warmup + 1}))
+        print(json.dumps({"forward_ms": ms, "launches": args.steps + args.warmup + 1, "v4": args.v4}))
         return
 
     for _ in range(args.warmup):
@@ -201,6 +207,28 @@ def main():
     torch.cuda.synchronize()
 
     sched = denoise_schedule(p, qd, kd, vd, ws, o, flops)
+
+    # the 4-bit value residual (E2M1 + one power of two per 32-key group) on the
+    # same workload, in its own workspace
+    p4 = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                           flags=vc.DEFAULT_FLAGS | vc.V4)
+    ws4 = vc.alloc_workspace(p4, dev)
+    o4 = torch.empty_like(qd)
+
+    def step4():
+        vc.prepare(p4, qd, kd, vd, ws4)
+        vc.forward(p4, ws4, o4)
+
+    for _ in range(max(args.warmup, 1)):
+        step4()
+    ms4_step = _events_ms(step4, max(args.steps // 2, 5))
+    ms4_fwd = _events_ms(lambda: vc.forward(p4, ws4, o4), max(args.steps, 10))
+    ms4_prep = _events_ms(lambda: vc.prepare(p4, qd, kd, vd, ws4), max(args.steps // 2, 5))
+    del ws4, o4
+    v4 = {"flags": "VSMOOTH|REPAIR|PERMUTE_Q|V4", "ms_per_step": round(ms4_step, 4),
+          "tflops": round(flops / (ms4_step * 1e-3) / 1e12, 3), "forward_ms": round(ms4_fwd, 4),
+          "forward_tflops": round(flops / (ms4_fwd * 1e-3) / 1e12, 3), "prepare_ms": round(ms4_prep, 4)}
+
     vc.prepare(p, qd, kd, vd, ws)
     vc.forward(p, ws, o)
     torch.cuda.synchronize()
@@ -231,6 +259,7 @@ def main():
         "prepare_reuse_clusters_ms": round(ms_reuse, 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "denoise_schedule": sched,
+        "v4_residual": v4,
         "roofline": {"bound": "mfma", "kernel": "k_fwd", "achieved": round(fwd_tflops, 3),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 5),

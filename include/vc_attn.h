@@ -80,11 +80,23 @@ enum {
                             VC_VSMOOTH, excludes VC_REUSE_CLUSTERS; without
                             clusters of this shape prepare returns
                             VC_ERR_NOT_PREPARED */
-  VC_EXACT_SCORES = 16u  /* QK^T as the exact dot product of the E4M3 codes (bf16
+  VC_EXACT_SCORES = 16u, /* QK^T as the exact dot product of the E4M3 codes (bf16
                             MFMA, twice the matrix-core time) instead of the FP8
                             MFMA, whose accumulation cuts each product 13 bits below
                             the largest exponent of its 8-channel group; set the
                             same flag on prepare and forward */
+  VC_V4 = 64u            /* 4-bit value residual: the article's V-Smooth section
+                            offers NVFP4 instead of per-channel E4M3 for the demeaned
+                            residual; here it takes the OCP MX form gfx950's scaled
+                            MFMA reads.  Each 128-key block splits into four 32-key
+                            groups (key k in group 2*(k/64) + (k%16)/8); every
+                            (block, group, channel) gets the power of two 2^X with
+                            X = floor(log2 max|r|) - 2 (-127 for an all-zero group)
+                            and the residual r = V - mu is coded in E2M1 (round to
+                            nearest, ties to the even code, saturating at 6, no
+                            negative zero).  No per-channel scale (sv = inv = 1),
+                            repair deltas in real units, P stays ExpCast E4M3.  Set
+                            the same flag on prepare and forward */
 };
 
 typedef struct {
@@ -132,12 +144,24 @@ typedef struct {
   size_t sv;         /* f32 [BH][128] per-channel V residual scale               */
   size_t inv;        /* f32 [BH][128] its inverse                                */
   size_t v8t;        /* u8  [BH][128][Npad] residual codes, channel-major; inside
-                        each 128-key block key 16t+4g+v sits at column 32g+4t+v  */
+                        each 128-key block key 16t+4g+v sits at column 32g+4t+v.
+                        Not allocated (0 bytes) with VC_V4                       */
   size_t err;        /* f32 [BH][N] repair criterion per position                */
   size_t rep_pos;    /* i32 [BH][mpad] repaired positions ascending, padded with -1 */
   size_t rep_dt;     /* bf16 [BH][128][mpad] residual error of the repaired tokens
                         in V code units, channel-major; inside each 128-slot group
-                        slot 32u+16t'+4g+v sits at column 32u+8g+4t'+v           */
+                        slot 32u+16t'+4g+v sits at column 32u+8g+4t'+v; with
+                        VC_V4 in real units                                      */
+  size_t v4t;        /* VC_V4 only (else 0 bytes): u8 [BH][nblk][128][64] E2M1
+                        residual codes, one 8 KB tile per block, channel-major,
+                        two codes per byte.  Key k of the block (group
+                        G = 2(k/64) + (k/8)%2) sits in byte
+                        16G + 8((k/4)%2) + 4((k/32)%2) + 2((k/16)%2) + (k/2)%2,
+                        low nibble for even k                                    */
+  size_t v4s;        /* VC_V4 only (else 0 bytes): u8 [BH*nblk + 1][4][16][8]
+                        E8M0 exponents X + 127: record [(b*H+h)*nblk + block]
+                        holds group G, channel 16j + i at byte [G][i][j]; the
+                        last record is padding                                   */
 } vc_attn_ws_layout;
 
 /* Fill *p with the defaults: d = block = 128, C = 16, T = 10, k = 8, seed 0,

@@ -109,6 +109,11 @@ def prepare(P: Params, q, k, v, heads=None, init_centroids=None) -> dict:
     (fp32 [nheads, C, 128]) are the starting centroids when P has WARM_START."""
     B, H, N, d = P.B, P.H, P.N, P.d
     heads = np.arange(B * H, dtype=np.int32) if heads is None else np.asarray(heads, np.int32)
+    if heads.ndim != 1 or np.any(heads < 0) or np.any(heads >= B * H):
+        raise ValueError(f"heads must be global head indices in [0, {B * H})")
+    for t in (q, k, v):
+        if tuple(np.shape(t)) != (B, H, N, d):
+            raise ValueError(f"inputs must have shape {(B, H, N, d)}, got {np.shape(t)}")
     nh = len(heads)
     nblk = (N + 127) // 128
     npad = nblk * 128

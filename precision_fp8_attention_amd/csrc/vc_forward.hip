@@ -39,9 +39,17 @@
 // MFMA group adds sum_b l_b * mu'_b to the accumulator: the restore costs no
 // per-element VALU work and no second pass over the keys.
 //
+// 4-bit residual (VC_V4).  V^T is E2M1 with one E8M0 power of two per channel
+// and 32-key group, and PV runs on the same instruction in its scaled form: A
+// is the FP4 tile (16 bytes per lane), B the unchanged ExpCast bytes, and each
+// lane's scale register carries the exponents of its channel for four channel
+// tiles (op_sel picks the byte).  Prepare orders each block's codes so that the
+// FP4 operand's K positions meet the lanes' key interleave, so P again never
+// touches LDS; the restore and the epilogue are unchanged (sV = 1).
+//
 // K tiles (E4M3 codes, 16 KB; bf16 codes, 32 KB, for exact scores) and V tiles
-// (E4M3, 16 KB) are double-buffered in LDS and filled by direct global->LDS
-// loads while the previous block runs.
+// (E4M3, 16 KB; E2M1, 8 KB + 512 B of exponents) are staged in LDS and filled
+// by direct global->LDS loads while earlier blocks run.
 #include "vc_internal.h"
 
 namespace vc {
@@ -55,6 +63,18 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
   // unscaled FP8 (E4M3) x FP8 (E4M3) -> fp32, 16x16x128
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// E2M1 (FP4) A x E4M3 B -> fp32, 16x16x128, A scaled by 2^(s - 127) with s the
+// byte `sel` of the lane's scale register (one E8M0 exponent per lane, i.e. per
+// row and 32-wide K group of A); B unscaled (127).  Only a[0..3] are read.
+__device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, int scale, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale, 0, 127);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 1, scale, 0, 127);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 2, scale, 0, 127);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 3, scale, 0, 127);
+  }
 }
 
 __device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
@@ -84,6 +104,11 @@ __device__ __forceinline__ v8i lds_row32(const uint8_t* tile, int row, int g) {
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
   return r;
 }
+
+// Chunk swizzle of the 64-byte rows of a 4-bit value tile: lane (g, i) reads
+// chunk g of row 16ct + i; XOR-ing bit 1 of the chunk with bit 2 of the row puts
+// the 16 lanes of every ds_read_b128 pass on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int v4_swz(int row) { return ((row >> 2) & 1) << 1; }
 
 // 8 bf16 (16 bytes) of row `row` of a 128x128 bf16 tile: K positions
 // 32kc+8g..32kc+8g+7, i.e. 16-byte chunk 4kc+g, XOR-swizzled by row%16.
@@ -256,14 +281,17 @@ template <bool EXACT> struct QOp;
 template <> struct QOp<true> { v8bf v[2][4]; };
 template <> struct QOp<false> { v8i v[2]; };
 
-template <bool EXACT>
+template <bool EXACT, bool V4>
 __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
   // LDS stages: FP8 mode holds four key blocks (two computed per barrier while
   // the next two land), exact-score mode two (its bf16 K tiles are twice as big)
   constexpr int NST = EXACT ? 2 : 4;
+  constexpr int VTILE = V4 ? V4_TILE : D * BLK;              // V^T tile bytes
+  constexpr int SREC = V4 ? 1024 : 16;                        // E8M0 exponents (V4)
   __shared__ __align__(1024) uint8_t ksm[NST][BLK * KROW];   // [stage] K rows
-  __shared__ __align__(1024) uint8_t vsm[NST][D * BLK];      // [stage] V^T codes
+  __shared__ __align__(1024) uint8_t vsm[NST][VTILE];        // [stage] V^T codes
+  __shared__ __align__(1024) uint8_t ssm[NST][SREC];         // [stage] V exponents
   __shared__ float alpha_s[2][BLK];
 
   // block scales are read-only here: constant address space -> scalar loads
@@ -310,11 +338,21 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
         dma16(kg + ((size_t)kb * BLK + row) * D + cc * 16, kd + r * 1024);
       }
     }
+    if constexpr (V4) {
+      // one contiguous 8 KB tile: wave w lands rows 16w..16w+15; wave 0 also the
+      // block's 512 exponent bytes (its 1 KB copy runs into the next record,
+      // which the layout pads at the end)
+      const uint8_t* vt = a.v4t + ((size_t)bh * a.nblk + kb) * V4_TILE;
+      const int row = 16 * w + (lane >> 2), cc = (lane & 3) ^ v4_swz(row);
+      dma16(vt + row * (BLK / 2) + cc * 16, vd + w * 1024);
+      if (w == 0) dma16(a.v4s + ((size_t)bh * a.nblk + kb) * V4_SREC + 16 * lane, ssm[kb % NST]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * i + w;
-      const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
-      dma16(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024);
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + w;
+        const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
+        dma16(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024);
+      }
     }
   };
 
@@ -418,11 +456,28 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
     for (int i = 0; i < 8; ++i) onesop[i] = o;
     rs[0].L = mfma_f8(onesop, pop[0], rs[0].L);
     rs[1].L = mfma_f8(onesop, pop[1], rs[1].L);
+    if constexpr (V4) {
+      // lane (g, i) holds the E8M0 exponents of channel 16ct + i, group g for
+      // ct = 0..7: byte ct&3 of dword ct/4
+      const uint2 sc = *reinterpret_cast<const uint2*>(ssm[kb % NST] + 8 * lane);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const v8i vop = lds_row32(Vs, 16 * ct + l16, g);
-      rs[0].acc[ct] = mfma_f8(vop, pop[0], rs[0].acc[ct]);
-      rs[1].acc[ct] = mfma_f8(vop, pop[1], rs[1].acc[ct]);
+      for (int ct = 0; ct < 8; ++ct) {
+        const int row = 16 * ct + l16;
+        const uint4 c4 = *reinterpret_cast<const uint4*>(Vs + row * (BLK / 2) + ((g ^ v4_swz(row)) << 4));
+        v8i vop;
+        vop[0] = (int)c4.x; vop[1] = (int)c4.y; vop[2] = (int)c4.z; vop[3] = (int)c4.w;
+        vop[4] = 0; vop[5] = 0; vop[6] = 0; vop[7] = 0;
+        const int scl = ct < 4 ? (int)sc.x : (int)sc.y;
+        rs[0].acc[ct] = mfma_fp4(vop, pop[0], rs[0].acc[ct], scl, ct & 3);
+        rs[1].acc[ct] = mfma_fp4(vop, pop[1], rs[1].acc[ct], scl, ct & 3);
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const v8i vop = lds_row32(Vs, 16 * ct + l16, g);
+        rs[0].acc[ct] = mfma_f8(vop, pop[0], rs[0].acc[ct]);
+        rs[1].acc[ct] = mfma_f8(vop, pop[1], rs[1].acc[ct]);
+      }
     }
     if (onesrow == 15 || kb + 1 == a.nblk) {
       const uint16_t* grp = mupt + (size_t)(kb >> 4) * 2 * D * 16;
@@ -572,10 +627,15 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
 
 hipError_t launch_forward(const Args& a, hipStream_t st) {
   const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
-  if (a.flags & VC_EXACT_SCORES)
-    hipLaunchKernelGGL(k_fwd<true>, dim3(tiles), dim3(512), 0, st, a);
+  const bool exact = (a.flags & VC_EXACT_SCORES) != 0, v4 = (a.flags & VC_V4) != 0;
+  if (exact && v4)
+    hipLaunchKernelGGL((k_fwd<true, true>), dim3(tiles), dim3(512), 0, st, a);
+  else if (exact)
+    hipLaunchKernelGGL((k_fwd<true, false>), dim3(tiles), dim3(512), 0, st, a);
+  else if (v4)
+    hipLaunchKernelGGL((k_fwd<false, true>), dim3(tiles), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL(k_fwd<false>, dim3(tiles), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_fwd<false, false>), dim3(tiles), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -15,11 +15,14 @@ constexpr int BLK = 128;            // quantisation block (tokens)
 constexpr int KSUM_CHUNK = 512;     // tokens per partial K-sum workgroup
 constexpr int KM_CHUNK = 2048;      // tokens per k-means assignment workgroup
 constexpr int MAX_CLUSTERS = 64;    // centroids and bins live in LDS
+constexpr int V4_TILE = D * BLK / 2;  // bytes of one block's E2M1 value tile
+constexpr int V4_SREC = 512;        // bytes of one block's E8M0 exponents
 constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 
 // Shape derived from the public parameters.
 struct Shape {
   int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
+  bool v4;  // 4-bit value residual (VC_V4)
 };
 
 // Workspace header (first 256 bytes of the workspace).
@@ -70,6 +73,8 @@ struct Args {
   float* sv;
   float* inv;
   uint8_t* v8t;
+  uint8_t* v4t;  // [BH][nblk][128][64] E2M1 codes (VC_V4)
+  uint8_t* v4s;  // [BH*nblk+1][512] E8M0 group exponents (VC_V4)
   float* err;
   int* rep_pos;
   uint16_t* rep_dt;

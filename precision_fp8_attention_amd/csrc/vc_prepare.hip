@@ -87,6 +87,58 @@ __device__ __forceinline__ int rep_col(int s) {
   return 32 * u + 8 * g + 4 * tp + v;
 }
 
+// E2M1 (OCP FP4) code of y, |y| < 8: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// ties to the even code, saturating at 6; a zero magnitude is code 0 (no
+// negative zero).  Each threshold is a midpoint; which side includes it follows
+// from which neighbour has the even code.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return m == 0u ? 0u : (m | (y < 0.0f ? 8u : 0u));
+}
+
+// Value of E2M1 code c: magnitudes 2..7 are 2^(m/2 - 1) * (1 + (m%2)/2), built
+// as fp32 bits; 1 is the subnormal 0.5.
+__device__ __forceinline__ float e2m1_val(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float mag = m >= 2u ? __uint_as_float(((126u + (m >> 1)) << 23) | ((m & 1u) << 22)) : 0.5f * (float)m;
+  return (c & 8u) ? -mag : mag;
+}
+
+// MX exponent of a group whose largest magnitude is amax: X with amax * 2^-X in
+// [4, 8) (E2M1's top binade), -127 for an all-zero group, clamped to E8M0.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int x = __builtin_amdgcn_frexp_expf(amax) - 3;  // amax = f 2^e, f in [0.5, 1)
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// 32-key group of key r of a block (4-bit residual) and the byte of its code in
+// the block's 64-byte channel row: the order the FP4 operand of the forward's
+// scaled MFMA expects for the lanes' key interleave 16t+4g+v.
+__device__ __forceinline__ int v4_group(int r) { return 2 * (r >> 6) + ((r >> 3) & 1); }
+__device__ __forceinline__ int v4_byte(int r) {
+  return 16 * v4_group(r) + 8 * ((r >> 2) & 1) + 4 * ((r >> 5) & 1) + 2 * ((r >> 4) & 1) + ((r >> 1) & 1);
+}
+
+// Maximum of x >= 0 over the 32 lanes of a wave that share lane bit 3 (one
+// 32-key group when lane = key mod 64): the integer order of non-negative fp32
+// bits is their numeric order.  Mirror within 8 lanes, then lane ^ 1 and ^ 2
+// (DPP), then the lanes 16 and 32 apart (permlane swaps).
+__device__ __forceinline__ float group_max32(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = max(p16[0], p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  u = max(p32[0], p32[1]);
+  return __uint_as_float(u);
+}
+
 // ---------------------------------------------------------------------------
 // K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; the same
 // workgroup records max|V| of the chunk (the k-means fixed-point scale).
@@ -638,6 +690,7 @@ __global__ __launch_bounds__(128) void k_v_scale(Args a) {
                            fmaxf(fmaxf(A[4], A[5]), fmaxf(A[6], A[7])));
   float s, inv;
   scale_from_amax(amax, &s, &inv);
+  if (a.flags & VC_V4) s = inv = 1.0f;  // the 4-bit residual carries its own powers of two
   a.sv[(size_t)bh * D + c] = s;
   a.inv[(size_t)bh * D + c] = inv;
 }
@@ -728,6 +781,60 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + t * BLK + 16 * i);
+}
+
+// 4-bit residual codes (VC_V4), the repair criterion and the group exponents.
+// One thread per row of the block, as k_v_quant.  Key r's group 2(r/64) + (r/8)%2
+// is the wave and lane bit 3, so a group maximum is a reduction over 32 lanes;
+// keys r and r^1 share a code byte and the odd lane hands its nibble to the even
+// one.  The criterion is the fp32 fma chain of (r - value)^2 over channels 0..127
+// (sv = 1).  grid (nblk, BH), 128 threads.
+__global__ __launch_bounds__(128) void k_v_quant4(Args a) {
+  __shared__ float smu[D];
+  __shared__ __align__(16) uint8_t tile[V4_TILE];
+  __shared__ __align__(16) uint8_t sexp[V4_SREC];
+  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, lane = t & 63;
+  const int p0 = blk * BLK, n = min(BLK, a.N - p0);
+  smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
+  const int r = t, p = p0 + r;
+  const bool valid = r < n;
+  const int G = v4_group(r), byte = v4_byte(r);
+  // the row's 16-byte chunks (8 channels each), loaded two chunks ahead of use
+  const uint4* src = reinterpret_cast<const uint4*>(
+      a.v + ((size_t)bh * a.N + (valid ? a.perm[(size_t)bh * a.N + p] : 0)) * D);
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 nxt0 = valid ? src[0] : zero4, nxt1 = valid ? src[1] : zero4;
+  __syncthreads();
+  float e = 0.0f;
+#pragma unroll 1
+  for (int i = 0; i < D / 8; ++i) {
+    const uint4 u = nxt0;
+    nxt0 = nxt1;
+    if (i + 2 < D / 8) nxt1 = valid ? src[i + 2] : zero4;
+    const uint32_t hw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * i + j;
+      // rows past N have residual 0: they raise no maximum and get code 0
+      const float x = valid ? bf2f((j & 1) ? (hw[j >> 1] >> 16) : hw[j >> 1]) - smu[c] : 0.0f;
+      const int X = mx_exponent(group_max32(fabsf(x)));
+      const uint32_t code = e2m1_code(__builtin_ldexpf(x, -X));
+      const float dl = x - __builtin_ldexpf(e2m1_val(code), X);
+      e = __builtin_fmaf(dl, dl, e);
+      const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code, 0xb1, 0xf, 0xf, false);
+      if (!(r & 1)) tile[c * (BLK / 2) + byte] = (uint8_t)(code | (odd << 4));
+      if ((lane & ~8) == 0) sexp[(16 * G + (c & 15)) * 8 + (c >> 4)] = (uint8_t)(X + 127);
+    }
+  }
+  if (valid) a.err[(size_t)bh * a.N + p] = e;
+  __syncthreads();
+  uint8_t* dt = a.v4t + ((size_t)bh * a.nblk + blk) * V4_TILE;
+#pragma unroll
+  for (int i = 0; i < V4_TILE / (16 * 128); ++i)
+    *reinterpret_cast<uint4*>(dt + 16 * (t + 128 * i)) = *reinterpret_cast<const uint4*>(tile + 16 * (t + 128 * i));
+  if (t < V4_SREC / 16)
+    *reinterpret_cast<uint4*>(a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC + 16 * t) =
+        *reinterpret_cast<const uint4*>(sexp + 16 * t);
 }
 
 // ---------------------------------------------------------------------------
@@ -825,15 +932,33 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
 }
 
-// Residual error (code units, bf16) of the repaired positions, channel-major
-// with the repair-slot interleave.  grid (mpad/128, BH), 128 threads = slots.
+// Residual error (bf16; V code units, real units with VC_V4) of the repaired
+// positions, channel-major with the repair-slot interleave.  grid (mpad/128, BH), 128 threads = slots.
 __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
   __shared__ __align__(16) uint16_t tile[D * BLK];
   const int grp = blockIdx.x, bh = blockIdx.y, s = threadIdx.x;
   const int gs = grp * BLK + s;
   const int col = rep_col(s);
   const int p = gs < a.m ? a.rep_pos[(size_t)bh * a.mpad + gs] : -1;
-  if (p >= 0) {
+  if (p >= 0 && (a.flags & VC_V4)) {
+    // 4-bit residual: the error of the E2M1 code under its group's power of two,
+    // in real units (the code is recomputed exactly as k_v_quant4 forms it)
+    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
+    const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
+    const uint8_t* xr = a.v4s + ((size_t)bh * a.nblk + p / BLK) * V4_SREC + 16 * v4_group(p % BLK) * 8;
+    for (int i = 0; i < D / 8; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = i * 8 + j;
+        const int X = (int)xr[(c & 15) * 8 + (c >> 4)] - 127;
+        const float x = bf2f((j & 1) ? (h[j >> 1] >> 16) : h[j >> 1]) - mu[c];
+        const uint32_t code = e2m1_code(__builtin_ldexpf(x, -X));
+        tile[c * BLK + col] = f2bf_rne(x - __builtin_ldexpf(e2m1_val(code), X));
+      }
+    }
+  } else if (p >= 0) {
     const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
     const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
     const float* inv = a.inv + (size_t)bh * D;
@@ -910,7 +1035,10 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
-  hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
+  if (a.flags & VC_V4)
+    hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(128), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
   if (a.m > 0) {
     hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
     hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);

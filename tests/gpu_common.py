@@ -29,7 +29,7 @@ def oracle_params(p) -> orc.Params:
     return orc.make_params(p.B, p.H, p.N, C_=p.n_clusters, T=p.kmeans_iters, seed=p.seed,
                            rho=p.rho, sm_scale=p.sm_scale, expcast_k=p.expcast_k, tau=p.tau,
                            flags=p.flags & (vc.VSMOOTH | vc.REPAIR | vc.PERMUTE_Q |
-                                            vc.EXACT_SCORES | vc.WARM_START))
+                                            vc.EXACT_SCORES | vc.WARM_START | vc.V4))
 
 
 def to_device(q, k, v):
@@ -56,6 +56,12 @@ def out_f64(o) -> np.ndarray:
 
 def _v_col(r):
     return 32 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3)
+
+
+def _v4_byte(k):
+    """Byte of key k's E2M1 code in its block's 64-byte channel row."""
+    g = 2 * (k >> 6) + ((k >> 3) & 1)
+    return 16 * g + 8 * ((k >> 2) & 1) + 4 * ((k >> 5) & 1) + 2 * ((k >> 4) & 1) + ((k >> 1) & 1)
 
 
 def _rep_col(s):
@@ -86,9 +92,20 @@ def read_prepared(p, ws, heads) -> dict:
         sk=arr("sk", np.float32, (BH, nblk)), mu=arr("mu", np.float32, (BH, nblk, 128)),
         mup=arr("mup", np.float32, (BH, nblk, 128)), sv=arr("sv", np.float32, (BH, 128)),
         inv=arr("inv", np.float32, (BH, 128)), err=arr("err", np.float32, (BH, N)))
-    v8t = arr("v8t", np.uint8, (BH, 128, npad))
-    cols = (np.arange(npad) // 128) * 128 + _v_col(np.arange(npad) % 128)
-    out["v8"] = np.ascontiguousarray(v8t[:, :, cols].transpose(0, 2, 1))
+    if p.flags & vc.V4:
+        # codes as one byte per (position, channel), exponents [nblk][4][128]
+        t = arr("v4t", np.uint8, (BH, nblk, 128, 64))
+        k = np.arange(128)
+        by = t[:, :, :, _v4_byte(k)]                      # [h][b][c][k]
+        codes = (by >> (4 * (k & 1)).astype(np.uint8)) & 15
+        out["v8"] = np.ascontiguousarray(codes.transpose(0, 1, 3, 2).reshape(len(heads), npad, 128))
+        rec = host[L["v4s"]:L["v4s"] + BH * nblk * 512].reshape(BH, nblk, 4, 16, 8)[heads]
+        c = np.arange(128)
+        out["vexp"] = (rec[:, :, :, c & 15, c >> 4].astype(np.int16) - 127).astype(np.int8)
+    else:
+        v8t = arr("v8t", np.uint8, (BH, 128, npad))
+        cols = (np.arange(npad) // 128) * 128 + _v_col(np.arange(npad) % 128)
+        out["v8"] = np.ascontiguousarray(v8t[:, :, cols].transpose(0, 2, 1))
     if m > 0:
         out["rep_pos"] = arr("rep_pos", np.int32, (BH, mpad))[:, :m]
         dt = arr("rep_dt", np.uint16, (BH, 128, mpad))
@@ -107,7 +124,8 @@ def compare_prepared(gpu: dict, ora: dict, vsmooth: bool) -> list[str]:
     """Names of arrays that are not bit-identical (with mismatch counts)."""
     bad = []
     m = gpu["m"]
-    for key in EXACT_KEYS:
+    keys = EXACT_KEYS + (("vexp",) if "vexp" in gpu else ())
+    for key in keys:
         if key in ("labels", "centroids") and not vsmooth:
             continue
         if key in ("rep_pos", "rep_delta"):

@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 import precision_fp8_attention_amd as vc
@@ -52,7 +53,7 @@ BAD = [
     (dict(tau=7.0), vc.ERR_INVALID_ARG),
     (dict(expcast_k=0, tau=71.0), vc.ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), vc.ERR_INVALID_ARG),
-    (dict(flags=64), vc.ERR_INVALID_ARG),
+    (dict(flags=128), vc.ERR_INVALID_ARG),
     (dict(flags=vc.WARM_START | vc.REPAIR), vc.ERR_INVALID_ARG),  # warm start needs V-Smooth
     (dict(flags=vc.DEFAULT_FLAGS | vc.WARM_START | vc.REUSE_CLUSTERS), vc.ERR_INVALID_ARG),
 ]
@@ -93,11 +94,13 @@ def test_pointer_and_workspace_errors_before_device_work():
     assert L.vc_attn_forward_pcodes(C.byref(bad), fake, need, fake, None, None) == vc.ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("v4", [False, True], ids=["e4m3_v", "v4"])
 @pytest.mark.parametrize("B,H,N,C_,rho", [(1, 2, 1024, 8, 0.005), (2, 24, 16544, 32, 0.005),
                                           (1, 40, 75600, 64, 0.005), (1, 1, 1, 1, 1.0),
                                           (1, 3, 300, 5, 0.0)])
-def test_layout_aligned_and_disjoint(B, H, N, C_, rho):
-    p = vc.default_params(B, H, N, n_clusters=C_, rho=rho)
+def test_layout_aligned_and_disjoint(B, H, N, C_, rho, v4):
+    p = vc.default_params(B, H, N, n_clusters=C_, rho=rho,
+                          flags=vc.DEFAULT_FLAGS | (vc.V4 if v4 else 0))
     L = vc.workspace_layout(p)
     BH, nblk = B * H, (N + 127) // 128
     npad = nblk * 128
@@ -108,11 +111,40 @@ def test_layout_aligned_and_disjoint(B, H, N, C_, rho):
                  q8=BH * npad * 128, k8=BH * npad * 128, k16=BH * npad * 256, sq=BH * nblk * 4, sk=BH * nblk * 4,
                  mu=BH * nblk * 512, bamax=BH * nblk * 512, mup=BH * nblk * 512,
                  mupt=BH * (-(-nblk // 16)) * 8192, sv=BH * 512,
-                 inv=BH * 512, v8t=BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,
-                 rep_dt=BH * 128 * mpad * 2)
+                 inv=BH * 512, v8t=0 if v4 else BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,
+                 rep_dt=BH * 128 * mpad * 2, v4t=BH * nblk * 8192 if v4 else 0,
+                 v4s=(BH * nblk + 1) * 512 if v4 else 0)
     spans = sorted((L[k], L[k] + n, k) for k, n in sizes.items())
     for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
         assert a1 <= b0, (ka, kb)
     for k in sizes:
         assert L[k] % 256 == 0
     assert spans[-1][1] <= L["total"] == vc.workspace_size(p)
+
+
+# Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 with an FP4 A operand, as
+# measured on gfx950 by an in-bounds probe: lane group g's dword d, nibble n
+# multiplies the B operand's K index FP4_K[g][d] + n (n = 0..7).
+FP4_K = [[0, 8, 32, 40], [64, 72, 96, 104], [16, 24, 48, 56], [80, 88, 112, 120]]
+
+
+def test_v4_code_bytes_meet_their_own_p_bytes():
+    """The 4-bit tile stores key k's code where the FP4 operand multiplies it
+    with key k's ExpCast byte: lane group g of the B operand holds keys
+    16t + 4g + v in byte 4t + v, i.e. K index 32g + 4t + v, and the exponent
+    group (a lane group of A) is 2(k/64) + (k/8)%2."""
+    sys_path = os.path.join(ROOT, "tests")
+    import sys
+    sys.path.insert(0, sys_path)
+    import gpu_common as G
+    seen = set()
+    for k in range(128):
+        b = int(G._v4_byte(np.int64(k)))
+        g, within = divmod(b, 16)
+        d, half = divmod(within, 4)
+        n = 2 * half + (k & 1)
+        assert g == 2 * (k >> 6) + ((k >> 3) & 1)
+        kappa = 32 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3)
+        assert FP4_K[g][d] + n == kappa, k
+        seen.add((b, k & 1))
+    assert len(seen) == 128

@@ -59,6 +59,13 @@ SMALL = [
     ("custom_scale_seed", 1, 2, 513, 6, dict(sm_scale=0.05, seed=12345, T=3)),
     ("exact_scores", 2, 2, 300, 5, dict(flags=1 | 2 | 4 | 16)),
     ("exact_scores_one_token", 1, 1, 1, 1, dict(flags=1 | 2 | 4 | 16)),
+    # 4-bit value residual (E2M1 with one power of two per 32-key group)
+    ("v4_one_token", 1, 1, 1, 1, dict(flags=1 | 2 | 4 | 64)),
+    ("v4_ragged_tail", 2, 2, 300, 5, dict(rho=0.05, flags=1 | 2 | 4 | 64)),
+    ("v4_several_tiles", 1, 3, 1000, 8, dict(flags=1 | 2 | 4 | 64)),
+    ("v4_vsmooth_off", 1, 2, 700, 4, dict(flags=64)),
+    ("v4_repair_all", 1, 1, 260, 3, dict(rho=1.0, flags=1 | 2 | 4 | 64)),
+    ("v4_exact_scores", 2, 2, 300, 5, dict(flags=1 | 2 | 4 | 16 | 64)),
 ]
 
 
@@ -105,6 +112,18 @@ def test_workloads_sampled(cfg, heads, nrows):
     p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
     rows = G.sample_rows(wl["N"], nrows, seed=cfg)
     _full_case(p, q, k, v, heads, rows, f"workload{cfg}")
+
+
+def test_workload3_v4_sampled():
+    """The 2048x2048 CFG workload with the 4-bit value residual, in the
+    benchmark's launch configuration: all 48 heads run, three are compared."""
+    import precision_fp8_attention_amd as vc
+    wl = inputs.WORKLOADS[3]
+    q, k, v = inputs.make_inputs(3)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"],
+                     flags=vc.DEFAULT_FLAGS | vc.V4)
+    rows = G.sample_rows(wl["N"], 160, seed=41)
+    _full_case(p, q, k, v, [0, 30, 47], rows, "workload3_v4")
 
 
 def test_workload4_video_sampled():

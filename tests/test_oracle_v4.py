@@ -184,3 +184,14 @@ def test_v4_simulation_tracks_exact_attention():
     assert res["v4"] < 0.20
     assert res["e4m3"] < res["v4"]
     assert res["v4_wide"] < res["v4"] < res["v4_norep"]
+
+
+def test_prepare_rejects_heads_and_shapes_outside_the_inputs():
+    q, k, v = inputs.make_custom(1, 2, 64, seed=1)
+    P = orc.make_params(1, 2, 64, C_=2, T=2, flags=orc.DEFAULT_FLAGS | orc.V4)
+    with pytest.raises(ValueError):
+        orc.prepare(P, q, k, v, heads=[0, 2])
+    with pytest.raises(ValueError):
+        orc.prepare(P, q, k, v, heads=[-1])
+    with pytest.raises(ValueError):
+        orc.prepare(orc.make_params(1, 3, 64, C_=2, T=2), q, k, v)

@@ -91,8 +91,9 @@ enum {
                             MFMA reads.  Each 128-key block splits into four 32-key
                             groups (key k in group 2*(k/64) + (k%16)/8); every
                             (block, group, channel) gets the power of two 2^X with
-                            X = floor(log2 max|r|) - 2 (-127 for an all-zero group)
-                            and the residual r = V - mu is coded in E2M1 (round to
+                            X = floor(log2 max|r|) - 2, kept in [-126, 127] (a
+                            normal fp32 scale; -126 for an all-zero group), and
+                            the residual r = V - mu is coded in E2M1 (round to
                             nearest, ties to the even code, saturating at 6, no
                             negative zero).  No per-channel scale (sv = inv = 1),
                             repair deltas in real units, P stays ExpCast E4M3.  Set

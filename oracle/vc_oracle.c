@@ -65,8 +65,10 @@
  *   - 4-bit residual (OC_V4): the pages also run V-Smooth with the residual in
  *     NVFP4 [P5 "V-Smooth", Demean]; here in the gfx950-native MX form.  Per
  *     128-position block, channel and 32-key group (key k of the block is in
- *     group 2*(k/64) + (k mod 16)/8), X = floor(log2 max|r|) - 2 and the code is
- *     E2M1(r * 2^-X), nearest with ties to the even code, saturating at 6.  There
+ *     group 2*(k/64) + (k mod 16)/8), X = floor(log2 max|r|) - 2 kept in
+ *     [-126, 127] (2^X a normal fp32 scale; -126 for an all-zero group), and the
+ *     code is E2M1(r * 2^-X), nearest with ties to the even code, saturating at
+ *     6, no negative zero.  There
  *     is no per-channel scale (sV = 1, mu' = mu), the repair error and the
  *     stored repair residuals are in real units, and P stays the ExpCast FP8
  *     code (the pages apply ExpCast only at 8 bits, so P's format is ours).
@@ -205,13 +207,15 @@ uint8_t oc_e2m1_encode(float y) {
 
 /* MX shared exponent of a 32-value group whose largest magnitude is a: the X
  * with a * 2^-X in [4, 8), i.e. floor(log2 a) - 2 (E2M1's largest binade starts
- * at 4); -127 (the smallest E8M0 scale) when the group is all zero. */
+ * at 4), kept in [-126, 127] so that the group scale 2^X is a normal fp32 power
+ * of two (E8M0's 2^-127 has no normal fp32 form); -126 when the group is all
+ * zero. */
 int oc_mx_exponent(float a) {
-  if (!(a > 0.0f)) return -127;
+  if (!(a > 0.0f)) return -126;
   int e;
   frexpf(a, &e); /* a = m 2^e with m in [0.5, 1): floor(log2 a) = e - 1 */
   int x = e - 3;
-  return x < -127 ? -127 : (x > 127 ? 127 : x);
+  return x < -126 ? -126 : (x > 127 ? 127 : x);
 }
 
 /* 32-key groups of a 128-key block for the 4-bit residual: key k (0..127) is in

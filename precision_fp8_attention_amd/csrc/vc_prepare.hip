@@ -87,57 +87,38 @@ __device__ __forceinline__ int rep_col(int s) {
   return 32 * u + 8 * g + 4 * tp + v;
 }
 
-// E2M1 (OCP FP4) code of y, |y| < 8: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
-// ties to the even code, saturating at 6; a zero magnitude is code 0 (no
-// negative zero).  Each threshold is a midpoint; which side includes it follows
-// from which neighbour has the even code.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
+// E2M1 (OCP FP4) rounding of y, |y| < 8: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6, ties to the even code, saturating at 6; a zero magnitude is code 0 (no
+// negative zero).  Returns the code and the value it decodes to (code 0 is
+// +0, whatever the sign of y).  Inside the binade
+// [2^e, 2^(e+1)) the E2M1 values are the multiples of 2^(e-1) (0.5 below 2),
+// and adding M = 2^(max(e,0)+22) leaves exactly that step as the sum's last bit:
+// fp32 round-to-nearest-even of a + M, minus M, is the E2M1 rounding, and an
+// even last bit is an even code.  The code is read off the rounded value's
+// exponent and mantissa bits.  Plain VALU arithmetic, no compares.
+__device__ __forceinline__ float e2m1_round(float y, uint32_t* code) {
   const float a = fabsf(y);
-  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return m == 0u ? 0u : (m | (y < 0.0f ? 8u : 0u));
-}
-
-// Value of E2M1 code c: magnitudes 2..7 are 2^(m/2 - 1) * (1 + (m%2)/2), built
-// as fp32 bits; 1 is the subnormal 0.5.
-__device__ __forceinline__ float e2m1_val(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const float mag = m >= 2u ? __uint_as_float(((126u + (m >> 1)) << 23) | ((m & 1u) << 22)) : 0.5f * (float)m;
-  return (c & 8u) ? -mag : mag;
+  const float M = __uint_as_float(max(__float_as_uint(a) & 0x7f800000u, 127u << 23) + (22u << 23));
+  const float r = fminf((a + M) - M, 6.0f);
+  // r in {0, 0.5, 1, 1.5, 2, 3, 4, 6}: b = bits >> 22 is 0, 252, 254, 255, ..., 259
+  const uint32_t b = __float_as_uint(r) >> 22;
+  const uint32_t m = max(b, 251u) - 251u - ((b + 2u) >> 8);
+  const uint32_t sgn = (__float_as_uint(y) >> 28) & 8u;
+  *code = m | (m != 0u ? sgn : 0u);
+  return __uint_as_float(__float_as_uint(r) | ((*code & 8u) << 28));
 }
 
 // MX exponent of a group whose largest magnitude is amax: X with amax * 2^-X in
-// [4, 8) (E2M1's top binade), -127 for an all-zero group, clamped to E8M0.
+// [4, 8) (E2M1's top binade), kept in [-126, 127] so that 2^X is a normal fp32
+// power of two; -126 for an all-zero group.
 __device__ __forceinline__ int mx_exponent(float amax) {
-  if (!(amax > 0.0f)) return -127;
+  if (!(amax > 0.0f)) return -126;
   const int x = __builtin_amdgcn_frexp_expf(amax) - 3;  // amax = f 2^e, f in [0.5, 1)
-  return x < -127 ? -127 : (x > 127 ? 127 : x);
+  return x < -126 ? -126 : (x > 127 ? 127 : x);
 }
 
-// 32-key group of key r of a block (4-bit residual) and the byte of its code in
-// the block's 64-byte channel row: the order the FP4 operand of the forward's
-// scaled MFMA expects for the lanes' key interleave 16t+4g+v.
+// 32-key group of key r of a block (4-bit residual).
 __device__ __forceinline__ int v4_group(int r) { return 2 * (r >> 6) + ((r >> 3) & 1); }
-__device__ __forceinline__ int v4_byte(int r) {
-  return 16 * v4_group(r) + 8 * ((r >> 2) & 1) + 4 * ((r >> 5) & 1) + 2 * ((r >> 4) & 1) + ((r >> 1) & 1);
-}
-
-// Maximum of x >= 0 over the 32 lanes of a wave that share lane bit 3 (one
-// 32-key group when lane = key mod 64): the integer order of non-negative fp32
-// bits is their numeric order.  Mirror within 8 lanes, then lane ^ 1 and ^ 2
-// (DPP), then the lanes 16 and 32 apart (permlane swaps).
-__device__ __forceinline__ float group_max32(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xf, 0xf, false));  // row_half_mirror
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
-  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  u = max(p16[0], p16[1]);
-  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  u = max(p32[0], p32[1]);
-  return __uint_as_float(u);
-}
 
 // ---------------------------------------------------------------------------
 // K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; the same
@@ -613,11 +594,13 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// V block means and block maxima of |V - mu|.  grid (nblk, BH), 256 threads:
-// thread = (8-channel chunk t%16, rows t/16 + 16i).
+// V block means and block maxima of |V - mu|; with VC_V4 also the maximum of each
+// 32-key group (rows r with 2(r/64) + (r/8)%2 = G) and its E8M0 exponent.
+// grid (nblk, BH), 256 threads: thread = (8-channel chunk t%16, rows t/16 + 16i),
+// so rows i < 4 and i >= 4 of a thread lie in groups (t/128)%2 and 2 + (t/128)%2.
 __global__ __launch_bounds__(256) void k_v_stats(Args a) {
   __shared__ long long ssum[16][D];
-  __shared__ float smax[16][D];
+  __shared__ float smax[2][16][D];
   __shared__ float smu[D];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
@@ -654,24 +637,37 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
     smu[t] = vs ? fixed_mean(tot, n) : 0.0f;
   }
   __syncthreads();
-  float m[8];
+  float m[2][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+  for (int e = 0; e < 8; ++e) m[0][e] = m[1][e] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     if (r0 + 16 * i < n) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[i][e] - smu[cg * 8 + e]));
+      for (int e = 0; e < 8; ++e) m[i >> 2][e] = fmaxf(m[i >> 2][e], fabsf(x[i][e] - smu[cg * 8 + e]));
     }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) smax[r0][cg * 8 + e] = m[e];
+  for (int e = 0; e < 8; ++e) {
+    smax[0][r0][cg * 8 + e] = m[0][e];
+    smax[1][r0][cg * 8 + e] = m[1][e];
+  }
   __syncthreads();
   if (t < D) {
-    float mm = 0.0f;
-    for (int rr = 0; rr < 16; ++rr) mm = fmaxf(mm, smax[rr][t]);
+    float gm[4];  // group G = 2h + b: rows of half h, threads with (r0/8)%2 = b
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      float mm = 0.0f;
+      for (int rr = 0; rr < 8; ++rr) mm = fmaxf(mm, smax[G >> 1][8 * (G & 1) + rr][t]);
+      gm[G] = mm;
+    }
     const size_t o = ((size_t)bh * a.nblk + blk) * D + t;
     a.mu[o] = smu[t];
-    a.bamax[o] = mm;
+    a.bamax[o] = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+    if (a.flags & VC_V4) {
+      uint8_t* rec = a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) rec[(16 * G + (t & 15)) * 8 + (t >> 4)] = (uint8_t)(mx_exponent(gm[G]) + 127);
+    }
   }
 }
 
@@ -783,58 +779,84 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
     *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + t * BLK + 16 * i);
 }
 
-// 4-bit residual codes (VC_V4), the repair criterion and the group exponents.
-// One thread per row of the block, as k_v_quant.  Key r's group 2(r/64) + (r/8)%2
-// is the wave and lane bit 3, so a group maximum is a reduction over 32 lanes;
-// keys r and r^1 share a code byte and the odd lane hands its nibble to the even
-// one.  The criterion is the fp32 fma chain of (r - value)^2 over channels 0..127
-// (sv = 1).  grid (nblk, BH), 128 threads.
-__global__ __launch_bounds__(128) void k_v_quant4(Args a) {
-  __shared__ float smu[D];
-  __shared__ __align__(16) uint8_t tile[V4_TILE];
-  __shared__ __align__(16) uint8_t sexp[V4_SREC];
-  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, lane = t & 63;
-  const int p0 = blk * BLK, n = min(BLK, a.N - p0);
+// 4-bit residual codes (VC_V4) and the repair criterion.  The group exponents
+// come from k_v_stats.  Thread t owns the key pair 2t, 2t+1 of a block, whose
+// two codes share one byte of every channel row of the block's tile.  Per
+// channel, gfx950's v_cvt_scalef32_pk_fp4_f32 rounds the pair's two residuals
+// by their group's power of two into that byte (nearest, ties to the even code,
+// saturating at 6; it keeps the sign of a zero, which is cleared after), and
+// v_cvt_scalef32_pk_f32_fp4 decodes them again for the criterion: two fp32 fma
+// chains (r - value)^2 over channels 0..127 (sv = 1).  The 64 lanes' bytes make
+// up each 64-byte channel row, so every store is one coalesced row.  No
+// cross-lane traffic.  grid (nblk, BH), 64 threads.
+__global__ __launch_bounds__(64) void k_v_quant4(Args a) {
+  __shared__ __align__(16) uint8_t sx[4][D];  // [group][channel] E8M0 exponents
+  __shared__ __align__(16) float smu[D];
+  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
-  const int r = t, p = p0 + r;
-  const bool valid = r < n;
-  const int G = v4_group(r), byte = v4_byte(r);
-  // the row's 16-byte chunks (8 channels each), loaded two chunks ahead of use
-  const uint4* src = reinterpret_cast<const uint4*>(
-      a.v + ((size_t)bh * a.N + (valid ? a.perm[(size_t)bh * a.N + p] : 0)) * D);
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-  uint4 nxt0 = valid ? src[0] : zero4, nxt1 = valid ? src[1] : zero4;
+  smu[t + 64] = a.mu[((size_t)bh * a.nblk + blk) * D + t + 64];
+  {
+    // the record is [group][channel % 16][channel / 16]: transpose to channel order
+    const uint8_t* rec = a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC;
+    for (int q = t; q < V4_SREC; q += 64) sx[q >> 7][16 * (q & 7) + ((q >> 3) & 15)] = rec[q];
+  }
+  const int p0 = blk * BLK, n = min(BLK, a.N - p0);
+  const int k0 = 2 * t;
+  const int G = v4_group(k0);
+  const int byte = 16 * G + 8 * ((k0 >> 2) & 1) + 4 * ((k0 >> 5) & 1) + 2 * ((k0 >> 4) & 1) + ((k0 >> 1) & 1);
+  // a key past N reads the block's first row (finite input) and is zeroed by the
+  // multiply: residual 0, code 0; every load stays unconditional
+  const bool ok0 = k0 < n, ok1 = k0 + 1 < n;
+  const float keep0 = ok0 ? 1.0f : 0.0f, keep1 = ok1 ? 1.0f : 0.0f;
+  const int* perm = a.perm + (size_t)bh * a.N + p0;
+  const uint4* src0 = reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.N + perm[ok0 ? k0 : 0]) * D);
+  const uint4* src1 = reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.N + perm[ok1 ? k0 + 1 : 0]) * D);
+  uint8_t* dst = a.v4t + ((size_t)bh * a.nblk + blk) * V4_TILE + byte;
   __syncthreads();
-  float e = 0.0f;
+  float e0 = 0.0f, e1 = 0.0f;
+  // two halves of 64 channels: each half of a row is one 128-byte line, loaded
+  // in one burst and used at once; the loop is kept rolled so that no half's
+  // work moves into the other
 #pragma unroll 1
-  for (int i = 0; i < D / 8; ++i) {
-    const uint4 u = nxt0;
-    nxt0 = nxt1;
-    if (i + 2 < D / 8) nxt1 = valid ? src[i + 2] : zero4;
-    const uint32_t hw[4] = {u.x, u.y, u.z, u.w};
+  for (int hh = 0; hh < 2; ++hh) {
+    uint4 row0[8], row1[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 8 * i + j;
-      // rows past N have residual 0: they raise no maximum and get code 0
-      const float x = valid ? bf2f((j & 1) ? (hw[j >> 1] >> 16) : hw[j >> 1]) - smu[c] : 0.0f;
-      const int X = mx_exponent(group_max32(fabsf(x)));
-      const uint32_t code = e2m1_code(__builtin_ldexpf(x, -X));
-      const float dl = x - __builtin_ldexpf(e2m1_val(code), X);
-      e = __builtin_fmaf(dl, dl, e);
-      const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code, 0xb1, 0xf, 0xf, false);
-      if (!(r & 1)) tile[c * (BLK / 2) + byte] = (uint8_t)(code | (odd << 4));
-      if ((lane & ~8) == 0) sexp[(16 * G + (c & 15)) * 8 + (c >> 4)] = (uint8_t)(X + 127);
+    for (int i = 0; i < 8; ++i) {
+      row0[i] = src0[8 * hh + i];
+      row1[i] = src1[8 * hh + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cb = 64 * hh + 8 * i;  // first channel of the chunk
+      float mu8[8];
+      *reinterpret_cast<float4*>(mu8) = *reinterpret_cast<const float4*>(smu + cb);
+      *reinterpret_cast<float4*>(mu8 + 4) = *reinterpret_cast<const float4*>(smu + cb + 4);
+      const uint2 xb = *reinterpret_cast<const uint2*>(&sx[G][cb]);
+      const uint32_t w0[4] = {row0[i].x, row0[i].y, row0[i].z, row0[i].w};
+      const uint32_t w1[4] = {row1[i].x, row1[i].y, row1[i].z, row1[i].w};
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int c = cb + jj;
+        const uint32_t eb = ((jj < 4 ? xb.x : xb.y) >> (8 * (jj & 3))) & 0xffu;
+        const float sc = __uint_as_float(eb << 23);  // 2^X, X in [-126, 127]: normal
+        const uint32_t h0 = (jj & 1) ? (w0[jj >> 1] & 0xffff0000u) : (w0[jj >> 1] << 16);
+        const uint32_t h1 = (jj & 1) ? (w1[jj >> 1] & 0xffff0000u) : (w1[jj >> 1] << 16);
+        const float x0 = (__uint_as_float(h0) - mu8[jj]) * keep0;
+        const float x1 = (__uint_as_float(h1) - mu8[jj]) * keep1;
+        uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, sc, 0) & 0xffu;
+        // clear the sign of zero magnitudes (code 8 -> 0)
+        d &= 0x77u | (((d & 0x77u) + 0x77u) & 0x88u);
+        dst[c * (BLK / 2)] = (uint8_t)d;
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, sc, 0);
+        const float dl0 = x0 - v[0], dl1 = x1 - v[1];
+        e0 = __builtin_fmaf(dl0, dl0, e0);
+        e1 = __builtin_fmaf(dl1, dl1, e1);
+      }
     }
   }
-  if (valid) a.err[(size_t)bh * a.N + p] = e;
-  __syncthreads();
-  uint8_t* dt = a.v4t + ((size_t)bh * a.nblk + blk) * V4_TILE;
-#pragma unroll
-  for (int i = 0; i < V4_TILE / (16 * 128); ++i)
-    *reinterpret_cast<uint4*>(dt + 16 * (t + 128 * i)) = *reinterpret_cast<const uint4*>(tile + 16 * (t + 128 * i));
-  if (t < V4_SREC / 16)
-    *reinterpret_cast<uint4*>(a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC + 16 * t) =
-        *reinterpret_cast<const uint4*>(sexp + 16 * t);
+  if (ok0) a.err[(size_t)bh * a.N + p0 + k0] = e0;
+  if (ok1) a.err[(size_t)bh * a.N + p0 + k0 + 1] = e1;
 }
 
 // ---------------------------------------------------------------------------
@@ -954,8 +976,9 @@ __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
         const int c = i * 8 + j;
         const int X = (int)xr[(c & 15) * 8 + (c >> 4)] - 127;
         const float x = bf2f((j & 1) ? (h[j >> 1] >> 16) : h[j >> 1]) - mu[c];
-        const uint32_t code = e2m1_code(__builtin_ldexpf(x, -X));
-        tile[c * BLK + col] = f2bf_rne(x - __builtin_ldexpf(e2m1_val(code), X));
+        uint32_t code;
+        const float val = e2m1_round(__builtin_ldexpf(x, -X), &code);
+        tile[c * BLK + col] = f2bf_rne(x - __builtin_ldexpf(val, X));
       }
     }
   } else if (p >= 0) {
@@ -1036,7 +1059,7 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
   if (a.flags & VC_V4)
-    hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
   if (a.m > 0) {

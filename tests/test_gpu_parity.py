@@ -79,6 +79,45 @@ def test_small_cases(label, B, H, N, C_, kw):
     _full_case(p, q, k, v, heads, np.arange(N, dtype=np.int32), label)
 
 
+def _v4_midpoint_values(N, seed):
+    """bf16 V [1, 1, N, 128] whose 32-key groups hit every E2M1 rounding case.
+    With V-Smooth off the residual is V itself (mean 0).  Each (block, group,
+    channel) gets an exponent X in [-8, -2] and the group maximum 7 * 2^X (so the
+    MX exponent is X); the other members are the midpoints 0.25 ... 5, the
+    saturating 7 and 6, the grid values, and signed zeros, times 2^X: all exact
+    in bf16.  |V| <= 1.75 keeps the output within the absolute bar."""
+    rng = np.random.default_rng(seed)
+    base = np.array([7, -7, 5, -5, 3.5, -3.5, 2.5, -2.5, 1.75, -1.75, 1.25, -1.25, 0.75, -0.75,
+                     0.25, -0.25, 6, -6, 0.0, -0.0, 0.5, -0.5, 1, -1, 1.5, -1.5, 2, -2, 3, -3, 4, -4],
+                    np.float32)
+    v = np.zeros((N, 128), np.float32)
+    k = np.arange(128)
+    grp = 2 * (k >> 6) + ((k >> 3) & 1)
+    for b in range((N + 127) // 128):
+        for G in range(4):
+            rows = b * 128 + k[grp == G]
+            rows = rows[rows < N]
+            for c in range(128):
+                X = (c + 3 * G + 5 * b) % 7 - 8
+                vals = base[rng.permutation(32)] * np.float32(2.0 ** X)
+                vals[0] = 7 * 2.0 ** X if len(rows) else 0  # the maximum is present
+                v[rows, c] = vals[:len(rows)]
+    bits = v.view(np.uint32)
+    assert np.all((bits & 0xffff) == 0)  # exact in bf16
+    return (bits >> 16).astype(np.uint16).reshape(1, 1, N, 128)
+
+
+@pytest.mark.parametrize("N,flags,rho", [(256, 64, 0.0), (300, 64 | 2, 0.05)],
+                         ids=["two_blocks", "ragged_repair"])
+def test_v4_codes_at_every_rounding_midpoint(N, flags, rho):
+    """E2M1 ties (to the even code), saturation and signed zeros on the GPU,
+    bit-exact with the oracle, whose encoder is pinned to the closed form."""
+    q, k, _ = inputs.make_custom(1, 1, N, seed=77)
+    v = _v4_midpoint_values(N, seed=N)
+    p = G.lib_params(1, 1, N, 2, rho=rho, flags=flags)
+    _full_case(p, q, k, v, [0], np.arange(N, dtype=np.int32), f"v4_midpoints_{N}")
+
+
 @pytest.mark.parametrize("exact", [False, True], ids=["fp8_scores", "exact_scores"])
 def test_workload0_all_rows(exact):
     import precision_fp8_attention_amd as vc

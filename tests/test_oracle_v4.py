@@ -55,12 +55,15 @@ def test_e2m1_encode_matches_closed_form():
 
 def test_mx_exponent_puts_group_max_in_the_top_binade():
     rng = np.random.default_rng(3)
-    a = (rng.random(5000) * 2.0 ** rng.integers(-40, 40, 5000)).astype(np.float32)
+    a = (rng.random(5000) * 2.0 ** rng.integers(-40, 40, 5000)).astype(np.float32)  # X well inside the clamp
     a = a[a > 0]
     X = orc.mx_exponent(a)
     y = a.astype(np.float64) * 2.0 ** -X.astype(np.float64)
     assert np.all((y >= 4.0) & (y < 8.0))
-    assert list(orc.mx_exponent(np.array([0.0, 1.0, 4.0, 2.0 ** 20], np.float32))) == [-127, -2, 0, 18]
+    assert list(orc.mx_exponent(np.array([0.0, 1.0, 4.0, 2.0 ** 20], np.float32))) == [-126, -2, 0, 18]
+    # the scale stays a normal fp32 power of two: tiny groups clamp at 2^-126
+    assert list(orc.mx_exponent(np.array([2.0 ** -124, 2.0 ** -125, 2.0 ** -140], np.float32))) == [-126, -126, -126]
+    assert list(orc.mx_exponent(np.array([2.0 ** -123], np.float32))) == [-125]
 
 
 def test_v4_groups_partition_each_block():

@@ -29,6 +29,7 @@ PERMUTE_Q = 4
 EXACT_SCORES = 16
 WARM_START = 32
 V4 = 64
+SMOOTH_Q = 128
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 
@@ -53,7 +54,7 @@ class Params(C.Structure):
 class _Prep(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "labels", "perm", "iperm", "centroids", "kbar", "q8", "k8", "sq", "sk", "mu", "mup",
-        "v8", "sv", "inv", "err", "rep_pos", "rep_delta", "vexp")] + [("mcap", C.c_int32)]
+        "v8", "sv", "inv", "err", "rep_pos", "rep_delta", "vexp", "qbar", "qbias")] + [("mcap", C.c_int32)]
 
 
 _lib = None
@@ -128,7 +129,9 @@ def prepare(P: Params, q, k, v, heads=None, init_centroids=None) -> dict:
         mup=np.zeros((nh, nblk, d), np.float32), v8=np.zeros((nh, npad, d), np.uint8),
         sv=np.zeros((nh, d), np.float32), inv=np.zeros((nh, d), np.float32),
         err=np.zeros((nh, N), np.float32), rep_pos=np.zeros((nh, mcap), np.int32),
-        rep_delta=np.zeros((nh, mcap, d), np.uint16), vexp=np.zeros((nh, nblk, 4, d), np.int8))
+        rep_delta=np.zeros((nh, mcap, d), np.uint16), vexp=np.zeros((nh, nblk, 4, d), np.int8),
+        qbar=np.zeros((nh, nblk, d), np.float32),
+        qbias=np.zeros((nh, nblk, npad) if P.flags & SMOOTH_Q else (nh, 1, 1), np.float32))
     if P.flags & WARM_START:
         if init_centroids is None:
             raise ValueError("WARM_START needs init_centroids")

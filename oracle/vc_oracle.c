@@ -72,6 +72,16 @@
  *     is no per-channel scale (sV = 1, mu' = mu), the repair error and the
  *     stored repair residuals are in real units, and P stays the ExpCast FP8
  *     code (the pages apply ExpCast only at 8 bits, so P's format is ours).
+ *   - Q smoothing (OC_SMOOTH_Q): the pages name the query and key smoothing of
+ *     earlier methods (SageAttention2) [P5 "Por que a atencao e o gargalo"];
+ *     here each 128-position query block b subtracts its channel mean qbar_b
+ *     (an exact fixed-point mean, like the V means) before its codes and scale
+ *     are formed, and the dropped part returns as a per-key term of the score:
+ *     delta_bj = qbar_b . k~_j, an fp32 fma chain over channels 0..127 with the
+ *     same fp32 k~ = k - kbar the K codes come from, and d_bj = fp32(c0 *
+ *     delta_bj) in code units.  A score becomes t = fma(S_raw, alpha, d_bj); the
+ *     block maximum is taken over t, and code = clamp(rne(t + (56 + 8k - M)),
+ *     0, 126), the sum an fp32 add.  Repaired keys use the same d.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma -shared -fPIC (fp32 operations
  * must not be contracted; fmaf is always an explicit single-rounding fma).
@@ -87,6 +97,7 @@
 #define OC_EXACT_SCORES 16u
 #define OC_WARM_START 32u
 #define OC_V4 64u
+#define OC_SMOOTH_Q 128u
 
 typedef struct {
   int32_t B, H, N, d;     /* d must be 128 */
@@ -117,6 +128,9 @@ typedef struct {
   int32_t *rep_pos;  /* [nh][mcap] repaired positions, ascending                 */
   uint16_t *rep_delta; /* [nh][mcap][d] bf16 residual error, V code units        */
   int8_t *vexp;      /* [nh][nblk][4][d] MX exponents of the 4-bit residual (OC_V4) */
+  float *qbar;       /* [nh][nblk][d] query block means (OC_SMOOTH_Q)            */
+  float *qbias;      /* [nh][nblk][Npad] score correction c0 * qbar_b . k~_j in
+                        code units, query block b, key position j (OC_SMOOTH_Q) */
   int32_t mcap;      /* capacity of the repair arrays (>= m)                     */
 } oc_prep;
 
@@ -369,6 +383,16 @@ static void kmeans_head(const oc_params *P, int64_t head, const float *v /*[N][d
 /* Prepare: one (batch, head)                                                 */
 /* ------------------------------------------------------------------------- */
 
+static float sm_scale_of(const oc_params *P) {
+  return P->sm_scale > 0.0f ? P->sm_scale : (float)(1.0 / sqrt((double)P->d));
+}
+
+/* c0 converts a raw score (code units of Q times code units of K, times the two
+ * block scales) to ExpCast code units: 8 * log2(e) * softmax scale. */
+static float code_gain(const oc_params *P) {
+  return (float)(8.0 * 1.4426950408889634074 * (double)sm_scale_of(P));
+}
+
 /* Value of residual code `code` of position p, channel c, in the units of the
  * residual x: the E4M3 value (V code units), or with the 4-bit residual the E2M1
  * value times its group's power of two (real units; exact in fp32). */
@@ -385,6 +409,7 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
   const int nblk = (N + 127) / 128, Npad = nblk * 128;
   const int vs = (P->flags & OC_VSMOOTH) != 0;
   const int v4 = (P->flags & OC_V4) != 0;
+  const int sq_on = (P->flags & OC_SMOOTH_Q) != 0;
   const int m = repair_count(P);
   float *q = (float *)malloc(sizeof(float) * (size_t)N * d);
   float *k = (float *)malloc(sizeof(float) * (size_t)N * d);
@@ -432,16 +457,25 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
     kbar[c] = fixed_mean(s, N);
   }
 
-  /* Per-128-position-block E4M3 quantisation of Q and smoothed K [P1 intro]. */
+  /* Per-128-position-block E4M3 quantisation of Q and smoothed K [P1 intro].
+   * With OC_SMOOTH_Q the Q block first subtracts its channel mean. */
   memset(q8, 0, (size_t)Npad * d);
   memset(k8, 0, (size_t)Npad * d);
   for (int b = 0; b < nblk; ++b) {
     int p0 = b * 128, p1 = p0 + 128 < N ? p0 + 128 : N;
     float aq = 0.0f, ak = 0.0f, s, iv;
+    float qm[128];
+    for (int c = 0; c < d; ++c) {
+      int64_t sum = 0;
+      if (sq_on)
+        for (int p = p0; p < p1; ++p) sum += fx24(q[(size_t)((P->flags & OC_PERMUTE_Q) ? perm[p] : p) * d + c]);
+      qm[c] = sq_on ? fixed_mean(sum, p1 - p0) : 0.0f;
+      if (sq_on) o->qbar[((size_t)slot * nblk + b) * d + c] = qm[c];
+    }
     for (int p = p0; p < p1; ++p) {
       int jq = (P->flags & OC_PERMUTE_Q) ? perm[p] : p, jk = perm[p];
       for (int c = 0; c < d; ++c) {
-        float xq = q[(size_t)jq * d + c];
+        float xq = q[(size_t)jq * d + c] - qm[c];
         float xk = k[(size_t)jk * d + c] - kbar[c];
         if (fabsf(xq) > aq) aq = fabsf(xq);
         if (fabsf(xk) > ak) ak = fabsf(xk);
@@ -451,7 +485,7 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
     sq[b] = s;
     for (int p = p0; p < p1; ++p) {
       int jq = (P->flags & OC_PERMUTE_Q) ? perm[p] : p;
-      for (int c = 0; c < d; ++c) q8[(size_t)p * d + c] = oc_e4m3_encode(q[(size_t)jq * d + c] * iv);
+      for (int c = 0; c < d; ++c) q8[(size_t)p * d + c] = oc_e4m3_encode((q[(size_t)jq * d + c] - qm[c]) * iv);
     }
     scale_from_amax(ak, &s, &iv);
     sk[b] = s;
@@ -460,6 +494,22 @@ static void prepare_head(const oc_params *P, int64_t head, const uint16_t *qh, c
       for (int c = 0; c < d; ++c) {
         float xk = k[(size_t)jk * d + c] - kbar[c];
         k8[(size_t)p * d + c] = oc_e4m3_encode(xk * iv);
+      }
+    }
+  }
+
+  /* Score correction of the smoothed queries: d_bj = fp32(c0 * qbar_b . k~_j),
+   * the dot product an fp32 fma chain in channel order (padding keys: 0). */
+  if (sq_on) {
+    const float c0 = code_gain(P);
+    for (int b = 0; b < nblk; ++b) {
+      const float *qm = o->qbar + ((size_t)slot * nblk + b) * d;
+      float *db = o->qbias + ((size_t)slot * nblk + b) * Npad;
+      for (int p = 0; p < Npad; ++p) {
+        float delta = 0.0f;
+        if (p < N)
+          for (int c = 0; c < d; ++c) delta = fmaf(qm[c], k[(size_t)perm[p] * d + c] - kbar[c], delta);
+        db[p] = p < N ? c0 * delta : 0.0f;
       }
     }
   }
@@ -586,16 +636,6 @@ int oc_prepare(const oc_params *P, const uint16_t *q, const uint16_t *k, const u
 /* Forward: online ExpCast softmax with Restore and repair                    */
 /* ------------------------------------------------------------------------- */
 
-static float sm_scale_of(const oc_params *P) {
-  return P->sm_scale > 0.0f ? P->sm_scale : (float)(1.0 / sqrt((double)P->d));
-}
-
-/* c0 converts a raw score (code units of Q times code units of K, times the two
- * block scales) to ExpCast code units: 8 * log2(e) * softmax scale. */
-static float code_gain(const oc_params *P) {
-  return (float)(8.0 * 1.4426950408889634074 * (double)sm_scale_of(P));
-}
-
 /* Decoded value of every code, filled from oc_e4m3_decode before any
  * parallel region (a cache of the decoder, nothing more). */
 static double DEC[256];
@@ -662,6 +702,8 @@ static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t 
   const int p = (P->flags & OC_PERMUTE_Q) ? o->iperm[(size_t)slot * N + row] : row;
   const int a = p / 128;
   const int v4 = (P->flags & OC_V4) != 0;
+  /* smoothed queries: per-key score term of this row's query block, code units */
+  const float *dq = (P->flags & OC_SMOOTH_Q) ? o->qbias + ((size_t)slot * nblk + a) * Npad : NULL;
   const float c0 = code_gain(P);
   const float bias = (float)(56 + 8 * P->expcast_k);
   float M = -INFINITY;
@@ -677,14 +719,16 @@ static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t 
     double r, lb = 0.0;
     for (int j = j0; j < j1; ++j) {
       S[j - j0] = raw_score(P, q8 + (size_t)p * d, k8 + (size_t)j * d, d);
+      if (dq) S[j - j0] = fmaf(S[j - j0], alpha, dq[j]); /* t, code units */
       if (S[j - j0] > smax) smax = S[j - j0];
     }
-    tmax = smax * alpha;
+    tmax = dq ? smax : smax * alpha;
     Mn = (isinf(M) || (tmax - M) > P->tau) ? tmax : M;
     beta = bias - Mn;
     r = isinf(M) ? 0.0 : exp2(((double)M - (double)Mn) / 8.0);
     for (int j = j0; j < j1; ++j) {
-      code[j - j0] = oc_expcast(S[j - j0], alpha, beta);
+      /* with smoothed queries fma(t, 1, beta) is the fp32 sum t + beta */
+      code[j - j0] = dq ? oc_expcast(S[j - j0], 1.0f, beta) : oc_expcast(S[j - j0], alpha, beta);
       lb += DEC[code[j - j0]];
       if (pcodes) pcodes[j] = code[j - j0];
     }
@@ -709,7 +753,7 @@ static void forward_row(const oc_params *P, const oc_prep *o, int slot, int32_t 
     int b = j / 128;
     float alpha = (sq[a] * sk[b]) * c0;
     float s = raw_score(P, q8 + (size_t)p * d, k8 + (size_t)j * d, d);
-    double pw = DEC[oc_expcast(s, alpha, bias - M)];
+    double pw = dq ? DEC[oc_expcast(fmaf(s, alpha, dq[j]), 1.0f, bias - M)] : DEC[oc_expcast(s, alpha, bias - M)];
     const uint16_t *dl = o->rep_delta + ((size_t)slot * o->mcap + i) * d;
     for (int c = 0; c < d; ++c) acc[c] += pw * (double)bf16_to_f32(dl[c]);
   }

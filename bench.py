@@ -138,6 +138,8 @@ def main():
                     help="time only vc_attn_forward launches (profiling runs)")
     ap.add_argument("--v4", action="store_true",
                     help="with --forward-only: the 4-bit value residual variant")
+    ap.add_argument("--smooth-q", action="store_true",
+                    help="with --forward-only: the smoothed-query variant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -177,16 +179,18 @@ def main():
         vc.forward(p, ws, o)
 
     if args.forward_only:
-        if args.v4:
+        if args.v4 or args.smooth_q:
             p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
-                                  flags=vc.DEFAULT_FLAGS | vc.V4)
+                                  flags=vc.DEFAULT_FLAGS | (vc.V4 if args.v4 else 0) |
+                                  (vc.SMOOTH_Q if args.smooth_q else 0))
             ws = vc.alloc_workspace(p, dev)
         step()
         for _ in range(args.warmup):
             vc.forward(p, ws, o)
         torch.cuda.synchronize()
         ms = _events_ms(lambda: vc.forward(p, ws, o), args.steps)
-        print(json.dumps({"forward_ms": ms, "launches": args.steps + args.warmup + 1, "v4": args.v4}))
+        print(json.dumps({"forward_ms": ms, "launches": args.steps + args.warmup + 1, "v4": args.v4,
+                          "smooth_q": args.smooth_q}))
         return
 
     for _ in range(args.warmup):
@@ -208,26 +212,32 @@ def main():
 
     sched = denoise_schedule(p, qd, kd, vd, ws, o, flops)
 
-    # the 4-bit value residual (E2M1 + one power of two per 32-key group) on the
-    # same workload, in its own workspace
-    p4 = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
-                           flags=vc.DEFAULT_FLAGS | vc.V4)
-    ws4 = vc.alloc_workspace(p4, dev)
-    o4 = torch.empty_like(qd)
+    def variant(extra, name):
+        """Step, forward and prepare times of a flag variant on the same workload,
+        in its own workspace."""
+        pv_ = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                                flags=vc.DEFAULT_FLAGS | extra)
+        wsv = vc.alloc_workspace(pv_, dev)
+        ov = torch.empty_like(qd)
 
-    def step4():
-        vc.prepare(p4, qd, kd, vd, ws4)
-        vc.forward(p4, ws4, o4)
+        def stepv():
+            vc.prepare(pv_, qd, kd, vd, wsv)
+            vc.forward(pv_, wsv, ov)
 
-    for _ in range(max(args.warmup, 1)):
-        step4()
-    ms4_step = _events_ms(step4, max(args.steps // 2, 5))
-    ms4_fwd = _events_ms(lambda: vc.forward(p4, ws4, o4), max(args.steps, 10))
-    ms4_prep = _events_ms(lambda: vc.prepare(p4, qd, kd, vd, ws4), max(args.steps // 2, 5))
-    del ws4, o4
-    v4 = {"flags": "VSMOOTH|REPAIR|PERMUTE_Q|V4", "ms_per_step": round(ms4_step, 4),
-          "tflops": round(flops / (ms4_step * 1e-3) / 1e12, 3), "forward_ms": round(ms4_fwd, 4),
-          "forward_tflops": round(flops / (ms4_fwd * 1e-3) / 1e12, 3), "prepare_ms": round(ms4_prep, 4)}
+        for _ in range(max(args.warmup, 1)):
+            stepv()
+        ms_s = _events_ms(stepv, max(args.steps // 2, 5))
+        ms_f = _events_ms(lambda: vc.forward(pv_, wsv, ov), max(args.steps, 10))
+        ms_p = _events_ms(lambda: vc.prepare(pv_, qd, kd, vd, wsv), max(args.steps // 2, 5))
+        del wsv, ov
+        return {"flags": "VSMOOTH|REPAIR|PERMUTE_Q|" + name, "ms_per_step": round(ms_s, 4),
+                "tflops": round(flops / (ms_s * 1e-3) / 1e12, 3), "forward_ms": round(ms_f, 4),
+                "forward_tflops": round(flops / (ms_f * 1e-3) / 1e12, 3), "prepare_ms": round(ms_p, 4)}
+
+    # the 4-bit value residual (E2M1 + one power of two per 32-key group) and the
+    # smoothed queries (per-block query means, per-key score term)
+    v4 = variant(vc.V4, "V4")
+    smq = variant(vc.SMOOTH_Q, "SMOOTH_Q")
 
     vc.prepare(p, qd, kd, vd, ws)
     vc.forward(p, ws, o)
@@ -260,6 +270,7 @@ def main():
         "wall_ms_per_step": round(wall_ms, 4),
         "denoise_schedule": sched,
         "v4_residual": v4,
+        "smooth_q": smq,
         "roofline": {"bound": "mfma", "kernel": "k_fwd", "achieved": round(fwd_tflops, 3),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 5),

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvcattn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_PREPARED, ERR_HIP, ERR_INTERNAL = range(7)
-VSMOOTH, REPAIR, PERMUTE_Q, REUSE_CLUSTERS, EXACT_SCORES, WARM_START, V4 = 1, 2, 4, 8, 16, 32, 64
+VSMOOTH, REPAIR, PERMUTE_Q, REUSE_CLUSTERS, EXACT_SCORES, WARM_START, V4, SMOOTH_Q = 1, 2, 4, 8, 16, 32, 64, 128
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 EXPORTS = ("vc_attn_default_params", "vc_attn_workspace_size", "vc_attn_workspace_layout",
@@ -30,7 +30,7 @@ class Params(C.Structure):
 
 LAYOUT_FIELDS = ("total", "header", "kbar", "ksum", "init_idx", "centroids", "labels", "perm",
                  "iperm", "q8", "k8", "k16", "sq", "sk", "mu", "bamax", "mup", "mupt", "sv", "inv", "v8t", "err",
-                 "rep_pos", "rep_dt", "v4t", "v4s")
+                 "rep_pos", "rep_dt", "v4t", "v4s", "qbar", "qbias")
 
 
 class Layout(C.Structure):

@@ -28,7 +28,7 @@ static vc_status check(const vc_attn_params* p) {
   if (!std::isfinite(p->sm_scale)) return VC_ERR_INVALID_ARG;
   if (!(p->tau >= 0.0f) || 56.0f + 8.0f * p->expcast_k + p->tau > 126.0f) return VC_ERR_INVALID_ARG;
   if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS |
-                         VC_EXACT_SCORES | VC_WARM_START | VC_V4))
+                         VC_EXACT_SCORES | VC_WARM_START | VC_V4 | VC_SMOOTH_Q))
     return VC_ERR_INVALID_ARG;
   if ((p->flags & VC_WARM_START) && (!(p->flags & VC_VSMOOTH) || (p->flags & VC_REUSE_CLUSTERS)))
     return VC_ERR_INVALID_ARG;
@@ -51,6 +51,7 @@ bool shape_of(const vc_attn_params* p, Shape* s) {
   s->nkm = (p->N + KM_CHUNK - 1) / KM_CHUNK;
   s->nch16 = (s->nblk + 15) / 16;
   s->v4 = (p->flags & VC_V4) != 0;
+  s->smooth_q = (p->flags & VC_SMOOTH_Q) != 0;
   return true;
 }
 
@@ -97,6 +98,8 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.rep_dt = take(BH * D * (size_t)s.mpad * 2);
   L.v4t = take(s.v4 ? BH * nb * V4_TILE : 0);
   L.v4s = take(s.v4 ? (BH * nb + 1) * V4_SREC : 0);
+  L.qbar = take(s.smooth_q ? BH * nb * D * 4 : 0);
+  L.qbias = take(s.smooth_q ? BH * nb * Np * 4 : 0);
   L.total = off;
 }
 
@@ -154,6 +157,8 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.v8t = b + L.v8t;
   a.v4t = b + L.v4t;
   a.v4s = b + L.v4s;
+  a.qbar = reinterpret_cast<float*>(b + L.qbar);
+  a.qbias = reinterpret_cast<float*>(b + L.qbias);
   a.err = reinterpret_cast<float*>(b + L.err);
   a.rep_pos = reinterpret_cast<int*>(b + L.rep_pos);
   a.rep_dt = reinterpret_cast<uint16_t*>(b + L.rep_dt);
@@ -280,6 +285,6 @@ const char* vc_attn_status_string(vc_status s) {
   return "unknown status";
 }
 
-int32_t vc_attn_version(void) { return 101; }
+int32_t vc_attn_version(void) { return 102; }
 
 }  // extern "C"

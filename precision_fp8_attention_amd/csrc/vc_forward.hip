@@ -281,7 +281,7 @@ template <bool EXACT> struct QOp;
 template <> struct QOp<true> { v8bf v[2][4]; };
 template <> struct QOp<false> { v8i v[2]; };
 
-template <bool EXACT, bool V4>
+template <bool EXACT, bool V4, bool SQ>
 __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
   // LDS stages: FP8 mode holds four key blocks (two computed per barrier while
@@ -292,7 +292,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
   __shared__ __align__(1024) uint8_t ksm[NST][BLK * KROW];   // [stage] K rows
   __shared__ __align__(1024) uint8_t vsm[NST][VTILE];        // [stage] V^T codes
   __shared__ __align__(1024) uint8_t ssm[NST][SREC];         // [stage] V exponents
+  __shared__ __align__(16) float sbias[SQ ? NST : 1][2][BLK];  // [stage][query block] score terms
   __shared__ float alpha_s[2][BLK];
+  __shared__ float dsel_s[SQ ? 2 : 1][BLK];                   // repair: score terms of the slots
 
   // block scales are read-only here: constant address space -> scalar loads
   typedef __attribute__((address_space(4))) const float cfloat;
@@ -352,6 +354,14 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
         const int r = 8 * i + w;
         const int row = 8 * r + (lane >> 3), cc = (lane & 7) ^ row_swz(row);
         dma16(v8t + (size_t)row * a.Npad + (size_t)kb * BLK + cc * 16, vd + r * 1024);
+      }
+    }
+    if constexpr (SQ) {
+      // smoothed queries: the block's 128 score terms of both query blocks
+      // (lanes 0-31 the first, 32-63 the second), 1 KB
+      if (w == 1) {
+        const int qsel = min(2 * (logical % npair) + (lane >> 5), a.nblk - 1);
+        dma16(a.qbias + ((size_t)bh * a.nblk + qsel) * a.Npad + (size_t)kb * BLK + 4 * (lane & 31), sbias[kb % NST]);
       }
     }
   };
@@ -414,6 +424,17 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
         S[0][t] = mfma_f8(kop, qop.v[0], zero);
         S[1][t] = mfma_f8(kop, qop.v[1], zero);
       }
+      if constexpr (SQ) {
+        // smoothed queries: scores become t = fma(S, alpha, d) in code units;
+        // lane group g holds keys 16t+4g..16t+4g+3
+        const float alpha = (sQa * sk[kb]) * a.c0;
+        const float4 d4 = *reinterpret_cast<const float4*>(&sbias[kb % NST][wg][16 * t + 4 * g]);
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) S[qs][t][v] = __builtin_fmaf(S[qs][t][v], alpha, dv[v]);
+      }
     }
   };
   // masking, row maximum, rescale and ExpCast codes of one key block
@@ -429,8 +450,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
           for (int v = 0; v < 4; ++v)
             if (16 * t + 4 * g + v >= nvalid) S[qs][t][v] = -INFINITY;
     }
-    pop[0] = softmax_codes(S[0], rs[0], alpha, a.bias, a.tau);
-    pop[1] = softmax_codes(S[1], rs[1], alpha, a.bias, a.tau);
+    // smoothed queries already hold t in code units: fma(t, 1, beta) = t + beta
+    pop[0] = softmax_codes(S[0], rs[0], SQ ? 1.0f : alpha, a.bias, a.tau);
+    pop[1] = softmax_codes(S[1], rs[1], SQ ? 1.0f : alpha, a.bias, a.tau);
     if (a.pcodes) {
       // lane (g, q) holds keys 16t+4g..16t+4g+3 of query row q: one dword each
 #pragma unroll
@@ -562,9 +584,15 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
       alpha_s[0][tid] = (a.sq[(size_t)bh * a.nblk + 2 * (logical % npair)] * sk_pos) * a.c0;
       const int qb1 = min(2 * (logical % npair) + 1, a.nblk - 1);
       alpha_s[1][tid] = (a.sq[(size_t)bh * a.nblk + qb1] * sk_pos) * a.c0;
+      if constexpr (SQ) {
+        const size_t col = (size_t)(pos < 0 ? 0 : pos);
+        dsel_s[0][tid] = a.qbias[((size_t)bh * a.nblk + 2 * (logical % npair)) * a.Npad + col];
+        dsel_s[1][tid] = a.qbias[((size_t)bh * a.nblk + qb1) * a.Npad + col];
+      }
     }
     __syncthreads();
     const float* al = alpha_s[w >> 2];
+    const float* dsl = dsel_s[SQ ? (w >> 2) : 0];
     const uint16_t* dt = a.rep_dt + (size_t)bh * D * a.mpad + (size_t)grp * BLK;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -584,7 +612,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
             S = score_tile8(Ks, 16 * t + l16, g, qop.v[qs]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t code = expcast_byte(S[v], al[16 * t + 4 * g + v], beta);
+            const int slot = 16 * t + 4 * g + v;
+            const uint32_t code = SQ ? expcast_byte(__builtin_fmaf(S[v], al[slot], dsl[slot]), 1.0f, beta)
+                                     : expcast_byte(S[v], al[slot], beta);
             // E4M3 values are exact in bf16
             bop[4 * tp + v] = __builtin_bit_cast(__bf16, f2bf_rne(__builtin_amdgcn_cvt_f32_fp8((int)code, 0)));
           }
@@ -628,14 +658,18 @@ __global__ __launch_bounds__(512, 1) void k_fwd(Args a) {
 hipError_t launch_forward(const Args& a, hipStream_t st) {
   const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
   const bool exact = (a.flags & VC_EXACT_SCORES) != 0, v4 = (a.flags & VC_V4) != 0;
-  if (exact && v4)
-    hipLaunchKernelGGL((k_fwd<true, true>), dim3(tiles), dim3(512), 0, st, a);
-  else if (exact)
-    hipLaunchKernelGGL((k_fwd<true, false>), dim3(tiles), dim3(512), 0, st, a);
-  else if (v4)
-    hipLaunchKernelGGL((k_fwd<false, true>), dim3(tiles), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_fwd<false, false>), dim3(tiles), dim3(512), 0, st, a);
+  const bool sq = (a.flags & VC_SMOOTH_Q) != 0;
+  const dim3 grid(tiles), block(512);
+  switch ((exact ? 4 : 0) | (v4 ? 2 : 0) | (sq ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((k_fwd<false, false, false>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_fwd<false, false, true>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_fwd<false, true, false>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_fwd<false, true, true>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_fwd<true, false, false>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_fwd<true, false, true>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_fwd<true, true, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_fwd<true, true, true>), grid, block, 0, st, a); break;
+  }
   return hipGetLastError();
 }
 

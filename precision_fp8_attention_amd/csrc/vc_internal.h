@@ -23,6 +23,7 @@ constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 struct Shape {
   int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
   bool v4;  // 4-bit value residual (VC_V4)
+  bool smooth_q;  // query smoothing (VC_SMOOTH_Q)
 };
 
 // Workspace header (first 256 bytes of the workspace).
@@ -75,6 +76,8 @@ struct Args {
   uint8_t* v8t;
   uint8_t* v4t;  // [BH][nblk][128][64] E2M1 codes (VC_V4)
   uint8_t* v4s;  // [BH*nblk+1][512] E8M0 group exponents (VC_V4)
+  float* qbar;   // [BH][nblk][128] query block means (VC_SMOOTH_Q)
+  float* qbias;  // [BH][nblk][Npad] score term of query block b, key j (VC_SMOOTH_Q)
   float* err;
   int* rep_pos;
   uint16_t* rep_dt;

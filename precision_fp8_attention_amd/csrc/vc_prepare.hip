@@ -529,19 +529,23 @@ __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
 
 // ---------------------------------------------------------------------------
 // Per-block E4M3 codes of Q (z = 0) and smoothed K (z = 1), and for K the bf16
-// copy of the codes.  grid (nblk, BH, 2), 256 threads: thread = (8-channel
-// chunk t%16, rows t/16 + 16i), so 16 threads cover one 256-byte row.
+// copy of the codes.  With VC_SMOOTH_Q a Q block first subtracts its channel
+// mean (exact fixed-point sum, as for the V block means), which is kept.
+// grid (nblk, BH, 2), 256 threads: thread = (8-channel chunk t%16, rows
+// t/16 + 16i), so 16 threads cover one 256-byte row.
 __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
   __shared__ float wmax[4];
+  __shared__ long long qsum[16][D];
+  __shared__ float qmean[D];
   const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z, t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
   const bool follow = isk || (a.flags & VC_PERMUTE_Q);
+  const bool smooth = !isk && (a.flags & VC_SMOOTH_Q);  // uniform over the workgroup
   const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
   float kb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) kb[i] = isk ? a.kbar[(size_t)bh * D + cg * 8 + i] : 0.0f;
   float x[8][8];
-  float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = blk * BLK + r0 + 16 * i;
@@ -554,13 +558,43 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
         float val = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
         if (isk) val = val - kb[e];
         x[i][e] = val;
-        amax = fmaxf(amax, fabsf(val));
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
     }
   }
+  if (smooth) {
+    const int n = min(BLK, a.N - blk * BLK);
+    double sm[8];  // 8 rows per thread: exact in fp64 (see fx24d)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm[e] += fx24d(x[i][e]);  // rows past N hold 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qsum[r0][cg * 8 + e] = (long long)sm[e];
+    __syncthreads();
+    if (t < D) {
+      long long tot = 0;
+      for (int rr = 0; rr < 16; ++rr) tot += qsum[rr][t];
+      qmean[t] = fixed_mean(tot, n);
+      a.qbar[((size_t)bh * a.nblk + blk) * D + t] = qmean[t];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (blk * BLK + r0 + 16 * i < a.N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - qmean[cg * 8 + e];
+      }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   amax = wave_max(amax);
   if ((t & 63) == 0) wmax[t >> 6] = amax;
   __syncthreads();
@@ -591,6 +625,82 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
     }
   }
   if (t == 0) (isk ? a.sk : a.sq)[(size_t)bh * a.nblk + blk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Score term of the smoothed queries (VC_SMOOTH_Q): for every query block b and
+// key position p, d = fp32(c0 * delta) with delta the fp32 fma chain over
+// channels 0..127 of qbar_b[c] * (k[c] - kbar[c]), the same fp32 values the K
+// codes are made from; 0 for positions past N.  A product of a (nblk x 128) and
+// a (128 x Npad) matrix whose every output accumulates in channel order, so it
+// runs on VALU fma, register-tiled: a workgroup computes 16 query blocks x 256
+// keys, each thread 4 x 4 outputs; 32 channels at a time pass through LDS
+// (k - kbar channel-major, the means channel-major), and per channel a thread
+// reads two float4 and issues 16 fma.  grid (ceil(nblk/16), ceil(Npad/256), BH),
+// 256 threads; the block groups of one key tile are neighbours, so the key rows
+// are fetched from HBM about once.
+__global__ __launch_bounds__(256) void k_qbias(Args a) {
+  constexpr int QB = 16, KT = 256, CC = 32;
+  __shared__ __align__(16) float skt[CC][KT];  // k - kbar, [channel][key]
+  __shared__ __align__(16) float sqm[CC][QB];  // qbar, [channel][block]
+  const int bh = blockIdx.z, t = threadIdx.x;
+  const int b0 = blockIdx.x * QB, nb = min(QB, a.nblk - b0);
+  const int p0 = blockIdx.y * KT;
+  const int bq = t >> 6, kq = t & 63;  // outputs: blocks 4bq..4bq+3, keys 4kq..4kq+3
+  // loader role: key p0 + t of the tile
+  const int pl = p0 + t;
+  const bool vl = pl < a.N;
+  const uint4* row = reinterpret_cast<const uint4*>(a.k + ((size_t)bh * a.N + (vl ? a.perm[(size_t)bh * a.N + pl] : 0)) * D);
+  const float* kbar = a.kbar + (size_t)bh * D;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+#pragma unroll 1
+  for (int c0 = 0; c0 < D; c0 += CC) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CC / 8; ++i) {
+      const uint4 u = row[c0 / 8 + i];
+      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * i + e;
+        skt[c][t] = vl ? bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]) - kbar[c0 + c] : 0.0f;
+      }
+    }
+    for (int j = t; j < CC * QB; j += 256) {
+      const int c = j / QB, bb = j % QB;
+      sqm[c][bb] = bb < nb ? a.qbar[((size_t)bh * a.nblk + b0 + bb) * D + c0 + c] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < CC; ++c) {
+      const float4 qv = *reinterpret_cast<const float4*>(&sqm[c][4 * bq]);
+      const float4 kv = *reinterpret_cast<const float4*>(&skt[c][4 * kq]);
+      const float qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(qa[i], ka[j], acc[i][j]);
+    }
+  }
+  const int pk = p0 + 4 * kq;
+  if (pk < a.Npad) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * bq + i;
+      if (b < nb) {
+        float4 o;
+        o.x = pk + 0 < a.N ? a.c0 * acc[i][0] : 0.0f;
+        o.y = pk + 1 < a.N ? a.c0 * acc[i][1] : 0.0f;
+        o.z = pk + 2 < a.N ? a.c0 * acc[i][2] : 0.0f;
+        o.w = pk + 3 < a.N ? a.c0 * acc[i][3] : 0.0f;
+        *reinterpret_cast<float4*>(a.qbias + ((size_t)bh * a.nblk + b0 + b) * a.Npad + pk) = o;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1055,6 +1165,8 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
     hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 0u);
   }
   hipLaunchKernelGGL(k_qk_quant, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
+  if (a.flags & VC_SMOOTH_Q)
+    hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 15) / 16, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);

@@ -29,7 +29,7 @@ def oracle_params(p) -> orc.Params:
     return orc.make_params(p.B, p.H, p.N, C_=p.n_clusters, T=p.kmeans_iters, seed=p.seed,
                            rho=p.rho, sm_scale=p.sm_scale, expcast_k=p.expcast_k, tau=p.tau,
                            flags=p.flags & (vc.VSMOOTH | vc.REPAIR | vc.PERMUTE_Q |
-                                            vc.EXACT_SCORES | vc.WARM_START | vc.V4))
+                                            vc.EXACT_SCORES | vc.WARM_START | vc.V4 | vc.SMOOTH_Q))
 
 
 def to_device(q, k, v):
@@ -106,6 +106,9 @@ def read_prepared(p, ws, heads) -> dict:
         v8t = arr("v8t", np.uint8, (BH, 128, npad))
         cols = (np.arange(npad) // 128) * 128 + _v_col(np.arange(npad) % 128)
         out["v8"] = np.ascontiguousarray(v8t[:, :, cols].transpose(0, 2, 1))
+    if p.flags & vc.SMOOTH_Q:
+        out["qbar"] = arr("qbar", np.float32, (BH, nblk, 128))
+        out["qbias"] = arr("qbias", np.float32, (BH, nblk, npad))
     if m > 0:
         out["rep_pos"] = arr("rep_pos", np.int32, (BH, mpad))[:, :m]
         dt = arr("rep_dt", np.uint16, (BH, 128, mpad))
@@ -124,7 +127,7 @@ def compare_prepared(gpu: dict, ora: dict, vsmooth: bool) -> list[str]:
     """Names of arrays that are not bit-identical (with mismatch counts)."""
     bad = []
     m = gpu["m"]
-    keys = EXACT_KEYS + (("vexp",) if "vexp" in gpu else ())
+    keys = EXACT_KEYS + tuple(k for k in ("vexp", "qbar", "qbias") if k in gpu)
     for key in keys:
         if key in ("labels", "centroids") and not vsmooth:
             continue

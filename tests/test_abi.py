@@ -53,7 +53,7 @@ BAD = [
     (dict(tau=7.0), vc.ERR_INVALID_ARG),
     (dict(expcast_k=0, tau=71.0), vc.ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), vc.ERR_INVALID_ARG),
-    (dict(flags=128), vc.ERR_INVALID_ARG),
+    (dict(flags=256), vc.ERR_INVALID_ARG),
     (dict(flags=vc.WARM_START | vc.REPAIR), vc.ERR_INVALID_ARG),  # warm start needs V-Smooth
     (dict(flags=vc.DEFAULT_FLAGS | vc.WARM_START | vc.REUSE_CLUSTERS), vc.ERR_INVALID_ARG),
 ]
@@ -94,13 +94,14 @@ def test_pointer_and_workspace_errors_before_device_work():
     assert L.vc_attn_forward_pcodes(C.byref(bad), fake, need, fake, None, None) == vc.ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("v4", [False, True], ids=["e4m3_v", "v4"])
+@pytest.mark.parametrize("v4,sq", [(False, False), (True, False), (False, True), (True, True)],
+                         ids=["e4m3_v", "v4", "smooth_q", "v4_smooth_q"])
 @pytest.mark.parametrize("B,H,N,C_,rho", [(1, 2, 1024, 8, 0.005), (2, 24, 16544, 32, 0.005),
                                           (1, 40, 75600, 64, 0.005), (1, 1, 1, 1, 1.0),
                                           (1, 3, 300, 5, 0.0)])
-def test_layout_aligned_and_disjoint(B, H, N, C_, rho, v4):
+def test_layout_aligned_and_disjoint(B, H, N, C_, rho, v4, sq):
     p = vc.default_params(B, H, N, n_clusters=C_, rho=rho,
-                          flags=vc.DEFAULT_FLAGS | (vc.V4 if v4 else 0))
+                          flags=vc.DEFAULT_FLAGS | (vc.V4 if v4 else 0) | (vc.SMOOTH_Q if sq else 0))
     L = vc.workspace_layout(p)
     BH, nblk = B * H, (N + 127) // 128
     npad = nblk * 128
@@ -113,7 +114,8 @@ def test_layout_aligned_and_disjoint(B, H, N, C_, rho, v4):
                  mupt=BH * (-(-nblk // 16)) * 8192, sv=BH * 512,
                  inv=BH * 512, v8t=0 if v4 else BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,
                  rep_dt=BH * 128 * mpad * 2, v4t=BH * nblk * 8192 if v4 else 0,
-                 v4s=(BH * nblk + 1) * 512 if v4 else 0)
+                 v4s=(BH * nblk + 1) * 512 if v4 else 0, qbar=BH * nblk * 512 if sq else 0,
+                 qbias=BH * nblk * npad * 4 if sq else 0)
     spans = sorted((L[k], L[k] + n, k) for k, n in sizes.items())
     for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
         assert a1 <= b0, (ka, kb)

@@ -66,6 +66,14 @@ SMALL = [
     ("v4_vsmooth_off", 1, 2, 700, 4, dict(flags=64)),
     ("v4_repair_all", 1, 1, 260, 3, dict(rho=1.0, flags=1 | 2 | 4 | 64)),
     ("v4_exact_scores", 2, 2, 300, 5, dict(flags=1 | 2 | 4 | 16 | 64)),
+    # smoothed queries (per-block query means, per-key score term)
+    ("sq_one_token", 1, 1, 1, 1, dict(flags=1 | 2 | 4 | 128)),
+    ("sq_ragged_tail", 2, 2, 300, 5, dict(rho=0.05, flags=1 | 2 | 4 | 128)),
+    ("sq_several_tiles", 1, 3, 1000, 8, dict(flags=1 | 2 | 4 | 128)),
+    ("sq_q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2 | 128)),
+    ("sq_exact_scores", 2, 2, 300, 5, dict(flags=1 | 2 | 4 | 16 | 128)),
+    ("sq_v4", 1, 2, 520, 4, dict(rho=0.02, flags=1 | 2 | 4 | 64 | 128)),
+    ("sq_lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0, flags=1 | 2 | 4 | 128)),
 ]
 
 
@@ -151,6 +159,42 @@ def test_workloads_sampled(cfg, heads, nrows):
     p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
     rows = G.sample_rows(wl["N"], nrows, seed=cfg)
     _full_case(p, q, k, v, heads, rows, f"workload{cfg}")
+
+
+def _offset_queries(q, off, seed):
+    """Queries with a per-(head, channel) mean offset, the regime query
+    smoothing is for."""
+    rng = np.random.default_rng(seed)
+    B, H = q.shape[:2]
+    qf = inputs.bf16_bits_to_f32(q) + np.float32(off) * rng.standard_normal((B, H, 1, 128)).astype(np.float32)
+    return inputs.to_bf16_bits(qf)
+
+
+def test_smooth_q_offset_queries_all_rows():
+    """Queries with a mean offset of 4: every prepare array bit-exact, every row
+    within the bar, and closer to exact attention than without smoothing."""
+    import precision_fp8_attention_amd as vc
+    q, k, v = inputs.make_custom(1, 2, 1000, seed=31, rate=0.01, sigma=20.0)
+    q = _offset_queries(q, 4.0, 31)
+    rows = np.arange(1000, dtype=np.int32)
+    res = {}
+    for name, flags in (("plain", vc.DEFAULT_FLAGS), ("smooth", vc.DEFAULT_FLAGS | vc.SMOOTH_Q)):
+        p = G.lib_params(1, 2, 1000, 8, flags=flags)
+        res[name] = _full_case(p, q, k, v, [0, 1], rows, f"offset_queries_{name}")
+    assert res["smooth"]["rel_l2_exact"] < 0.7 * res["plain"]["rel_l2_exact"], res
+
+
+def test_workload3_smooth_q_sampled():
+    """The 2048x2048 CFG workload with smoothed queries, all 48 heads on the GPU,
+    two heads compared (prepare bit-exact, including the 130 x 16640 score
+    terms per head)."""
+    import precision_fp8_attention_amd as vc
+    wl = inputs.WORKLOADS[3]
+    q, k, v = inputs.make_inputs(3)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"],
+                     flags=vc.DEFAULT_FLAGS | vc.SMOOTH_Q)
+    rows = G.sample_rows(wl["N"], 128, seed=43)
+    _full_case(p, q, k, v, [0, 47], rows, "workload3_smooth_q")
 
 
 def test_workload3_v4_sampled():
@@ -244,6 +288,8 @@ PCODE_CASES = [
     ("q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2)),
     ("lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0)),
     ("literal_56", 1, 1, 520, 4, dict(expcast_k=0)),
+    ("smooth_q", 1, 2, 300, 5, dict(flags=1 | 2 | 4 | 128)),
+    ("smooth_q_exact_tau6", 1, 2, 520, 4, dict(tau=6.0, flags=1 | 2 | 4 | 16 | 128)),
 ]
 
 

@@ -281,6 +281,16 @@ template <bool EXACT, int NS> struct QOp;
 template <int NS> struct QOp<true, NS> { v8bf v[NS][4]; };
 template <int NS> struct QOp<false, NS> { v8i v[NS]; };
 
+// V operands of one key block read from LDS before its softmax, so that their
+// latency hides behind the VALU work and P.V issues without LDS waits: four of
+// the eight E4M3 channel tiles (all eight push the kernel past 256 VGPRs and
+// spill), or all eight 4-bit tiles (4 VGPRs each) with the exponents.  Not in
+// exact-score mode, whose bf16 K operands leave no room for them.
+constexpr int VPRE8 = 4;
+template <bool V4> struct VPre;
+template <> struct VPre<false> { v8i t[VPRE8]; };
+template <> struct VPre<true> { uint4 t[8]; uint2 sc; };
+
 template <bool EXACT, bool V4, bool SQ, int NS>
 __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
   // NS 16-query subtiles per wave: 16 / NS waves cover the workgroup's two
@@ -447,13 +457,16 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
     const float alpha = (sQa * sk[kb]) * a.c0;
     const int nvalid = a.N - kb * BLK;
     if (nvalid < BLK) {
+      // key 16t + 4g + v is past N when 16t + v >= nvalid - 4g: one register
+      // per lane instead of 32 key indices held through the key loop
+      const int lim = nvalid - 4 * g;
 #pragma unroll
       for (int qs = 0; qs < NS; ++qs)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (16 * t + 4 * g + v >= nvalid) S[qs][t][v] = -INFINITY;
+            if (16 * t + v >= lim) S[qs][t][v] = -INFINITY;
     }
     // smoothed queries already hold t in code units: fma(t, 1, beta) = t + beta
 #pragma unroll
@@ -472,7 +485,27 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
     }
   };
   // row sums (ones MFMA), P.V (FP8 MFMA) and the 16-block restore of one block
-  auto pv = [&](int kb, const v8i (&pop)[NS]) {
+  constexpr bool PRE = !EXACT;
+  auto read_v = [&](int kb, VPre<V4>& vp) {
+    const uint8_t* Vs = vsm[kb % NST];
+    if constexpr (!PRE) {
+      (void)Vs;
+      (void)vp;
+    } else if constexpr (V4) {
+      // lane (g, i) holds the E8M0 exponents of channel 16ct + i, group g for
+      // ct = 0..7: byte ct&3 of dword ct/4
+      vp.sc = *reinterpret_cast<const uint2*>(ssm[kb % NST] + 8 * lane);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const int row = 16 * ct + l16;
+        vp.t[ct] = *reinterpret_cast<const uint4*>(Vs + row * (BLK / 2) + ((g ^ v4_swz(row)) << 4));
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < VPRE8; ++ct) vp.t[ct] = lds_row32(Vs, 16 * ct + l16, g);
+    }
+  };
+  auto pv = [&](int kb, const v8i (&pop)[NS], const VPre<V4>& vp) {
     const uint8_t* Vs = vsm[kb % NST];
     // ones in A row kb%16: the block's row sum accumulates in L element v of
     // lane group g where 4g+v = kb%16
@@ -484,13 +517,11 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
 #pragma unroll
     for (int qs = 0; qs < NS; ++qs) rs[qs].L = mfma_f8(onesop, pop[qs], rs[qs].L);
     if constexpr (V4) {
-      // lane (g, i) holds the E8M0 exponents of channel 16ct + i, group g for
-      // ct = 0..7: byte ct&3 of dword ct/4
-      const uint2 sc = *reinterpret_cast<const uint2*>(ssm[kb % NST] + 8 * lane);
+      const uint2 sc = PRE ? vp.sc : *reinterpret_cast<const uint2*>(ssm[kb % NST] + 8 * lane);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
         const int row = 16 * ct + l16;
-        const uint4 c4 = *reinterpret_cast<const uint4*>(Vs + row * (BLK / 2) + ((g ^ v4_swz(row)) << 4));
+        const uint4 c4 = PRE ? vp.t[ct] : *reinterpret_cast<const uint4*>(Vs + row * (BLK / 2) + ((g ^ v4_swz(row)) << 4));
         v8i vop;
         vop[0] = (int)c4.x; vop[1] = (int)c4.y; vop[2] = (int)c4.z; vop[3] = (int)c4.w;
         vop[4] = 0; vop[5] = 0; vop[6] = 0; vop[7] = 0;
@@ -501,7 +532,7 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
     } else {
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const v8i vop = lds_row32(Vs, 16 * ct + l16, g);
+        const v8i vop = PRE && ct < VPRE8 ? vp.t[ct < VPRE8 ? ct : 0] : lds_row32(Vs, 16 * ct + l16, g);
 #pragma unroll
         for (int qs = 0; qs < NS; ++qs) rs[qs].acc[ct] = mfma_f8(vop, pop[qs], rs[qs].acc[ct]);
       }
@@ -531,16 +562,20 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
       {
         v4f S[NS][8];
         v8i pop[NS];
+        VPre<V4> vp;
         qk(kb, S);
+        read_v(kb, vp);
         soft(kb, S, pop);
-        pv(kb, pop);
+        pv(kb, pop, vp);
       }
       if (kb + 1 < a.nblk) {
         v4f S[NS][8];
         v8i pop[NS];
+        VPre<V4> vp;
         qk(kb + 1, S);
+        read_v(kb + 1, vp);
         soft(kb + 1, S, pop);
-        pv(kb + 1, pop);
+        pv(kb + 1, pop, vp);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -553,9 +588,11 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
       if (kb + 1 < a.nblk) issue(kb + 1);
       v4f S[NS][8];
       v8i pop[NS];
+      VPre<V4> vp;
       qk(kb, S);
+      read_v(kb, vp);
       soft(kb, S, pop);
-      pv(kb, pop);
+      pv(kb, pop, vp);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }

@@ -44,6 +44,20 @@ def _events_ms(fn, n):
     return e0.elapsed_time(e1) / n
 
 
+def _events_each_ms(fn, n):
+    """Duration of each of n calls, every one bracketed by its own pair of HIP
+    events on the current stream."""
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(s)
+        fn()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
 def _traffic(launches_per_step: int):
     """HBM bytes per forward launch from the committed rocprofv3 counter summary,
     or None when it is missing or the kernel source changed since."""
@@ -201,6 +215,7 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     ms_fwd = _events_ms(lambda: vc.forward(p, ws, o), max(args.steps, 10))
+    fwd_each = sorted(_events_each_ms(lambda: vc.forward(p, ws, o), max(args.steps, 20)))
     ms_prep = _events_ms(lambda: vc.prepare(p, qd, kd, vd, ws), max(args.steps // 2, 5))
     preuse = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
                                flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
@@ -243,6 +258,7 @@ def main():
     vc.forward(p, ws, o)
     torch.cuda.synchronize()
 
+    props = torch.cuda.get_device_properties(0)
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
     traffic = _traffic(1)
@@ -265,12 +281,16 @@ def main():
         "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 3),
         "forward_ms": round(ms_fwd, 4),
         "forward_tflops": round(fwd_tflops, 3),
+        "forward_ms_each": {"launches": len(fwd_each), "median": round(float(np.median(fwd_each)), 4),
+                            "min": round(fwd_each[0], 4), "max": round(fwd_each[-1], 4)},
         "prepare_ms": round(ms_prep, 4),
         "prepare_reuse_clusters_ms": round(ms_reuse, 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "denoise_schedule": sched,
         "v4_residual": v4,
         "smooth_q": smq,
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "fp8_peak_at_2p4ghz_tflops": round(props.multi_processor_count * 2.4e9 * 8192 / 1e12, 1)},
         "roofline": {"bound": "mfma", "kernel": "k_fwd", "achieved": round(fwd_tflops, 3),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 5),

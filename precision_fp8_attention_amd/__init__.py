@@ -53,6 +53,12 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m precision_fp8_attention_amd.build`")
+        # torch ships its own HIP runtime, which its libraries request as
+        # libamdhip64.so; the library asks for the SONAME libamdhip64.so.7 and binds
+        # to torch's copy only if that is loaded first.  Loaded the other way round
+        # the process holds two runtimes, and the library's own (which does not own
+        # torch's streams or allocations) fails every launch.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         P = C.POINTER(Params)
         L.vc_attn_default_params.argtypes = [P]

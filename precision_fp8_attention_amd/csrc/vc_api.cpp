@@ -239,6 +239,9 @@ vc_status vc_attn_prepare(const vc_attn_params* p, const void* q, const void* k,
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   const ClusterMode mode = reuse ? ClusterMode::Reuse : (warm ? ClusterMode::Warm : ClusterMode::Cold);
+  // the launches are checked with hipGetLastError, which also returns an error an
+  // earlier runtime call of this thread (the caller's) left behind: drop it first
+  (void)hipGetLastError();
   return launch_prepare(a, mode, hs) == hipSuccess ? VC_OK : VC_ERR_HIP;
 }
 
@@ -255,6 +258,7 @@ static vc_status forward_impl(const vc_attn_params* p, const void* workspace, si
   Args a = make_args(p, s, L, const_cast<void*>(workspace));
   a.o = static_cast<uint16_t*>(o);
   a.pcodes = pcodes;
+  (void)hipGetLastError();  // as in prepare: report only this call's launches
   return launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? VC_OK : VC_ERR_HIP;
 }
 

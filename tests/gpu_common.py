@@ -161,8 +161,16 @@ def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
     return r.astype(np.int32)
 
 
-def check_output(p, q, k, v, o_gpu, heads, rows, prep_oracle=None, label=""):
-    """Compare GPU output rows with the oracle's simulation (and report exact)."""
+BF16_STEP = 2.0 ** -7  # one bf16 step of |x| is at most 2^-7 |x| (7 stored mantissa bits)
+
+
+def check_output(p, q, k, v, o_gpu, heads, rows, prep_oracle=None, label="", bf16_step=False):
+    """Compare GPU output rows with the oracle's simulation (and report exact).
+
+    O is returned in bf16, whose rounding alone is up to half a step, 2^-8 |O|:
+    above |O| ~ 2.5 that exceeds the max-abs bar by itself.  With bf16_step the
+    bar applies to what lies beyond one bf16 step of |O| (the GPU's fp32 value and
+    the fp64 simulation may round to neighbouring bf16 values)."""
     P = oracle_params(p)
     if prep_oracle is None:
         prep_oracle = orc.prepare(P, q, k, v, heads=heads)
@@ -173,9 +181,10 @@ def check_output(p, q, k, v, o_gpu, heads, rows, prep_oracle=None, label=""):
     og = out_f64(o_gpu).reshape(p.B * p.H, p.N, 128)[ghead, idx]
     ex = orc.exact_rows(P, q, k, v, ghead, idx)
     res = dict(max_abs=float(np.max(np.abs(og - sim))), rel_l2=rel_l2(og, sim),
-               rel_l2_exact=rel_l2(og, ex), sim_rel_l2_exact=rel_l2(sim, ex))
+               rel_l2_exact=rel_l2(og, ex), sim_rel_l2_exact=rel_l2(sim, ex),
+               max_abs_beyond_bf16_step=float(np.max(np.abs(og - sim) - BF16_STEP * np.abs(sim))))
     log(f"{label} output vs oracle: {res}")
     assert np.all(np.isfinite(og))
-    assert res["max_abs"] <= ATOL, res
+    assert (res["max_abs_beyond_bf16_step"] if bf16_step else res["max_abs"]) <= ATOL, res
     assert res["rel_l2"] <= RTOL_L2, res
     return res

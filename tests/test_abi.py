@@ -150,3 +150,18 @@ def test_v4_code_bytes_meet_their_own_p_bytes():
         assert FP4_K[g][d] + n == kappa, k
         seen.add((b, k & 1))
     assert len(seen) == 128
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loading the library through the binding before torch is imported must not
+    bring a second HIP runtime into the process (torch's libraries request the
+    runtime under another file name; two runtimes leave the library with no
+    device and fail every launch).  Checked in a fresh process, no GPU needed."""
+    import subprocess
+    import sys
+    code = ("import precision_fp8_attention_amd as vc; vc.lib(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1", r.stdout

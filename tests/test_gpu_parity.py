@@ -223,6 +223,17 @@ def test_workload4_video_sampled():
 
 # ------------------------------------------------------------------ behaviour
 
+def test_max_tokens_one_head():
+    """The largest token count the ABI accepts, N = 2^20, on one head (8 clusters,
+    2 Lloyd rounds keep the oracle's prepare to ~20 s): every prepare array
+    bit-exact, 16 sampled rows of O within the bar."""
+    N = 1 << 20
+    p = G.lib_params(1, 1, N, 8, T=2)
+    q, k, v = inputs.make_custom(1, 1, N, seed=5)
+    G.log(f"[case] max_tokens: N={N}")
+    _full_case(p, q, k, v, [0], G.sample_rows(N, 16, seed=3), "max_tokens")
+
+
 def test_deterministic_and_reuse_clusters():
     """Two full runs are bit-identical; a prepare that reuses the clusters gives the
     same output as the full prepare; reuse on a fresh workspace is refused."""

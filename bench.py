@@ -227,6 +227,24 @@ def main():
 
     sched = denoise_schedule(p, qd, kd, vd, ws, o, flops)
 
+    # the same step captured once in a HIP graph and replayed (no per-launch host
+    # work); the library issues no memset and no host synchronisation on this path
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(max(args.warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_graph = _events_ms(graph.replay, args.steps)
+    del graph
+
     def variant(extra, name):
         """Step, forward and prepare times of a flag variant on the same workload,
         in its own workspace."""
@@ -287,6 +305,8 @@ def main():
         "prepare_reuse_clusters_ms": round(ms_reuse, 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "denoise_schedule": sched,
+        "graph_replay": {"ms_per_step": round(ms_graph, 4),
+                         "tflops": round(flops / (ms_graph * 1e-3) / 1e12, 3)},
         "v4_residual": v4,
         "smooth_q": smq,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,

@@ -121,9 +121,11 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 __device__ __forceinline__ int v4_group(int r) { return 2 * (r >> 6) + ((r >> 3) & 1); }
 
 // ---------------------------------------------------------------------------
-// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; the same
-// workgroup records max|V| of the chunk (the k-means fixed-point scale).
+// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; with WITH_V
+// the same workgroup records max|V| of the chunk (the k-means fixed-point scale,
+// needed only when k-means runs).
 // grid (nkc, BH), 256 threads: thread = (row r = t/16, 8-channel group t%16).
+template <bool WITH_V>
 __global__ __launch_bounds__(256) void k_ksum(Args a) {
   __shared__ long long red[16][D];
   __shared__ float wm[4];
@@ -139,7 +141,6 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
   for (int i = 0; i < 8; ++i) s[i] = 0.0;
   for (int j = j0 + r; j < j1; j += 16) {
     const uint4 u = *reinterpret_cast<const uint4*>(kh + (size_t)j * D + cg * 8);
-    const uint4 w = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + cg * 8);
     s[0] += fx24d(bf2f(u.x));
     s[1] += fx24d(bf2f(u.x >> 16));
     s[2] += fx24d(bf2f(u.y));
@@ -148,22 +149,27 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
     s[5] += fx24d(bf2f(u.z >> 16));
     s[6] += fx24d(bf2f(u.w));
     s[7] += fx24d(bf2f(u.w >> 16));
-    vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
-                         fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
-    vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
-                         fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
+    if constexpr (WITH_V) {
+      const uint4 w = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + cg * 8);
+      vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
+                           fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
+      vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
+                           fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = (long long)s[i];
-  vm = wave_max(vm);
-  if ((t & 63) == 0) wm[t >> 6] = vm;
+  if constexpr (WITH_V) {
+    vm = wave_max(vm);
+    if ((t & 63) == 0) wm[t >> 6] = vm;
+  }
   __syncthreads();
   if (t < D) {
     long long tot = 0;
     for (int rr = 0; rr < 16; ++rr) tot += red[rr][t];
     a.ksum[((size_t)bh * a.nkc + ch) * D + t] = tot;
   }
-  if (t == 0) a.vmaxp[(size_t)bh * a.nkc + ch] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  if (WITH_V && t == 0) a.vmaxp[(size_t)bh * a.nkc + ch] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
 }
 
 // K channel mean.  grid BH, 128 threads.
@@ -1135,7 +1141,10 @@ __global__ void k_header(Args a, uint32_t clustered) {
 hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
   const unsigned BH = (unsigned)a.BH;
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
-  hipLaunchKernelGGL(k_ksum, dim3(a.nkc, BH), dim3(256), 0, st, a);
+  if (vs && mode != ClusterMode::Reuse)
+    hipLaunchKernelGGL(k_ksum<true>, dim3(a.nkc, BH), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_ksum<false>, dim3(a.nkc, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_kbar, dim3(BH), dim3(128), 0, st, a);
   if (vs) {
     if (mode != ClusterMode::Reuse) {

@@ -52,6 +52,8 @@
 // by direct global->LDS loads while earlier blocks run.
 #include "vc_internal.h"
 
+#include <type_traits>
+
 namespace vc {
 namespace {
 
@@ -291,11 +293,12 @@ template <bool V4> struct VPre;
 template <> struct VPre<false> { v8i t[VPRE8]; };
 template <> struct VPre<true> { uint4 t[8]; uint2 sc; };
 
-template <bool EXACT, bool V4, bool SQ, int NS>
-__global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
-  // NS 16-query subtiles per wave: 16 / NS waves cover the workgroup's two
-  // 128-query blocks, 8 / NS of them per block
-  constexpr int NWV = 16 / NS, NWQ = 8 / NS;
+template <bool EXACT, bool V4, bool SQ, int NS, int QB>
+__global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0) {
+  // NS 16-query subtiles per wave; 8 / NS waves per 128-query block and QB
+  // query blocks per workgroup: two (a tile) in the main launch, one in the
+  // launch that spreads the last tiles over more CUs
+  constexpr int NWV = 8 * QB / NS, NWQ = 8 / NS;
   constexpr int KROW = EXACT ? 2 * D : D;                     // bytes per K row in LDS
   // LDS stages: FP8 mode holds four key blocks (two computed per barrier while
   // the next two land), exact-score mode two (its bf16 K tiles are twice as big)
@@ -315,10 +318,16 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g = lane >> 4, l16 = lane & 15;
   const int npair = (a.nblk + 1) / 2;
+  // workgroup -> tile (head, pair of query blocks), or with QB = 1 -> one query
+  // block of the tiles from tile0 on
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int wg = w / NWQ;           // which of the two query blocks
-  const int bh = logical / npair, qb = 2 * (logical % npair) + wg;
+  const int tile = QB == 2 ? logical : tile0 + logical / 2;
+  const int wg = w / NWQ;           // which of the workgroup's query blocks
+  const int bh = tile / npair;
+  const int qb0 = 2 * (tile % npair) + (QB == 2 ? 0 : (logical & 1));  // first query block
+  const int qb = qb0 + wg;
   const bool active = qb < a.nblk;  // the second block of an odd count is empty
+  if (QB == 1 && !active) return;   // uniform over the workgroup, before any barrier
   const int qbv = active ? qb : qb - 1;
   const int wq = w % NWQ;           // wave within its query block
 
@@ -354,13 +363,18 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
       }
     }
     if constexpr (V4) {
-      // one contiguous 8 KB tile: wave w lands rows 16w..16w+15; wave 0 also the
-      // block's 512 exponent bytes (its 1 KB copy runs into the next record,
-      // which the layout pads at the end)
+      // one contiguous 8 KB tile as eight 1 KB regions of 16 rows, region r from
+      // wave r mod NWV; wave 0 (8 with more than eight waves) also the block's
+      // 512 exponent bytes (its 1 KB copy runs into the next record, which the
+      // layout pads at the end)
       const uint8_t* vt = a.v4t + ((size_t)bh * a.nblk + kb) * V4_TILE;
-      if (w < 8) {
-        const int row = 16 * w + (lane >> 2), cc = (lane & 3) ^ v4_swz(row);
-        dma16(vt + row * (BLK / 2) + cc * 16, vd + w * 1024);
+#pragma unroll
+      for (int i = 0; i < (8 + NWV - 1) / NWV; ++i) {
+        const int r = NWV * i + w;
+        if (r < 8) {
+          const int row = 16 * r + (lane >> 2), cc = (lane & 3) ^ v4_swz(row);
+          dma16(vt + row * (BLK / 2) + cc * 16, vd + r * 1024);
+        }
       }
       if (w == (NWV > 8 ? 8 : 0)) dma16(a.v4s + ((size_t)bh * a.nblk + kb) * V4_SREC + 16 * lane, ssm[kb % NST]);
     } else {
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
       // smoothed queries: the block's 128 score terms of both query blocks
       // (lanes 0-31 the first, 32-63 the second), 1 KB
       if (w == (NWV > 8 ? 9 : 1)) {
-        const int qsel = min(2 * (logical % npair) + (lane >> 5), a.nblk - 1);
+        const int qsel = min(qb0 + (QB == 2 ? (lane >> 5) : 0), a.nblk - 1);
         dma16(a.qbias + ((size_t)bh * a.nblk + qsel) * a.Npad + (size_t)kb * BLK + 4 * (lane & 31), sbias[kb % NST]);
       }
     }
@@ -623,12 +637,12 @@ __global__ __launch_bounds__(64 * (16 / NS), 1) void k_fwd(Args a) {
     if (tid < BLK) {
       const int pos = rp[tid];
       const float sk_pos = sk[pos < 0 ? 0 : pos / BLK];
-      alpha_s[0][tid] = (a.sq[(size_t)bh * a.nblk + 2 * (logical % npair)] * sk_pos) * a.c0;
-      const int qb1 = min(2 * (logical % npair) + 1, a.nblk - 1);
+      alpha_s[0][tid] = (a.sq[(size_t)bh * a.nblk + qb0] * sk_pos) * a.c0;
+      const int qb1 = min(qb0 + 1, a.nblk - 1);
       alpha_s[1][tid] = (a.sq[(size_t)bh * a.nblk + qb1] * sk_pos) * a.c0;
       if constexpr (SQ) {
         const size_t col = (size_t)(pos < 0 ? 0 : pos);
-        dsel_s[0][tid] = a.qbias[((size_t)bh * a.nblk + 2 * (logical % npair)) * a.Npad + col];
+        dsel_s[0][tid] = a.qbias[((size_t)bh * a.nblk + qb0) * a.Npad + col];
         dsel_s[1][tid] = a.qbias[((size_t)bh * a.nblk + qb1) * a.Npad + col];
       }
     }
@@ -705,17 +719,36 @@ hipError_t launch_forward(const Args& a, hipStream_t st) {
   // four per SIMD) caps a wave at 128 VGPRs: it spills in the key loop, reads
   // every K/V tile twice as often, and measured 8% slower.
   constexpr int NS = 2;
-  const dim3 grid(tiles), block(64 * (16 / NS));
-  switch ((exact ? 4 : 0) | (v4 ? 2 : 0) | (sq ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((k_fwd<false, false, false, NS>), grid, block, 0, st, a); break;
-    case 1: hipLaunchKernelGGL((k_fwd<false, false, true, NS>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_fwd<false, true, false, NS>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_fwd<false, true, true, NS>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_fwd<true, false, false, NS>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_fwd<true, false, true, NS>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_fwd<true, true, false, NS>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_fwd<true, true, true, NS>), grid, block, 0, st, a); break;
-  }
+  // A tile workgroup fills its CU (one per CU), so the tiles run in rounds of
+  // one per CU.  Whole rounds run as tiles.  The rest run as one-query-block
+  // workgroups of 8 waves with one 16-query subtile each: half the work per
+  // wave, and a wave's time is set by its own MFMA -> softmax -> MFMA chain
+  // more than by the other wave on its SIMD, so the last partial round takes
+  // about half as long.  The per-row arithmetic is the same in both shapes.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return hipErrorInvalidDevice;
+  const unsigned full = tiles / (unsigned)cus * (unsigned)cus;
+  const unsigned rest = tiles - full;
+  const int variant = (exact ? 4 : 0) | (v4 ? 2 : 0) | (sq ? 1 : 0);
+  auto go = [&](auto qb_tag, auto ns_tag, unsigned nwg) {
+    constexpr int QB = decltype(qb_tag)::value, S = decltype(ns_tag)::value;
+    const dim3 grid(nwg), block(64 * (8 * QB / S));
+    const int tile0 = (int)full;
+    switch (variant) {
+      case 0: hipLaunchKernelGGL((k_fwd<false, false, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 1: hipLaunchKernelGGL((k_fwd<false, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 2: hipLaunchKernelGGL((k_fwd<false, true, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 3: hipLaunchKernelGGL((k_fwd<false, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 4: hipLaunchKernelGGL((k_fwd<true, false, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 5: hipLaunchKernelGGL((k_fwd<true, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 6: hipLaunchKernelGGL((k_fwd<true, true, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      default: hipLaunchKernelGGL((k_fwd<true, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
+    }
+  };
+  if (full > 0) go(std::integral_constant<int, 2>{}, std::integral_constant<int, NS>{}, full);
+  if (rest > 0) go(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, 2 * rest);
   return hipGetLastError();
 }
 

@@ -311,7 +311,8 @@ def main():
         "smooth_q": smq,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "fp8_peak_at_2p4ghz_tflops": round(props.multi_processor_count * 2.4e9 * 8192 / 1e12, 1)},
-        "roofline": {"bound": "mfma", "kernel": "k_fwd", "achieved": round(fwd_tflops, 3),
+        "roofline": {"bound": "mfma", "kernel": "k_fwd (one forward call: tile launch + last-round launch)",
+                     "achieved": round(fwd_tflops, 3),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 5),
                      "traffic": traffic},

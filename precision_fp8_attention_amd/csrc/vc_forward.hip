@@ -14,11 +14,15 @@
 //   after the loop the repaired tokens add P(final M) . delta (bf16 MFMA), and
 //   O = sV * acc / l, written as bf16 to the token's original row.
 //
-// Layout.  A workgroup of 8 waves owns two 128-row query blocks; wave w owns
-// rows 32w..32w+31 as two 16-row subtiles.  Scores are computed transposed
-// (S^T = K . Q^T) so each lane holds 32 keys of one query: key 16t+4g+v of the
-// block in S[t][v], g = lane/16.  Those 32 ExpCast bytes are exactly the lane's
-// B operand of O^T = V8^T . P^T on v_mfma_f32_16x16x128_f8f6f4, because prepare
+// Layout.  A workgroup of 8 waves owns two 128-row query blocks (a tile); wave
+// w owns rows 32w..32w+31 as two 16-row subtiles.  Such a workgroup fills its
+// CU, so tiles run in rounds of one per CU; the tiles past the last whole round
+// run in a second launch as one-query-block workgroups of 8 waves with one
+// 16-row subtile each, which halves the length of that last round.
+//   Scores are computed transposed (S^T = K . Q^T) so each lane holds 32 keys
+// of one query: key 16t+4g+v of the block in S[t][v], g = lane/16.  Those 32
+// ExpCast bytes are exactly the lane's B operand of O^T = V8^T . P^T on
+// v_mfma_f32_16x16x128_f8f6f4, because prepare
 // stores V8 channel-major with the same key interleave: P never touches LDS.
 // v_cvt_pk_u8_f32 rounds to nearest even, saturates to [0, 255] and inserts the
 // byte, so one fma and one convert produce each packed code.

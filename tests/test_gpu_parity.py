@@ -457,3 +457,57 @@ def test_random_sweep(label, B, H, N, C_, kw):
     assert not bad, f"{label}: prepare mismatch: {bad}"
     G.check_output(p, q, k, v, o, heads, G.sample_rows(N, 300, seed=1), prep_oracle=ora, label=label,
                    bf16_step=True)
+
+
+def _warm_cases(n=12, seed=99):
+    """Cold prepare -> drifted V -> warm-started prepare, with random shapes, flag
+    subsets (V-Smooth on), cold and warm Lloyd rounds, repair budgets and drift
+    steps, drawn once from a fixed seed."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.choice([1, 5, 127, 128, 129, 300, 640, 1023, 1500, 2600]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        C_ = int(rng.integers(1, min(N, 64) + 1))
+        flags = 1
+        for f in (2, 4, 16, 64, 128):  # REPAIR PERMUTE_Q EXACT_SCORES V4 SMOOTH_Q
+            if rng.random() < 0.5:
+                flags |= f
+        kw = dict(flags=flags, Tc=int(rng.choice([1, 3, 10])), Tw=int(rng.choice([1, 2, 3, 5])),
+                  rho=float(rng.choice([0.0, 0.005, 0.05, 1.0])), step=int(rng.integers(1, 4)),
+                  seed=int(rng.integers(0, 1 << 30)))
+        cases.append((f"w{i}_B{B}H{H}N{N}C{C_}f{flags}", B, H, N, C_, kw))
+    return cases
+
+
+WARM = _warm_cases()
+
+
+@pytest.mark.parametrize("label,B,H,N,C_,kw", WARM, ids=[c[0] for c in WARM])
+def test_warm_start_sweep(label, B, H, N, C_, kw):
+    """The warm prepare's arrays bit-identical to the oracle's warm start from its
+    own cold centroids; O within the bar (beyond one bf16 step of |O|)."""
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    seed = kw["seed"]
+    q, k, v = inputs.make_custom(B, H, N, seed=seed % 1000)
+    v1 = inputs.drift(v, step=kw["step"], seed=seed % 997)
+    heads = list(range(B * H))
+    pc = G.lib_params(B, H, N, C_, T=kw["Tc"], seed=seed, rho=kw["rho"], flags=kw["flags"])
+    pw = G.lib_params(B, H, N, C_, T=kw["Tw"], seed=seed, rho=kw["rho"], flags=kw["flags"] | vc.WARM_START)
+    G.log(f"[case] {label}: {kw}")
+    qd, kd, vd = G.to_device(q, k, v)
+    vd1 = G.to_device(q, k, v1)[2]
+    ws = vc.alloc_workspace(pc)
+    o = torch.empty_like(qd)
+    vc.prepare(pc, qd, kd, vd, ws)
+    vc.prepare(pw, qd, kd, vd1, ws)
+    vc.forward(pw, ws, o)
+    torch.cuda.synchronize()
+    cold = orc.prepare(G.oracle_params(pc), q, k, v, heads=heads)
+    ora = orc.prepare(G.oracle_params(pw), q, k, v1, heads=heads, init_centroids=cold["centroids"])
+    bad = G.compare_prepared(G.read_prepared(pw, ws, heads), ora, vsmooth=True)
+    assert not bad, f"{label}: warm prepare mismatch: {bad}"
+    G.check_output(pw, q, k, v1, o, heads, G.sample_rows(N, 200, seed=1), prep_oracle=ora, label=label,
+                   bf16_step=True)

@@ -729,8 +729,9 @@ hipError_t launch_forward(const Args& a, hipStream_t st) {
   // wave, and a wave's time is set by its own MFMA -> softmax -> MFMA chain
   // more than by the other wave on its SIMD, so the last partial round takes
   // about half as long.  The per-row arithmetic is the same in both shapes.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
+  hipDevice_t dev = 0;  // the device the stream runs on (the current one for the null stream)
+  int cus = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return hipErrorInvalidDevice;
   const unsigned full = tiles / (unsigned)cus * (unsigned)cus;

@@ -55,7 +55,8 @@ extern "C" {
 typedef enum {
   VC_OK = 0,
   VC_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, out-of-range parameter */
-  VC_ERR_UNSUPPORTED = 2,  /* d != 128 or block != 128 */
+  VC_ERR_UNSUPPORTED = 2,  /* d != 128, block != 128, or VC_SMOOTH_Q with N above
+                              VC_SMOOTH_Q_MAX_TOKENS */
   VC_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
   VC_ERR_NOT_PREPARED = 4, /* VC_REUSE_CLUSTERS / VC_WARM_START without clusters
                               for this shape */
@@ -80,11 +81,22 @@ enum {
                             VC_VSMOOTH, excludes VC_REUSE_CLUSTERS; without
                             clusters of this shape prepare returns
                             VC_ERR_NOT_PREPARED */
-  VC_EXACT_SCORES = 16u, /* QK^T as the exact dot product of the E4M3 codes (bf16
-                            MFMA, twice the matrix-core time) instead of the FP8
-                            MFMA, whose accumulation cuts each product 13 bits below
-                            the largest exponent of its 8-channel group; set the
-                            same flag on prepare and forward */
+  VC_EXACT_SCORES = 16u, /* QK^T as the exact dot product of the E4M3 codes: the
+                            codes multiplied as bf16 (exact) on the bf16 MFMA, twice
+                            the matrix-core time of the FP8 MFMA.  The article's
+                            bottleneck section runs QK^T on FP8 tensor cores; their
+                            accumulation is not exact (gfx950's FP8 MFMA drops the
+                            low bits of products far below the largest one of each
+                            8-channel group), so about 2 ExpCast codes in 10^4 land
+                            one step away from the exact score's code.  One such
+                            step moves O by at most 1/8 of that key's share of the
+                            row sum times |V|, which for rows spread over fewer
+                            than a few thousand keys can exceed 1e-2.  Set the
+                            same score flag on prepare and forward */
+  VC_FP8_SCORES = 256u,  /* QK^T on the FP8 MFMA whatever N is.  Without either
+                            score flag the library takes FP8 scores when N >=
+                            VC_FP8_SCORES_MIN_TOKENS and exact scores below;
+                            setting both flags is VC_ERR_INVALID_ARG */
   VC_V4 = 64u,           /* 4-bit value residual: the article's V-Smooth section
                             offers NVFP4 instead of per-channel E4M3 for the demeaned
                             residual; here it takes the OCP MX form gfx950's scaled
@@ -98,7 +110,7 @@ enum {
                             negative zero).  No per-channel scale (sv = inv = 1),
                             repair deltas in real units, P stays ExpCast E4M3.  Set
                             the same flag on prepare and forward */
-  VC_SMOOTH_Q = 128u     /* query smoothing, the SageAttention2-style smoothing the
+  VC_SMOOTH_Q = 128u,    /* query smoothing, the SageAttention2-style smoothing the
                             article's section on the attention bottleneck names:
                             each 128-position query block subtracts its channel
                             mean qbar_b (exact fixed-point mean) before its codes
@@ -110,9 +122,17 @@ enum {
                             block maximum is taken over t and code = clamp(rne(t +
                             56 + 8k - M), 0, 126).  Costs a prepare pass over
                             nblk x N scores and one more VALU operation per score
-                            in the forward.  Set the same flag on prepare and
-                            forward */
+                            in the forward; the score terms take nblk * Npad * 4
+                            bytes of workspace per (batch, head), so the flag is
+                            VC_ERR_UNSUPPORTED above N = VC_SMOOTH_Q_MAX_TOKENS
+                            (512 MiB per head there).  Set the same flag on
+                            prepare and forward */
 };
+
+/* Token count from which the default score mode is the FP8 MFMA. */
+#define VC_FP8_SCORES_MIN_TOKENS 4096
+/* Largest N accepted with VC_SMOOTH_Q. */
+#define VC_SMOOTH_Q_MAX_TOKENS 131072
 
 typedef struct {
   int32_t B, H, N;       /* batch, heads, tokens; B*H >= 1, 1 <= N <= 2^20 */
@@ -146,8 +166,9 @@ typedef struct {
   size_t q8;         /* u8  [BH][Npad][128] Q codes, position order               */
   size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order      */
   size_t k16;        /* bf16 [BH][Npad][128] the same codes decoded (exact in bf16),
-                        operand of the exact score MFMA; written only with
-                        VC_EXACT_SCORES                                          */
+                        operand of the exact score MFMA; 0 bytes unless the
+                        scores are exact (VC_EXACT_SCORES, or neither score flag
+                        and N < VC_FP8_SCORES_MIN_TOKENS)                        */
   size_t sq;         /* f32 [BH][nblk] Q block scales                            */
   size_t sk;         /* f32 [BH][nblk] K block scales                            */
   size_t mu;         /* f32 [BH][nblk][128] V block means (real units)           */

@@ -26,10 +26,12 @@ LIB = os.path.join(HERE, "libvcoracle.so")
 VSMOOTH = 1
 REPAIR = 2
 PERMUTE_Q = 4
-EXACT_SCORES = 16
 WARM_START = 32
 V4 = 64
 SMOOTH_Q = 128
+# Diagnostic only: raw scores by the probe-fitted model of gfx950's FP8 matrix
+# instruction instead of the exact dot product (the reference reading).
+MFMA_RULE = 256
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
 
 
@@ -67,7 +69,7 @@ def lib():
         L = C.CDLL(LIB)
         vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.oc_prepare.argtypes = [C.POINTER(Params), vp, vp, vp, vp, i32, C.POINTER(_Prep)]
-        L.oc_forward_rows.argtypes = [C.POINTER(Params), C.POINTER(_Prep), vp, vp, i32, vp, vp]
+        L.oc_forward_rows.argtypes = [C.POINTER(Params), C.POINTER(_Prep), vp, vp, i32, vp, vp, vp]
         L.oc_exact_rows.argtypes = [C.POINTER(Params), vp, vp, vp, vp, vp, i32, vp]
         L.oc_e4m3_decode_array.argtypes = [vp, vp, i64]
         L.oc_e4m3_encode_array.argtypes = [vp, vp, i64]
@@ -147,19 +149,26 @@ def prepare(P: Params, q, k, v, heads=None, init_centroids=None) -> dict:
     return out
 
 
-def forward_rows(P: Params, prep: dict, row_slot, row_index, want_pcodes=False):
-    """Simulated outputs (fp64 [n, 128]) of query rows given in ORIGINAL order."""
+def forward_rows(P: Params, prep: dict, row_slot, row_index, want_pcodes=False, want_pvals=False):
+    """Simulated outputs (fp64 [n, 128]) of query rows given in ORIGINAL order.
+
+    want_pcodes adds the rows' ExpCast codes (uint8 [n, Npad], key position
+    order); want_pvals adds the fp32 values those codes round (-inf past N).
+    Returns out, or a tuple (out, pcodes?, pvals?) in that order."""
     row_slot = np.ascontiguousarray(row_slot, np.int32)
     row_index = np.ascontiguousarray(row_index, np.int32)
     n = len(row_index)
     out = np.zeros((n, P.d), np.float64)
     npad = ((P.N + 127) // 128) * 128
     pc = np.zeros((n, npad), np.uint8) if want_pcodes else None
+    pv = np.zeros((n, npad), np.float32) if want_pvals else None
     rc = lib().oc_forward_rows(C.byref(P), C.byref(prep["_struct"]), _ptr(row_slot),
-                               _ptr(row_index), n, _ptr(out), _ptr(pc) if want_pcodes else None)
+                               _ptr(row_index), n, _ptr(out), _ptr(pc) if want_pcodes else None,
+                               _ptr(pv) if want_pvals else None)
     if rc != 0:
         raise ValueError("oracle forward rejected the parameters")
-    return (out, pc) if want_pcodes else out
+    extra = tuple(x for x in (pc, pv) if x is not None)
+    return (out, *extra) if extra else out
 
 
 def exact_rows(P: Params, q, k, v, row_head, row_index):
@@ -225,8 +234,9 @@ def expcast(s, alpha: float, beta: float) -> np.ndarray:
 
 
 def scores(a, b, exact: bool = False) -> np.ndarray:
-    """Raw scores of code rows a[i] . b[i] (uint8 [n, d]): the FP8 matrix-
-    instruction accumulation, or the exact dot product rounded to fp32."""
+    """Raw scores of code rows a[i] . b[i] (uint8 [n, d]): the exact dot product
+    rounded to fp32 (exact=True), or the diagnostic FP8 matrix-instruction
+    model."""
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
     assert a.shape == b.shape and a.ndim == 2 and a.shape[1] % 8 == 0

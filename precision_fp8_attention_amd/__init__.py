@@ -14,7 +14,10 @@ LIB_PATH = os.path.join(PKG, "libvcattn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_PREPARED, ERR_HIP, ERR_INTERNAL = range(7)
 VSMOOTH, REPAIR, PERMUTE_Q, REUSE_CLUSTERS, EXACT_SCORES, WARM_START, V4, SMOOTH_Q = 1, 2, 4, 8, 16, 32, 64, 128
+FP8_SCORES = 256
 DEFAULT_FLAGS = VSMOOTH | REPAIR | PERMUTE_Q
+FP8_SCORES_MIN_TOKENS = 4096   # without a score flag: FP8 scores from this N on
+SMOOTH_Q_MAX_TOKENS = 131072   # largest N accepted with SMOOTH_Q
 
 EXPORTS = ("vc_attn_default_params", "vc_attn_workspace_size", "vc_attn_workspace_layout",
            "vc_attn_check_params", "vc_attn_prepare", "vc_attn_forward", "vc_attn_forward_pcodes",
@@ -121,26 +124,53 @@ def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
 
 
-def _stream(stream) -> int | None:
+def _check(what: str, p: Params, tensors: dict, workspace=None) -> None:
+    """The C ABI takes bare pointers: refuse tensors it would misread (wrong
+    dtype, shape or layout, host memory, mixed devices) before passing them."""
+    import torch
+    dev = None
+    for name, t in tensors.items():
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{what}: {name} must be bfloat16, got {t.dtype}")
+        if tuple(t.shape) != (p.B, p.H, p.N, p.d):
+            raise ValueError(f"{what}: {name} must have shape {(p.B, p.H, p.N, p.d)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: {name} must be contiguous [B, H, N, d]")
+        if t.device.type != "cuda":
+            raise ValueError(f"{what}: {name} must be a GPU tensor")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{what}: {name} is on {t.device}, expected {dev}")
+        dev = t.device
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+            raise ValueError(f"{what}: the workspace must be a contiguous 1-D uint8 tensor")
+        if dev is not None and workspace.device != dev:
+            raise ValueError(f"{what}: the workspace is on {workspace.device}, expected {dev}")
+
+
+def _stream(stream, device) -> int | None:
+    """The given stream, else the current stream of the tensors' device."""
     if stream is not None:
         return int(stream)
     import torch
-    return int(torch.cuda.current_stream().cuda_stream)
+    return int(torch.cuda.current_stream(device).cuda_stream)
 
 
 def prepare(p: Params, q, k, v, workspace, stream=None) -> None:
     """vc_attn_prepare on torch device tensors (bf16 [B,H,N,128], uint8 workspace)."""
+    _check("prepare", p, dict(q=q, k=k, v=v), workspace)
     st = lib().vc_attn_prepare(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream))
+                               workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     if st != OK:
         raise VCError(st, "vc_attn_prepare")
 
 
 def forward(p: Params, workspace, o, stream=None) -> None:
     """vc_attn_forward: writes o (bf16 [B,H,N,128], original token order)."""
+    _check("forward", p, dict(o=o), workspace)
     st = lib().vc_attn_forward(C.byref(p), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(o),
-                               _stream(stream))
+                               _stream(stream, o.device))
     if st != OK:
         raise VCError(st, "vc_attn_forward")
 
@@ -148,9 +178,16 @@ def forward(p: Params, workspace, o, stream=None) -> None:
 def forward_pcodes(p: Params, workspace, o, pcodes, stream=None) -> None:
     """vc_attn_forward_pcodes: forward plus every ExpCast byte of the main loop in
     pcodes (uint8 [B*H, Npad, Npad], processing order)."""
+    import torch
+    _check("forward_pcodes", p, dict(o=o), workspace)
+    npad = ((p.N + 127) // 128) * 128
+    if (pcodes.dtype != torch.uint8 or not pcodes.is_contiguous() or pcodes.device != o.device
+            or pcodes.numel() < p.B * p.H * npad * npad):
+        raise ValueError("forward_pcodes: pcodes must be a contiguous uint8 GPU tensor of "
+                         f"at least B*H*Npad*Npad = {p.B * p.H * npad * npad} bytes on {o.device}")
     st = lib().vc_attn_forward_pcodes(C.byref(p), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _ptr(o),
-                                      _ptr(pcodes), _stream(stream))
+                                      _ptr(pcodes), _stream(stream, o.device))
     if st != OK:
         raise VCError(st, "vc_attn_forward_pcodes")
 

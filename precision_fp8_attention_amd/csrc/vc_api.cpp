@@ -28,8 +28,11 @@ static vc_status check(const vc_attn_params* p) {
   if (!std::isfinite(p->sm_scale)) return VC_ERR_INVALID_ARG;
   if (!(p->tau >= 0.0f) || 56.0f + 8.0f * p->expcast_k + p->tau > 126.0f) return VC_ERR_INVALID_ARG;
   if (p->flags & ~(uint32_t)(VC_VSMOOTH | VC_REPAIR | VC_PERMUTE_Q | VC_REUSE_CLUSTERS |
-                         VC_EXACT_SCORES | VC_WARM_START | VC_V4 | VC_SMOOTH_Q))
+                         VC_EXACT_SCORES | VC_WARM_START | VC_V4 | VC_SMOOTH_Q | VC_FP8_SCORES))
     return VC_ERR_INVALID_ARG;
+  if ((p->flags & VC_EXACT_SCORES) && (p->flags & VC_FP8_SCORES)) return VC_ERR_INVALID_ARG;
+  // the smoothed-query score terms are nblk x Npad per head
+  if ((p->flags & VC_SMOOTH_Q) && p->N > VC_SMOOTH_Q_MAX_TOKENS) return VC_ERR_UNSUPPORTED;
   if ((p->flags & VC_WARM_START) && (!(p->flags & VC_VSMOOTH) || (p->flags & VC_REUSE_CLUSTERS)))
     return VC_ERR_INVALID_ARG;
   return VC_OK;
@@ -52,7 +55,14 @@ bool shape_of(const vc_attn_params* p, Shape* s) {
   s->nch16 = (s->nblk + 15) / 16;
   s->v4 = (p->flags & VC_V4) != 0;
   s->smooth_q = (p->flags & VC_SMOOTH_Q) != 0;
+  s->exact = exact_scores(p);
   return true;
+}
+
+bool exact_scores(const vc_attn_params* p) {
+  if (p->flags & VC_EXACT_SCORES) return true;
+  if (p->flags & VC_FP8_SCORES) return false;
+  return p->N < VC_FP8_SCORES_MIN_TOKENS;
 }
 
 void layout_of(const Shape& s, FullLayout* out) {
@@ -83,7 +93,7 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.iperm = take(BH * N * 4);
   L.q8 = take(BH * Np * D);
   L.k8 = take(BH * Np * D);
-  L.k16 = take(BH * Np * D * 2);
+  L.k16 = take(s.exact ? BH * Np * D * 2 : 0);
   L.sq = take(BH * nb * 4);
   L.sk = take(BH * nb * 4);
   L.mu = take(BH * nb * D * 4);
@@ -121,7 +131,8 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.nkc = s.nkc;
   a.nkm = s.nkm;
   a.nch16 = s.nch16;
-  a.flags = p->flags;
+  // the kernels see the score mode resolved: VC_EXACT_SCORES set or clear
+  a.flags = (p->flags & ~(uint32_t)(VC_EXACT_SCORES | VC_FP8_SCORES)) | (s.exact ? VC_EXACT_SCORES : 0u);
   a.seed = p->seed;
   const float scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)D));
   a.c0 = (float)(8.0 * 1.4426950408889634074 * (double)scale);
@@ -289,6 +300,6 @@ const char* vc_attn_status_string(vc_status s) {
   return "unknown status";
 }
 
-int32_t vc_attn_version(void) { return 102; }
+int32_t vc_attn_version(void) { return 200; }
 
 }  // extern "C"

@@ -24,7 +24,11 @@ struct Shape {
   int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
   bool v4;  // 4-bit value residual (VC_V4)
   bool smooth_q;  // query smoothing (VC_SMOOTH_Q)
+  bool exact;  // scores as the exact dot product (bf16 MFMA) rather than the FP8 MFMA
 };
+
+// Score mode of a parameter set: VC_EXACT_SCORES, VC_FP8_SCORES, or by N.
+bool exact_scores(const vc_attn_params* p);
 
 // Workspace header (first 256 bytes of the workspace).
 struct Header {
@@ -41,7 +45,7 @@ struct Args {
   const uint16_t* v;
   uint16_t* o;
   int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
-  uint32_t flags;
+  uint32_t flags;  // public flags with the score mode resolved into VC_EXACT_SCORES
   uint64_t seed;
   float c0;    // 8*log2(e)*softmax scale, fp32
   float bias;  // 56 + 8k

@@ -53,7 +53,11 @@ BAD = [
     (dict(tau=7.0), vc.ERR_INVALID_ARG),
     (dict(expcast_k=0, tau=71.0), vc.ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), vc.ERR_INVALID_ARG),
-    (dict(flags=256), vc.ERR_INVALID_ARG),
+    (dict(flags=512), vc.ERR_INVALID_ARG),
+    (dict(flags=vc.DEFAULT_FLAGS | vc.EXACT_SCORES | vc.FP8_SCORES), vc.ERR_INVALID_ARG),
+    # the smoothed-query score terms grow as N^2: refused above the documented bound
+    (dict(N=vc.SMOOTH_Q_MAX_TOKENS + 1, flags=vc.DEFAULT_FLAGS | vc.SMOOTH_Q), vc.ERR_UNSUPPORTED),
+    (dict(N=1 << 20, flags=vc.DEFAULT_FLAGS | vc.SMOOTH_Q), vc.ERR_UNSUPPORTED),
     (dict(flags=vc.WARM_START | vc.REPAIR), vc.ERR_INVALID_ARG),  # warm start needs V-Smooth
     (dict(flags=vc.DEFAULT_FLAGS | vc.WARM_START | vc.REUSE_CLUSTERS), vc.ERR_INVALID_ARG),
 ]
@@ -94,6 +98,46 @@ def test_pointer_and_workspace_errors_before_device_work():
     assert L.vc_attn_forward_pcodes(C.byref(bad), fake, need, fake, None, None) == vc.ERR_UNSUPPORTED
 
 
+def test_smooth_q_accepted_up_to_its_bound():
+    p = vc.default_params(1, 1, vc.SMOOTH_Q_MAX_TOKENS, flags=vc.DEFAULT_FLAGS | vc.SMOOTH_Q)
+    assert vc.check_params(p) == vc.OK
+    L = vc.workspace_layout(p)
+    nblk = vc.SMOOTH_Q_MAX_TOKENS // 128
+    assert L["total"] >= nblk * vc.SMOOTH_Q_MAX_TOKENS * 4  # the score terms, 512 MiB
+
+
+@pytest.mark.parametrize("N,flags,exact", [
+    (1024, 0, True), (vc.FP8_SCORES_MIN_TOKENS - 1, 0, True), (vc.FP8_SCORES_MIN_TOKENS, 0, False),
+    (16544, 0, False), (1024, vc.FP8_SCORES, False), (16544, vc.EXACT_SCORES, True)])
+def test_score_mode_by_flags_and_token_count(N, flags, exact):
+    """Exact scores (bf16 copy of the K codes in the workspace) below the token
+    count where the default turns to FP8 scores, or when asked for."""
+    p = vc.default_params(1, 1, N, flags=vc.DEFAULT_FLAGS | flags)
+    L = vc.workspace_layout(p)
+    npad = -(-N // 128) * 128
+    k16 = L["sq"] - L["k16"]  # k16 is followed by sq; 0 bytes (next offset) when unused
+    assert (k16 >= npad * 256) == exact and (k16 < 256) == (not exact)
+
+
+def test_binding_refuses_tensors_the_abi_would_misread():
+    """The binding checks dtype, shape, layout and device before it passes
+    bare pointers (here on CPU tensors, so no library call is made)."""
+    import torch
+    p = vc.default_params(1, 2, 64)
+    good = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="bfloat16"):
+        vc.prepare(p, good.float(), good, good, ws)
+    with pytest.raises(ValueError, match="shape"):
+        vc.prepare(p, good[:, :1], good, good, ws)
+    with pytest.raises(ValueError, match="contiguous"):
+        vc.prepare(p, good.transpose(1, 2).contiguous().transpose(1, 2), good, good, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        vc.prepare(p, good, good, good, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        vc.forward(p, ws, good)
+
+
 @pytest.mark.parametrize("v4,sq", [(False, False), (True, False), (False, True), (True, True)],
                          ids=["e4m3_v", "v4", "smooth_q", "v4_smooth_q"])
 @pytest.mark.parametrize("B,H,N,C_,rho", [(1, 2, 1024, 8, 0.005), (2, 24, 16544, 32, 0.005),
@@ -109,7 +153,8 @@ def test_layout_aligned_and_disjoint(B, H, N, C_, rho, v4, sq):
     mpad = -(-m // 128) * 128
     sizes = dict(header=256, kbar=BH * 512, ksum=BH * (-(-N // 512)) * 1024, init_idx=BH * C_ * 4,
                  centroids=BH * C_ * 512, labels=BH * N * 4, perm=BH * N * 4, iperm=BH * N * 4,
-                 q8=BH * npad * 128, k8=BH * npad * 128, k16=BH * npad * 256, sq=BH * nblk * 4, sk=BH * nblk * 4,
+                 q8=BH * npad * 128, k8=BH * npad * 128,
+                 k16=BH * npad * 256 if N < vc.FP8_SCORES_MIN_TOKENS else 0, sq=BH * nblk * 4, sk=BH * nblk * 4,
                  mu=BH * nblk * 512, bamax=BH * nblk * 512, mup=BH * nblk * 512,
                  mupt=BH * (-(-nblk // 16)) * 8192, sv=BH * 512,
                  inv=BH * 512, v8t=0 if v4 else BH * 128 * npad, err=BH * N * 4, rep_pos=BH * mpad * 4,

@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_driver.bin")
 
 
-@pytest.mark.parametrize("flags", [vc.DEFAULT_FLAGS, vc.DEFAULT_FLAGS | vc.V4 | vc.SMOOTH_Q],
-                         ids=["default", "v4_smooth_q"])
+@pytest.mark.parametrize("flags", [vc.DEFAULT_FLAGS, vc.DEFAULT_FLAGS | vc.V4 | vc.SMOOTH_Q | vc.FP8_SCORES],
+                         ids=["default", "v4_smooth_q_fp8"])
 def test_c_caller_matches_binding(tmp_path, flags):
     import torch
     if not torch.cuda.is_available():

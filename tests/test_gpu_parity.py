@@ -3,7 +3,12 @@
 Bar: every prepare output that is an integer or a code (cluster ids, the
 permutation, Q/K/V E4M3 codes, the repair set) and every fp32 scale, mean and
 criterion it is derived from is bit-identical to the oracle; the output O is
-within max-abs 1e-2 and relative-L2 5e-3 of the oracle's fp64 simulation."""
+within max-abs 1e-2 and relative-L2 5e-3 of the oracle's fp64 simulation, whose
+raw scores are the exact dot products of the E4M3 codes.  Calls that run QK^T
+on the FP8 MFMA (the default from 4096 tokens on) are held to the same bar; when
+FP8 scores are forced on fewer tokens only the relative-L2 bar is asserted
+(tests/gpu_common.py, check_output), and their ExpCast bytes are pinned code by
+code to the exact-score reference (compare_pcodes)."""
 import os
 import sys
 
@@ -79,6 +84,24 @@ SMALL = [
 ]
 
 
+FP8 = 1 | 2 | 4 | 256  # default flags with the FP8-score kernel forced
+# the same edge cases on the FP8-score kernel (forced below 4096 tokens)
+SMALL += [
+    ("fp8_one_token", 1, 1, 1, 1, dict(flags=FP8)),
+    ("fp8_one_block_ragged", 1, 2, 100, 3, dict(flags=FP8)),
+    ("fp8_ragged_tail", 2, 2, 300, 5, dict(rho=0.05, flags=FP8)),
+    ("fp8_several_tiles", 1, 3, 1000, 8, dict(flags=FP8)),
+    ("fp8_vsmooth_off", 1, 2, 700, 4, dict(flags=256)),
+    ("fp8_q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2 | 256)),
+    ("fp8_lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0, flags=FP8)),
+    ("fp8_literal_56", 1, 2, 700, 4, dict(expcast_k=0, flags=FP8)),
+    ("fp8_repair_all", 1, 1, 260, 3, dict(rho=1.0, flags=FP8)),
+    ("fp8_v4_ragged_tail", 2, 2, 300, 5, dict(rho=0.05, flags=FP8 | 64)),
+    ("fp8_sq_ragged_tail", 2, 2, 300, 5, dict(rho=0.05, flags=FP8 | 128)),
+    ("fp8_sq_v4", 1, 2, 520, 4, dict(rho=0.02, flags=FP8 | 64 | 128)),
+]
+
+
 @pytest.mark.parametrize("label,B,H,N,C_,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_small_cases(label, B, H, N, C_, kw):
     # the workloads' value distribution (1% outlier tokens, sigma 20, zero mean):
@@ -128,15 +151,39 @@ def test_v4_codes_at_every_rounding_midpoint(N, flags, rho):
     _full_case(p, q, k, v, [0], np.arange(N, dtype=np.int32), f"v4_midpoints_{N}")
 
 
-@pytest.mark.parametrize("exact", [False, True], ids=["fp8_scores", "exact_scores"])
-def test_workload0_all_rows(exact):
+@pytest.mark.parametrize("extra", [0, 256], ids=["default", "fp8_scores"])
+def test_workload0_all_rows(extra):
+    """All rows of the tiny workload against the exact-score oracle: the default
+    call (exact scores below 4096 tokens) at the full bar, and the FP8-score
+    kernel forced, whose relative L2 meets the bar while one code a step off
+    on an outlier key moves one row by ~0.017 (reported)."""
     import precision_fp8_attention_amd as vc
     q, k, v = inputs.make_inputs(0)
     wl = inputs.WORKLOADS[0]
-    flags = vc.DEFAULT_FLAGS | (vc.EXACT_SCORES if exact else 0)
-    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"], flags=flags)
+    p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"],
+                     flags=vc.DEFAULT_FLAGS | extra)
     _full_case(p, q, k, v, [0, 1], np.arange(wl["N"], dtype=np.int32),
-               "workload0" + ("_exact" if exact else ""))
+               "workload0" + ("_fp8" if extra else ""))
+
+
+@pytest.mark.parametrize("jump,extra", [(8, 0), (16, 0), (8, 256), (16, 256)],
+                         ids=["jump8", "jump16", "jump8_fp8", "jump16_fp8"])
+def test_online_rescale_closed_form(jump, extra):
+    """The hand-worked two-block case (tests/closed_form.py): the second key block
+    raises the row maximum by `jump` code units, and the checked row's output is
+    u + w exactly, in bf16 too (one nonzero product per score, so the FP8 MFMA
+    is exact here as well)."""
+    import closed_form
+    import precision_fp8_attention_amd as vc
+    qf, kf, vf, row, want = closed_form.rescale_case(jump, seed=jump)
+    q, k, v = (inputs.to_bf16_bits(x) for x in (qf, kf, vf))
+    p = G.lib_params(1, 1, 256, 1, T=2, flags=vc.DEFAULT_FLAGS | extra,
+                     sm_scale=closed_form.unit_gain_scale())
+    G.log(f"[case] closed-form rescale jump={jump} flags={p.flags}")
+    qd, kd, vd = G.to_device(q, k, v)
+    ws, o = G.run(p, qd, kd, vd)
+    got = G.out_f64(o).reshape(256, 128)[row]
+    np.testing.assert_array_equal(got, want)
 
 
 def test_workload3_exact_scores_sampled():
@@ -295,7 +342,7 @@ def test_output_in_original_order_when_inputs_permuted():
 # ------------------------------------------------------------------ P codes
 
 PCODE_CASES = [
-    # (label, B, H, N, C, kwargs)
+    # (label, B, H, N, C, kwargs); below 4096 tokens the default is exact scores
     ("ragged", 1, 2, 300, 5, {}),
     ("exact_scores", 1, 2, 300, 5, dict(flags=1 | 2 | 4 | 16)),
     ("q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2)),
@@ -303,12 +350,21 @@ PCODE_CASES = [
     ("literal_56", 1, 1, 520, 4, dict(expcast_k=0)),
     ("smooth_q", 1, 2, 300, 5, dict(flags=1 | 2 | 4 | 128)),
     ("smooth_q_exact_tau6", 1, 2, 520, 4, dict(tau=6.0, flags=1 | 2 | 4 | 16 | 128)),
+    # the FP8-score kernel
+    ("fp8_ragged", 1, 2, 300, 5, dict(flags=FP8)),
+    ("fp8_q_not_permuted", 1, 2, 700, 4, dict(flags=1 | 2 | 256)),
+    ("fp8_lazy_max_tau6", 1, 2, 700, 4, dict(tau=6.0, flags=FP8)),
+    ("fp8_literal_56", 1, 1, 520, 4, dict(expcast_k=0, flags=FP8)),
+    ("fp8_smooth_q", 1, 2, 300, 5, dict(flags=FP8 | 128)),
 ]
 
 
-def _pcodes_case(p, q, k, v, heads, rows, label):
-    """Every ExpCast byte the GPU main loop wrote for the given rows equals the
-    oracle's code (the scores' accumulation rule included)."""
+def _pcodes_case(p, q, k, v, heads, rows, label, min_agree=0.999):
+    """Every ExpCast byte the GPU main loop wrote for the given rows against the
+    exact-score oracle's code for the same (query, key): bit-exact with exact
+    scores; with FP8 scores differing only by one step next to a rounding
+    boundary (tests/gpu_common.py, compare_pcodes).  The diagnostic model of the
+    FP8 instruction's accumulation is reported beside it, not asserted."""
     import torch
 
     import precision_fp8_attention_amd as vc
@@ -324,18 +380,27 @@ def _pcodes_case(p, q, k, v, heads, rows, label):
     vc.forward(p, ws, o2)
     torch.cuda.synchronize()
     assert torch.equal(o, o2), "forward_pcodes changed the output"
+    exact = G.exact_mode(p)
     P = G.oracle_params(p)
     prep = orc.prepare(P, q, k, v, heads=heads)
+    Pd = G.oracle_params(p, diagnostic_rule=True)
     gpc = pc.view(p.B * p.H, npad, npad).cpu().numpy()
-    total = bad = 0
+    got, ref, pv, rule = [], [], [], []
     for slot, hd in enumerate(heads):
-        _, opc = orc.forward_rows(P, prep, np.full(len(rows), slot, np.int32), rows, want_pcodes=True)
+        sl = np.full(len(rows), slot, np.int32)
+        _, opc, opv = orc.forward_rows(P, prep, sl, rows, want_pcodes=True, want_pvals=True)
         pos = prep["iperm"][slot][rows] if (p.flags & vc.PERMUTE_Q) else rows
-        got = gpc[hd][pos]
-        bad += int(np.sum(got != opc))
-        total += got.size
-    G.log(f"pcodes {label}: {bad} of {total} codes differ")
-    assert bad == 0, f"{label}: {bad} of {total} P codes differ from the oracle"
+        got.append(gpc[hd][pos])
+        ref.append(opc)
+        pv.append(opv)
+        if not exact:
+            rule.append(orc.forward_rows(Pd, prep, sl, rows, want_pcodes=True)[1])
+    got, ref, pv = np.concatenate(got), np.concatenate(ref), np.concatenate(pv)
+    if rule:
+        rule = np.concatenate(rule)
+        G.log(f"pcodes {label}: diagnostic FP8-instruction model differs from the GPU on "
+              f"{int(np.sum(rule != got))} of {got.size} codes")
+    G.compare_pcodes(got, ref, pv, label, exact, min_agree=min_agree)
 
 
 @pytest.mark.parametrize("label,B,H,N,C_,kw", PCODE_CASES, ids=[c[0] for c in PCODE_CASES])
@@ -346,15 +411,29 @@ def test_pcodes_match_oracle(label, B, H, N, C_, kw):
 
 
 def test_pcodes_workloads_0_and_1():
-    """All codes of workload 0, and sampled rows of two heads of workload 1
-    (4256 keys, text and image tokens)."""
-    for cfg, heads, nrows in ((0, [0, 1], None), (1, [3, 20], 96)):
+    """All codes of workload 0 (exact scores by default, and the FP8-score kernel
+    forced), and sampled rows of two heads of workload 1 (4256 keys, text and
+    image tokens; FP8 scores by default)."""
+    import precision_fp8_attention_amd as vc
+    for cfg, heads, nrows, extra in ((0, [0, 1], None, 0), (0, [0, 1], None, vc.FP8_SCORES),
+                                     (1, [3, 20], 96, 0)):
         wl = inputs.WORKLOADS[cfg]
         q, k, v = inputs.make_inputs(cfg, heads=heads)
-        p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+        p = G.lib_params(wl["B"], wl["H"], wl["N"], wl["C"], T=wl["T"], rho=wl["rho"],
+                         flags=vc.DEFAULT_FLAGS | extra)
         rows = (np.arange(wl["N"], dtype=np.int32) if nrows is None
                 else G.sample_rows(wl["N"], nrows, seed=7))
-        _pcodes_case(p, q, k, v, heads, rows, f"workload{cfg}")
+        _pcodes_case(p, q, k, v, heads, rows, f"workload{cfg}" + ("_fp8" if extra else ""))
+
+
+def test_pcodes_benchmark_head():
+    """ExpCast bytes of the benchmark workload's last head (2048x2048 CFG pair,
+    16544 keys, FP8 scores) run as a one-head problem: sampled rows, every key."""
+    wl = inputs.WORKLOADS[3]
+    q, k, v = inputs.make_inputs(3, heads=[47])
+    q, k, v = (np.ascontiguousarray(x[1:2, 23:24]) for x in (q, k, v))
+    p = G.lib_params(1, 1, wl["N"], wl["C"], T=wl["T"], rho=wl["rho"])
+    _pcodes_case(p, q, k, v, [0], G.sample_rows(wl["N"], 48, seed=9), "workload3_head47")
 
 
 # ------------------------------------------------------------------ warm start
@@ -429,6 +508,8 @@ def _sweep_cases(n=40, seed=7):
         for f in (1, 2, 4, 16, 64, 128):  # VSMOOTH REPAIR PERMUTE_Q EXACT_SCORES V4 SMOOTH_Q
             if rng.random() < 0.5:
                 flags |= f
+        if not flags & 16:
+            flags |= 256  # the other half runs the FP8-score kernel
         kw = dict(flags=flags, rho=float(rng.choice([0.0, 0.005, 0.05, 0.3, 1.0])),
                   tau=float(rng.choice([0.0, 0.0, 3.0, 6.0])), expcast_k=int(rng.choice([8, 8, 0, 4])),
                   T=int(rng.choice([1, 3, 10])), sm_scale=float(rng.choice([0.0, 0.0, 0.02, 0.2])),
@@ -442,10 +523,11 @@ SWEEP = _sweep_cases()
 
 @pytest.mark.parametrize("label,B,H,N,C_,kw", SWEEP, ids=[c[0] for c in SWEEP])
 def test_random_sweep(label, B, H, N, C_, kw):
-    """Prepare bit-exact and O within the bar on every drawn case.  Softmax scale
-    0.2 over outlier values makes attention peaky and |O| reach ~20, where bf16
-    output rounding alone is ~0.06: the max-abs bar is taken beyond one bf16 step
-    of |O| here (relative L2 keeps its 5e-3 bar)."""
+    """Prepare bit-exact and O within the bar on every drawn case (against the
+    exact-score oracle; FP8-score cases, all below 4096 tokens, relative L2
+    only).  Softmax scale 0.2 over outlier values makes attention peaky and |O|
+    reach ~20, where bf16 output rounding alone is ~0.08: the max-abs bar is
+    taken beyond that rounding (2^-8 |O|) here."""
     p = G.lib_params(B, H, N, C_, **kw)
     q, k, v = inputs.make_custom(B, H, N, seed=kw["seed"] % 1000)
     G.log(f"[case] {label}: {kw}")
@@ -473,6 +555,8 @@ def _warm_cases(n=12, seed=99):
         for f in (2, 4, 16, 64, 128):  # REPAIR PERMUTE_Q EXACT_SCORES V4 SMOOTH_Q
             if rng.random() < 0.5:
                 flags |= f
+        if not flags & 16:
+            flags |= 256  # FP8-score kernel
         kw = dict(flags=flags, Tc=int(rng.choice([1, 3, 10])), Tw=int(rng.choice([1, 2, 3, 5])),
                   rho=float(rng.choice([0.0, 0.005, 0.05, 1.0])), step=int(rng.integers(1, 4)),
                   seed=int(rng.integers(0, 1 << 30)))

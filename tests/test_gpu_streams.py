@@ -37,7 +37,7 @@ def _case(seed, flags=vc.DEFAULT_FLAGS):
 
 def test_two_streams_overlap_bit_identical():
     import torch
-    cases = [_case(11), _case(12, vc.DEFAULT_FLAGS | vc.V4)]
+    cases = [_case(11), _case(12, vc.DEFAULT_FLAGS | vc.V4 | vc.FP8_SCORES)]
     G.log("[case] two streams: eager references on the current stream")
     ref = []
     for p, (qd, kd, vd) in cases:
@@ -64,7 +64,7 @@ def test_graph_replay_matches_eager():
     captured buffers, eager library calls and synchronisations in between; every
     replay must equal the eager result for the same inputs."""
     import torch
-    p, (qd, kd, vd) = _case(21)
+    p, (qd, kd, vd) = _case(21, vc.DEFAULT_FLAGS | vc.FP8_SCORES)  # the benchmark's kernel
     ws = vc.alloc_workspace(p)
     o = torch.empty_like(qd)
     side = torch.cuda.Stream()

@@ -13,6 +13,8 @@ import torch
 from oracle import oracle as orc
 from synthetic import inputs
 
+import closed_form  # noqa: E402  (tests/ is on sys.path under pytest)
+
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -504,21 +506,94 @@ def test_exact_invariant_to_joint_kv_permutation():
                                rtol=1e-12, atol=1e-14)
 
 
-def test_demean_restore_identity_fp64():
-    """Restore identity stated by the pages: with block means removed from V and
-    added back through each block's row sum, attention is unchanged."""
-    rng = np.random.default_rng(2)
-    N, nb = 384, 3
-    s = rng.standard_normal((5, N))
-    v = rng.standard_normal((N, 128)) + 3
-    p = np.exp(s - s.max(1, keepdims=True))
-    ref = p @ v / p.sum(1, keepdims=True)
-    acc = np.zeros((5, 128))
-    for b in range(nb):
-        sl = slice(b * 128, b * 128 + 128)
-        mu = v[sl].mean(0)
-        acc += p[:, sl] @ (v[sl] - mu) + p[:, sl].sum(1, keepdims=True) * mu
-    np.testing.assert_allclose(acc / p.sum(1, keepdims=True), ref, rtol=1e-12)
+def test_restore_returns_block_means_through_row_sums():
+    """V-Smooth's Restore (noticiai.com.br article, section V-Smooth: the block
+    mean comes back through the row sum online softmax already keeps), checked
+    against the P.V path of the same simulation.  With one cluster the order is
+    the identity, so V-Smooth on and off give the same Q/K codes and the same
+    ExpCast weights.  V = block indicator (channel c is 1 on the tokens of block
+    c): with V-Smooth off its E4M3 codes are exact and P.V returns the weight
+    w_b of each block (ragged tail included); with V-Smooth on every residual
+    code is 0 and only Restore (row sum times block mean) can return it.  The
+    two must agree, sum to 1, and any other block-constant V must give
+    sum_b w_b mu_b.  A dropped restore term, a mean added without its row sum,
+    or a rescale missing from the restore accumulator breaks the agreement."""
+    N = 300
+    nb = 3
+    q, k, _ = inputs.make_custom(1, 1, N, seed=12)
+    blk = np.arange(N) // 128
+    ind = np.zeros((N, 128), np.float32)
+    ind[np.arange(N), blk] = 1.75  # 448 * 2^-8: scale 2^-8, code 448, both exact
+    rows = np.arange(N, dtype=np.int32)
+
+    def run(vf, flags):
+        v = inputs.to_bf16_bits(vf).reshape(1, 1, N, 128)
+        P = orc.make_params(1, 1, N, C_=1, T=2, flags=flags)
+        (out, pc), pr, _, _ = _sim(P, q, k, v, rows=rows, pcodes=True)
+        return out, pc, pr
+
+    w_pv, pc_off, pr_off = run(ind, orc.PERMUTE_Q)
+    w_rs, pc_on, pr_on = run(ind, orc.VSMOOTH | orc.PERMUTE_Q)
+    w_pv, w_rs = w_pv / 1.75, w_rs / 1.75
+    np.testing.assert_array_equal(pc_on, pc_off)
+    assert np.all(pr_on["v8"] == 0) and np.array_equal(pr_on["perm"][0], np.arange(N))
+    np.testing.assert_allclose(pr_off["sv"][0][:nb] * orc.e4m3_decode(pr_off["v8"][0][:N, :nb]),
+                               ind[:, :nb], rtol=0, atol=0)  # indicator codes are exact
+    np.testing.assert_allclose(w_rs, w_pv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(w_pv[:, :nb].sum(1), 1.0, rtol=1e-12)
+    assert np.all(w_pv[:, nb:] == 0) and np.all(w_pv[:, :nb] > 0)
+    vf = closed_form.block_constant_values(N, seed=3)
+    out, _, _ = run(vf, orc.VSMOOTH | orc.PERMUTE_Q)
+    mu = vf[[0, 128, 256]].astype(np.float64)
+    np.testing.assert_allclose(out, w_pv[:, :nb] @ mu, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("jump,tau", [(8, 0.0), (16, 0.0), (8, 6.0)])
+def test_online_rescale_closed_form(jump, tau):
+    """Two key blocks, the second raising the row maximum by exactly `jump` code
+    units: the running sums are rescaled by 2^(-jump/8) and every code stays at
+    56 + 8k, so the output is (r mu0 + mu1)/(r + 1) = u + w exactly (worked out
+    in tests/closed_form.py).  A wrong base or divisor in the rescale, a missing
+    rescale of l or of the accumulator, or M moved after the block's codes
+    changes the result."""
+    q, k, v, row, want = closed_form.rescale_case(jump, seed=jump)
+    q, k, v = (inputs.to_bf16_bits(x) for x in (q, k, v))
+    P = orc.make_params(1, 1, 256, C_=1, T=2, tau=tau, sm_scale=closed_form.unit_gain_scale())
+    (out, pc), pr, _, _ = _sim(P, q, k, v, rows=[row], pcodes=True)
+    assert np.all(pc[0] == 120)
+    np.testing.assert_array_equal(out[0], want)
+    ex = orc.exact_rows(P, q, k, v, np.zeros(1), np.array([row]))
+    np.testing.assert_allclose(ex[0], want, rtol=1e-6, atol=1e-6)
+
+
+def test_online_equals_two_pass_when_the_maximum_never_moves():
+    """Rows whose largest score lies in the first key block never move M after
+    that block, so the online loop must give the codes of the two-pass
+    softmax: the row maximum over all keys first, then every code from it."""
+    N = 700
+    q, k, v = inputs.make_custom(1, 1, N, seed=19)
+    P = orc.make_params(1, 1, N, C_=4, T=3)
+    (out, pc), pr, _, _ = _sim(P, q, k, v, pcodes=True)
+    c0 = orc.code_gain(0.0)
+    k8 = pr["k8"][0][:N]
+    checked = 0
+    blk = np.arange(N) // 128
+    nb = blk[-1] + 1
+    for row in range(0, N, 3):
+        pos = pr["iperm"][0][row]
+        s = orc.scores(np.repeat(pr["q8"][0][pos][None], N, 0), k8, exact=True)
+        alpha = (pr["sq"][0][pos // 128] * pr["sk"][0][blk]).astype(np.float32) * c0
+        # block maxima in code units as the loop forms them: max raw score times
+        # the block's alpha (alpha > 0), one fp32 product
+        tb = np.array([np.float32(s[blk == b].max() * alpha[blk == b][0]) for b in range(nb)])
+        if np.any(tb[1:] > tb[0]):
+            continue
+        beta = np.float32(np.float32(120.0) - tb[0])
+        two_pass = np.concatenate([orc.expcast(s[blk == b], float(alpha[blk == b][0]), float(beta))
+                                   for b in range(nb)])
+        np.testing.assert_array_equal(pc[row][:N], two_pass)
+        checked += 1
+    assert checked >= 10
 
 
 # ------------------------------------------------------------------ warm start

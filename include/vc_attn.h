@@ -242,6 +242,25 @@ vc_status vc_attn_forward(const vc_attn_params* p, const void* workspace, size_t
 vc_status vc_attn_forward_pcodes(const vc_attn_params* p, const void* workspace, size_t ws_bytes,
                                  void* o, void* pcodes, void* stream);
 
+/* Size of the static device workspace of vc_attn_run_noalloc (per GPU). */
+#define VC_NOALLOC_WORKSPACE_BYTES (256u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): vc_attn_prepare then
+ * vc_attn_forward with the workspace in a static device array of
+ * VC_NOALLOC_WORKSPACE_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The caller passes only q, k, v (device bf16
+ * [B][H][N][128]) and o (device bf16, original token order); the device is the
+ * stream's.  Allocates nothing.  Returns VC_ERR_WORKSPACE when
+ * vc_attn_workspace_size(p) exceeds VC_NOALLOC_WORKSPACE_BYTES (about six heads
+ * of 16544 tokens), otherwise the statuses of prepare and forward.  Every call
+ * on one GPU uses that GPU's array, which keeps the last call's contents (so
+ * VC_REUSE_CLUSTERS / VC_WARM_START see the previous call's clusters when the
+ * shape matches): calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Asynchronous. */
+vc_status vc_attn_run_noalloc(const vc_attn_params* p, const void* q, const void* k,
+                              const void* v, void* o, void* stream);
+
 /* Static description of a status code. */
 const char* vc_attn_status_string(vc_status s);
 

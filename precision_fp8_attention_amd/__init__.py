@@ -21,7 +21,8 @@ SMOOTH_Q_MAX_TOKENS = 131072   # largest N accepted with SMOOTH_Q
 
 EXPORTS = ("vc_attn_default_params", "vc_attn_workspace_size", "vc_attn_workspace_layout",
            "vc_attn_check_params", "vc_attn_prepare", "vc_attn_forward", "vc_attn_forward_pcodes",
-           "vc_attn_status_string", "vc_attn_version")
+           "vc_attn_status_string", "vc_attn_version", "vc_attn_run_noalloc")
+NOALLOC_WORKSPACE_BYTES = 256 << 20  # static workspace of run_noalloc, per GPU
 
 
 class Params(C.Structure):
@@ -75,11 +76,13 @@ def lib() -> C.CDLL:
         L.vc_attn_forward.argtypes = [P, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.vc_attn_forward_pcodes.argtypes = [P, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                                              C.c_void_p]
+        L.vc_attn_run_noalloc.argtypes = [P, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                          C.c_void_p]
         L.vc_attn_status_string.argtypes = [C.c_int]
         L.vc_attn_status_string.restype = C.c_char_p
         L.vc_attn_version.restype = C.c_int32
         for f in ("vc_attn_workspace_layout", "vc_attn_check_params", "vc_attn_prepare",
-                  "vc_attn_forward", "vc_attn_forward_pcodes"):
+                  "vc_attn_forward", "vc_attn_forward_pcodes", "vc_attn_run_noalloc"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -190,6 +193,16 @@ def forward_pcodes(p: Params, workspace, o, pcodes, stream=None) -> None:
                                       _ptr(pcodes), _stream(stream, o.device))
     if st != OK:
         raise VCError(st, "vc_attn_forward_pcodes")
+
+
+def run_noalloc(p: Params, q, k, v, o, stream=None) -> None:
+    """vc_attn_run_noalloc: prepare + forward with the library's static
+    per-GPU workspace (no allocation); o receives the output."""
+    _check("run_noalloc", p, dict(q=q, k=k, v=v, o=o))
+    st = lib().vc_attn_run_noalloc(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _stream(stream, q.device))
+    if st != OK:
+        raise VCError(st, "vc_attn_run_noalloc")
 
 
 def alloc_workspace(p: Params, device="cuda"):

@@ -1,9 +1,17 @@
 // Host side of the VC-Attention FP8 C ABI: argument checks, workspace layout,
-// and the two stream-ordered entry points.  No device allocation, no global state.
+// and the stream-ordered entry points.  No device allocation; the only global
+// state is the static workspace of vc_attn_run_noalloc (per GPU) and the
+// per-device addresses of it.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "vc_internal.h"
+
+// Workspace of vc_attn_run_noalloc: one copy per GPU, held until the process
+// ends.  In host code this name is only a stand-in for the symbol: kernels get
+// the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[VC_NOALLOC_WORKSPACE_BYTES];
 
 namespace vc {
 
@@ -285,6 +293,54 @@ vc_status vc_attn_forward_pcodes(const vc_attn_params* p, const void* workspace,
     return st != VC_OK ? st : VC_ERR_INVALID_ARG;
   }
   return forward_impl(p, workspace, ws_bytes, o, static_cast<uint8_t*>(pcodes), stream);
+}
+
+}  // extern "C"
+
+namespace vc {
+
+// Device address of `scratch` on the device the stream runs on, looked up once
+// per device with that device current (each GPU holds its own copy of the
+// array at its own address).
+static vc_status scratch_of(hipStream_t st, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return VC_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return VC_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return VC_ERR_HIP;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return VC_OK;
+}
+
+}  // namespace vc
+
+extern "C" {
+
+vc_status vc_attn_run_noalloc(const vc_attn_params* p, const void* q, const void* k, const void* v,
+                              void* o, void* stream) {
+  const vc_status st = check(p);
+  if (st != VC_OK) return st;
+  if (!q || !k || !v || !o || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return VC_ERR_INVALID_ARG;
+  if (vc_attn_workspace_size(p) > (size_t)VC_NOALLOC_WORKSPACE_BYTES) return VC_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const vc_status sa = scratch_of(static_cast<hipStream_t>(stream), &ws);
+  if (sa != VC_OK) return sa;
+  // the same kernels as vc_attn_prepare + vc_attn_forward, workspace = the array
+  const vc_status sp = vc_attn_prepare(p, q, k, v, ws, VC_NOALLOC_WORKSPACE_BYTES, stream);
+  if (sp != VC_OK) return sp;
+  return vc_attn_forward(p, ws, VC_NOALLOC_WORKSPACE_BYTES, o, stream);
 }
 
 const char* vc_attn_status_string(vc_status s) {

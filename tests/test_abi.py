@@ -96,6 +96,13 @@ def test_pointer_and_workspace_errors_before_device_work():
     assert L.vc_attn_forward_pcodes(P, fake, need, fake, mis, None) == vc.ERR_INVALID_ARG
     assert L.vc_attn_forward_pcodes(P, fake, need - 1, fake, fake, None) == vc.ERR_WORKSPACE
     assert L.vc_attn_forward_pcodes(C.byref(bad), fake, need, fake, None, None) == vc.ERR_UNSUPPORTED
+    assert L.vc_attn_run_noalloc(P, fake, fake, None, fake, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_run_noalloc(P, fake, fake, fake, mis, None) == vc.ERR_INVALID_ARG
+    assert L.vc_attn_run_noalloc(C.byref(bad), fake, fake, fake, fake, None) == vc.ERR_UNSUPPORTED
+    # more than the static workspace: refused before any device work
+    big = vc.default_params(2, 24, 16544, n_clusters=32)
+    assert vc.workspace_size(big) > vc.NOALLOC_WORKSPACE_BYTES
+    assert L.vc_attn_run_noalloc(C.byref(big), fake, fake, fake, fake, None) == vc.ERR_WORKSPACE
 
 
 def test_smooth_q_accepted_up_to_its_bound():

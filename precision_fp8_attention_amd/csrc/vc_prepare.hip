@@ -313,8 +313,10 @@ __global__ __launch_bounds__(128) void k_km_warm(Args a) {
 }
 
 // Assignment step on int8 MFMA plus per-workgroup member sums.
-// grid (nkm, BH), KM_WAVES waves (each takes every KM_WAVES-th 16-token subtile),
-// KM_CHUNK tokens per workgroup.  Lane (g, j) of a 16-token subtile loads the
+// grid (nkm, BH), KM_WAVES waves (each takes every KM_WAVES-th 16-token subtile);
+// the head's tokens are cut into nkm chunks of equal size (a multiple of 16, at
+// most KM_CHUNK), one per workgroup, so that no workgroup is left with a short
+// tail chunk while the others run full ones.  Lane (g, j) of a 16-token subtile loads the
 // hi/lo bytes of channels 16g..16g+15 and 64+16g..64+16g+15 of token j as its
 // MFMA B operand; after the argmin the same registers are added to the LDS bins
 // of the token's cluster, so the planes are read once per iteration.
@@ -377,22 +379,24 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
   // wave w takes 16-token subtiles w, w+KM_WAVES, ... of the chunk; the operands
   // of the next subtile are loaded while the current one is processed
-  const int first = chunk * KM_CHUNK;
+  // chunks of equal size (a multiple of 16 tokens, at most KM_CHUNK)
+  const int csz = ((a.N + a.nkm - 1) / a.nkm + 15) & ~15;
+  const int first = chunk * csz, last = min(first + csz, a.N);
   auto load_sub = [&](int s, v4i& h0, v4i& h1, v4i& l0, v4i& l1) {
     int jj = first + s * 16 + l16;
-    jj = jj < a.N ? jj : a.N - 1;  // tail lanes read a valid row, add nothing
+    jj = jj < last ? jj : last - 1;  // tail lanes read a valid row, add nothing
     h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
     h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
     l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
     l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
   };
   v4i nh0, nh1, nl0, nl1;
-  if (first + w * 16 < a.N) load_sub(w, nh0, nh1, nl0, nl1);
+  if (first + w * 16 < last) load_sub(w, nh0, nh1, nl0, nl1);
 #pragma unroll 1
   for (int sub = w; sub < KM_CHUNK / 16; sub += KM_WAVES) {
-    if (first + sub * 16 >= a.N) break;  // uniform per wave
+    if (first + sub * 16 >= last) break;  // uniform per wave
     const v4i bh0 = nh0, bh1 = nh1, bl0 = nl0, bl1 = nl1;
-    if (sub + KM_WAVES < KM_CHUNK / 16 && first + (sub + KM_WAVES) * 16 < a.N)
+    if (sub + KM_WAVES < KM_CHUNK / 16 && first + (sub + KM_WAVES) * 16 < last)
       load_sub(sub + KM_WAVES, nh0, nh1, nl0, nl1);
     const int j = first + sub * 16 + l16;
     long long bestD = 0x7fffffffffffffffll;
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
       const int ob = __shfl_xor(best, off, 64);
       if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
     }
-    if (j < a.N) {
+    if (j < last) {
       if (g == 0) {
         a.labels[(size_t)bh * a.N + j] = best;
         atomicAdd(&cnt[best], 1);
@@ -538,47 +542,57 @@ __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
 // copy of the codes.  With VC_SMOOTH_Q a Q block first subtracts its channel
 // mean (exact fixed-point sum, as for the V block means), which is kept.
 // grid (nblk, BH, 2), 256 threads: thread = (8-channel chunk t%16, rows
-// t/16 + 16i), so 16 threads cover one 256-byte row.
-__global__ __launch_bounds__(256) void k_qk_quant(Args a) {
+// t/16 + 16i), so 16 threads cover one 256-byte row.  A thread keeps its 8 rows
+// as raw bf16 (32 registers, not 64 floats) and converts them where they are
+// used, which doubles the waves a CU holds and the rows in flight.
+template <bool SMOOTH>
+__global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
   __shared__ float wmax[4];
   __shared__ long long qsum[16][D];
   __shared__ float qmean[D];
   const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z, t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
   const bool follow = isk || (a.flags & VC_PERMUTE_Q);
-  const bool smooth = !isk && (a.flags & VC_SMOOTH_Q);  // uniform over the workgroup
+  const bool smooth = SMOOTH && !isk;  // uniform over the workgroup
   const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
-  float kb[8];
+  const int nrow = a.N - blk * BLK;  // rows r < nrow of the block are tokens
+  // value subtracted from channel e: the K channel mean, or (smoothed queries)
+  // the block mean once it is known
+  float sub[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kb[i] = isk ? a.kbar[(size_t)bh * D + cg * 8 + i] : 0.0f;
-  float x[8][8];
+  for (int e = 0; e < 8; ++e) sub[e] = isk ? a.kbar[(size_t)bh * D + cg * 8 + e] : 0.0f;
+  uint4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int p = blk * BLK + r0 + 16 * i;
-    if (p < a.N) {
+    const int r = r0 + 16 * i;
+    raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nrow) {
+      const int p = blk * BLK + r;
       const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
-      const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)j * D + cg * 8);
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float val = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
-        if (isk) val = val - kb[e];
-        x[i][e] = val;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
+      raw[i] = *reinterpret_cast<const uint4*>(src + (size_t)j * D + cg * 8);
     }
   }
+  // element e of row i as fp32, minus sub[e] (exact order of the reference: one
+  // fp32 subtraction)
+  auto val = [&](int i, int e) {
+    const uint32_t w = e < 2 ? raw[i].x : e < 4 ? raw[i].y : e < 6 ? raw[i].z : raw[i].w;
+    return bf2f((e & 1) ? (w >> 16) : w) - sub[e];
+  };
+  // Between the passes over the rows the compiler is told the raw words may have
+  // changed, so it converts them again instead of keeping 64 floats live.
+  auto fence = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+  };
   if (smooth) {
-    const int n = min(BLK, a.N - blk * BLK);
-    double sm[8];  // 8 rows per thread: exact in fp64 (see fx24d)
+    const int n = min(BLK, nrow);
+    double sm[8];  // 8 rows per thread: exact in fp64 (see fx24d); rows past N hold 0
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm[e] = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm[e] += fx24d(x[i][e]);  // rows past N hold 0
+      for (int e = 0; e < 8; ++e) sm[e] += fx24d(val(i, e));
 #pragma unroll
     for (int e = 0; e < 8; ++e) qsum[r0][cg * 8 + e] = (long long)sm[e];
     __syncthreads();
@@ -590,30 +604,30 @@ __global__ __launch_bounds__(256) void k_qk_quant(Args a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (blk * BLK + r0 + 16 * i < a.N) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - qmean[cg * 8 + e];
-      }
+    for (int e = 0; e < 8; ++e) sub[e] = qmean[cg * 8 + e];
+    fence();
   }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
+    if (r0 + 16 * i < nrow) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(val(i, e)));
+    }
   amax = wave_max(amax);
   if ((t & 63) == 0) wmax[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float s, inv;
   scale_from_amax(amax, &s, &inv);
+  fence();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int p = blk * BLK + r0 + 16 * i;
+    const int r = r0 + 16 * i, p = blk * BLK + r;
     uint32_t w0 = 0u, w1 = 0u;
-    if (p < a.N) {
-      w0 = e4m3x2(x[i][0] * inv, x[i][1] * inv) | (e4m3x2(x[i][2] * inv, x[i][3] * inv) << 16);
-      w1 = e4m3x2(x[i][4] * inv, x[i][5] * inv) | (e4m3x2(x[i][6] * inv, x[i][7] * inv) << 16);
+    if (r < nrow) {
+      w0 = e4m3x2(val(i, 0) * inv, val(i, 1) * inv) | (e4m3x2(val(i, 2) * inv, val(i, 3) * inv) << 16);
+      w1 = e4m3x2(val(i, 4) * inv, val(i, 5) * inv) | (e4m3x2(val(i, 6) * inv, val(i, 7) * inv) << 16);
     }
     uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + cg * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
@@ -714,9 +728,12 @@ __global__ __launch_bounds__(256) void k_qbias(Args a) {
 // 32-key group (rows r with 2(r/64) + (r/8)%2 = G) and its E8M0 exponent.
 // grid (nblk, BH), 256 threads: thread = (8-channel chunk t%16, rows t/16 + 16i),
 // so rows i < 4 and i >= 4 of a thread lie in groups (t/128)%2 and 2 + (t/128)%2.
-__global__ __launch_bounds__(256) void k_v_stats(Args a) {
-  __shared__ long long ssum[16][D];
-  __shared__ float smax[2][16][D];
+__global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
+  // the block sums and, after them, the block maxima share one 16 KB buffer, so
+  // six workgroups fit a CU
+  __shared__ __align__(16) long long sbuf[16 * D];
+  long long (*ssum)[D] = reinterpret_cast<long long (*)[D]>(sbuf);
+  float (*smax)[16][D] = reinterpret_cast<float (*)[16][D]>(sbuf);
   __shared__ float smu[D];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
@@ -724,26 +741,25 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
   const uint16_t* vh = a.v + (size_t)bh * a.N * D;
   const int* perm = a.perm + (size_t)bh * a.N;
-  float x[8][8];
+  // the thread's 8 rows as raw bf16 (32 registers); rows past N hold 0
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + 16 * i;
+    raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < n) raw[i] = *reinterpret_cast<const uint4*>(vh + (size_t)perm[p0 + r] * D + cg * 8);
+  }
+  auto val = [&](int i, int e) {
+    const uint32_t w = e < 2 ? raw[i].x : e < 4 ? raw[i].y : e < 6 ? raw[i].z : raw[i].w;
+    return bf2f((e & 1) ? (w >> 16) : w);
+  };
   double s[8];  // 8 rows per thread: exact in fp64 (see fx24d)
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 16 * i;
-    if (r < n) {
-      const uint4 u = *reinterpret_cast<const uint4*>(vh + (size_t)perm[p0 + r] * D + cg * 8);
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[i][e] = bf2f((e & 1) ? (h[e >> 1] >> 16) : h[e >> 1]);
-        s[e] += fx24d(x[i][e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = 0.0f;
-    }
-  }
+    for (int e = 0; e < 8; ++e) s[e] += fx24d(val(i, e));
 #pragma unroll
   for (int e = 0; e < 8; ++e) ssum[r0][cg * 8 + e] = (long long)s[e];
   __syncthreads();
@@ -753,6 +769,10 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
     smu[t] = vs ? fixed_mean(tot, n) : 0.0f;
   }
   __syncthreads();
+  // the raw words may have changed (for the compiler): convert them again
+  // rather than keep 64 floats live across the barrier
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
   float m[2][8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) m[0][e] = m[1][e] = 0.0f;
@@ -760,7 +780,7 @@ __global__ __launch_bounds__(256) void k_v_stats(Args a) {
   for (int i = 0; i < 8; ++i)
     if (r0 + 16 * i < n) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[i >> 2][e] = fmaxf(m[i >> 2][e], fabsf(x[i][e] - smu[cg * 8 + e]));
+      for (int e = 0; e < 8; ++e) m[i >> 2][e] = fmaxf(m[i >> 2][e], fabsf(val(i, e) - smu[cg * 8 + e]));
     }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -1173,7 +1193,10 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
     hipLaunchKernelGGL(k_perm_identity, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 0u);
   }
-  hipLaunchKernelGGL(k_qk_quant, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
+  if (a.flags & VC_SMOOTH_Q)
+    hipLaunchKernelGGL(k_qk_quant<true>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_qk_quant<false>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 15) / 16, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);

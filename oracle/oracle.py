@@ -221,9 +221,10 @@ def mx_exponent(a) -> np.ndarray:
 
 
 def v4_group(k):
-    """32-key group of key k (0..127) of a block for the 4-bit residual."""
+    """32-key group of key k (0..127) of a block for the 4-bit residual: 32
+    consecutive positions."""
     k = np.asarray(k)
-    return 2 * (k >> 6) + ((k >> 3) & 1)
+    return k >> 5
 
 
 def expcast(s, alpha: float, beta: float) -> np.ndarray:

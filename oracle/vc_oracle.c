@@ -66,8 +66,9 @@
  *     final row maximum; the row sum is left unchanged. *
  *   - 4-bit residual (OC_V4): the pages also run V-Smooth with the residual in
  *     NVFP4 [P5 "V-Smooth", Demean]; here in the gfx950-native MX form.  Per
- *     128-position block, channel and 32-key group (key k of the block is in
- *     group 2*(k/64) + (k mod 16)/8), X = floor(log2 max|r|) - 2 kept in
+ *     128-position block, channel and group of 32 consecutive positions (key
+ *     k of the block is in group k/32: the MX block of the OCP Microscaling
+ *     format is 32 consecutive elements), X = floor(log2 max|r|) - 2 kept in
  *     [-126, 127] (2^X a normal fp32 scale; -126 for an all-zero group), and the
  *     code is E2M1(r * 2^-X), nearest with ties to the even code, saturating at
  *     6, no negative zero.  There
@@ -234,9 +235,9 @@ int oc_mx_exponent(float a) {
   return x < -126 ? -126 : (x > 127 ? 127 : x);
 }
 
-/* 32-key groups of a 128-key block for the 4-bit residual: key k (0..127) is in
- * group 2 * (k / 64) + ((k mod 16) / 8). */
-int oc_v4_group(int k) { return 2 * (k >> 6) + ((k >> 3) & 1); }
+/* 32-key groups of a 128-key block for the 4-bit residual: consecutive
+ * positions, key k (0..127) in group k / 32. */
+int oc_v4_group(int k) { return k >> 5; }
 
 uint8_t oc_expcast(float s_raw, float alpha, float beta) {
   float y = rintf(fmaf(s_raw, alpha, beta));

@@ -72,9 +72,15 @@ def _v_col(r):
 
 
 def _v4_byte(k):
-    """Byte of key k's E2M1 code in its block's 64-byte channel row."""
-    g = 2 * (k >> 6) + ((k >> 3) & 1)
-    return 16 * g + 8 * ((k >> 2) & 1) + 4 * ((k >> 5) & 1) + 2 * ((k >> 4) & 1) + ((k >> 1) & 1)
+    """Byte of key k's E2M1 code in its block's 64-byte channel row (low nibble
+    for even k): key order."""
+    return k >> 1
+
+
+def v4_krow(r):
+    """With the 4-bit residual, row r of a block's K codes holds the key at block
+    position v4_krow(r) (bits 2-3 and 4-5 of r swapped; its own inverse)."""
+    return (r & 0x43) | ((r >> 2) & 0x0C) | ((r << 2) & 0x30)
 
 
 def _rep_col(s):
@@ -106,6 +112,9 @@ def read_prepared(p, ws, heads) -> dict:
         mup=arr("mup", np.float32, (BH, nblk, 128)), sv=arr("sv", np.float32, (BH, 128)),
         inv=arr("inv", np.float32, (BH, 128)), err=arr("err", np.float32, (BH, N)))
     if p.flags & vc.V4:
+        # K code rows back in position order
+        rows = (np.arange(npad) // 128) * 128 + v4_krow(np.arange(npad) % 128)
+        out["k8"] = np.ascontiguousarray(out["k8"][:, rows])
         # codes as one byte per (position, channel), exponents [nblk][4][128]
         t = arr("v4t", np.uint8, (BH, nblk, 128, 64))
         k = np.arange(128)

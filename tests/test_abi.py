@@ -184,22 +184,28 @@ FP4_K = [[0, 8, 32, 40], [64, 72, 96, 104], [16, 24, 48, 56], [80, 88, 112, 120]
 
 def test_v4_code_bytes_meet_their_own_p_bytes():
     """The 4-bit tile stores key k's code where the FP4 operand multiplies it
-    with key k's ExpCast byte: lane group g of the B operand holds keys
-    16t + 4g + v in byte 4t + v, i.e. K index 32g + 4t + v, and the exponent
-    group (a lane group of A) is 2(k/64) + (k/8)%2."""
+    with key k's ExpCast byte.  Lane group g of the B operand holds, in byte
+    4t + v (K index 32g + 4t + v), the key of K row 16t + 4g + v, and with the
+    4-bit residual that row holds block position v4_krow(16t + 4g + v).  The
+    tile keeps key k in byte k/2 (low nibble for even k), so lane group G of A
+    (one E8M0 scale) covers positions 32G .. 32G+31: 32 consecutive keys."""
     sys_path = os.path.join(ROOT, "tests")
     import sys
     sys.path.insert(0, sys_path)
     import gpu_common as G
+    assert sorted(G.v4_krow(np.arange(128))) == list(range(128))
+    assert np.array_equal(G.v4_krow(G.v4_krow(np.arange(128))), np.arange(128))
     seen = set()
     for k in range(128):
         b = int(G._v4_byte(np.int64(k)))
         g, within = divmod(b, 16)
         d, half = divmod(within, 4)
         n = 2 * half + (k & 1)
-        assert g == 2 * (k >> 6) + ((k >> 3) & 1)
-        kappa = 32 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3)
-        assert FP4_K[g][d] + n == kappa, k
+        assert g == k // 32
+        kappa = FP4_K[g][d] + n                  # B operand K index
+        bg, byte = divmod(kappa, 32)             # its lane group and byte
+        t, vv = divmod(byte, 4)
+        assert int(G.v4_krow(16 * t + 4 * bg + vv)) == k, k
         seen.add((b, k & 1))
     assert len(seen) == 128
 

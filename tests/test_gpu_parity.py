@@ -125,7 +125,7 @@ def _v4_midpoint_values(N, seed):
                     np.float32)
     v = np.zeros((N, 128), np.float32)
     k = np.arange(128)
-    grp = 2 * (k >> 6) + ((k >> 3) & 1)
+    grp = k >> 5
     for b in range((N + 127) // 128):
         for G in range(4):
             rows = b * 128 + k[grp == G]

@@ -69,9 +69,35 @@ def test_mx_exponent_puts_group_max_in_the_top_binade():
 def test_v4_groups_partition_each_block():
     g = orc.v4_group(np.arange(128))
     assert sorted(np.bincount(g)) == [32, 32, 32, 32]
-    # keys of one group share k div 64 and (k mod 16) div 8
+    # an MX block is 32 consecutive elements: positions 32G .. 32G+31
     for k in range(128):
-        assert g[k] == 2 * (k // 64) + (k % 16) // 8
+        assert g[k] == k // 32
+
+
+def test_v4_one_outlier_sets_only_its_own_group_exponent():
+    """Brute force on the prepared exponents: with V-Smooth off the residual is
+    V itself; values below 0.5 in magnitude everywhere and one 100 per channel
+    at position p give X = floor(log2 100) - 2 = 4 exactly in the group of p's
+    block that holds p, and X <= -3 in every other group.  Positions at both
+    ends of every group and in both blocks."""
+    N = 256
+    pos = [0, 8, 16, 31, 32, 40, 63, 64, 72, 95, 96, 104, 127, 128, 136, 159, 160, 191, 192, 255]
+    q, k, _ = inputs.make_custom(1, 1, N, seed=3)
+    rng = np.random.default_rng(4)
+    vf = rng.uniform(-0.49, 0.49, (N, 128)).astype(np.float32)
+    for c, p in enumerate(pos):
+        vf[p, c] = 100.0
+    bits = vf.view(np.uint32)
+    v = ((bits + 0x7fff + ((bits >> 16) & 1)) >> 16).astype(np.uint16).reshape(1, 1, N, 128)
+    P = orc.make_params(1, 1, N, C_=2, T=1, rho=0.0, flags=orc.V4)
+    pr = orc.prepare(P, q, k, v)
+    X = pr["vexp"][0]  # [block][group][channel]
+    want = np.full(X.shape, -99)
+    for c, p in enumerate(pos):
+        want[p // 128, (p % 128) // 32, c] = 4
+    hit = want == 4
+    assert np.array_equal(X[hit], want[hit])
+    assert np.all(X[~hit] <= -3)
 
 
 # --------------------------------------------------------------------------- prepare

@@ -100,8 +100,9 @@ enum {
   VC_V4 = 64u,           /* 4-bit value residual: the article's V-Smooth section
                             offers NVFP4 instead of per-channel E4M3 for the demeaned
                             residual; here it takes the OCP MX form gfx950's scaled
-                            MFMA reads.  Each 128-key block splits into four 32-key
-                            groups (key k in group 2*(k/64) + (k%16)/8); every
+                            MFMA reads.  Each 128-key block splits into four
+                            groups of 32 consecutive positions (key k in group
+                            k/32, the MX block of 32 elements); every
                             (block, group, channel) gets the power of two 2^X with
                             X = floor(log2 max|r|) - 2, kept in [-126, 127] (a
                             normal fp32 scale; -126 for an all-zero group), and
@@ -164,7 +165,9 @@ typedef struct {
   size_t perm;       /* i32 [BH][N] position -> original token                   */
   size_t iperm;      /* i32 [BH][N] original token -> position                   */
   size_t q8;         /* u8  [BH][Npad][128] Q codes, position order               */
-  size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order      */
+  size_t k8;         /* u8  [BH][Npad][128] smoothed-K codes, position order; with
+                        VC_V4 row r of a block holds the key at block position
+                        r with bits 2-3 and 4-5 swapped                          */
   size_t k16;        /* bf16 [BH][Npad][128] the same codes decoded (exact in bf16),
                         operand of the exact score MFMA; 0 bytes unless the
                         scores are exact (VC_EXACT_SCORES, or neither score flag
@@ -190,10 +193,8 @@ typedef struct {
                         VC_V4 in real units                                      */
   size_t v4t;        /* VC_V4 only (else 0 bytes): u8 [BH][nblk][128][64] E2M1
                         residual codes, one 8 KB tile per block, channel-major,
-                        two codes per byte.  Key k of the block (group
-                        G = 2(k/64) + (k/8)%2) sits in byte
-                        16G + 8((k/4)%2) + 4((k/32)%2) + 2((k/16)%2) + (k/2)%2,
-                        low nibble for even k                                    */
+                        two codes per byte in position order: key k of the block
+                        sits in byte k/2, low nibble for even k                  */
   size_t v4s;        /* VC_V4 only (else 0 bytes): u8 [BH*nblk + 1][4][16][8]
                         E8M0 exponents X + 127: record [(b*H+h)*nblk + block]
                         holds group G, channel 16j + i at byte [G][i][j]; the

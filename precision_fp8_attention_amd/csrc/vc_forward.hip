@@ -47,9 +47,14 @@
 // and 32-key group, and PV runs on the same instruction in its scaled form: A
 // is the FP4 tile (16 bytes per lane), B the unchanged ExpCast bytes, and each
 // lane's scale register carries the exponents of its channel for four channel
-// tiles (op_sel picks the byte).  Prepare orders each block's codes so that the
-// FP4 operand's K positions meet the lanes' key interleave, so P again never
-// touches LDS; the restore and the epilogue are unchanged (sV = 1).
+// tiles (op_sel picks the byte).  The FP4 operand's lane group G spans K
+// indices that P's lanes fill from score rows of two P lane groups, so prepare
+// stores each block's K code rows in the order v4_krow: the score row that
+// reaches the K index of block position j then holds key j, each scale group is
+// 32 consecutive positions, and the FP4 codes sit in position order.  P again
+// never touches LDS; the masking of keys past N, the smoothed-query score terms
+// and the repair gather follow the row order; the restore and the epilogue
+// are unchanged (sV = 1).
 //
 // K tiles (E4M3 codes, 16 KB; bf16 codes, 32 KB, for exact scores) and V tiles
 // (E4M3, 16 KB; E2M1, 8 KB + 512 B of exponents) are staged in LDS and filled
@@ -189,6 +194,20 @@ __device__ __forceinline__ float xsum16(float x) {
 __device__ __forceinline__ float xsum32(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Block position of the key in K tile row 16t + 4g + v, minus v: the row itself,
+// or with the 4-bit residual the row under v4_krow (64(t/4) + 16g + 4(t%4)).
+template <bool V4>
+__device__ __forceinline__ int key_pos4(int t, int g) {
+  return V4 ? 64 * (t >> 2) + 16 * g + 4 * (t & 3) : 16 * t + 4 * g;
+}
+
+// K tile row of position pos (a repaired token; -1 pads to row 0).
+template <bool V4>
+__device__ __forceinline__ int krow_of(int pos) {
+  if (pos < 0) return 0;
+  return V4 ? (pos & ~(BLK - 1)) | v4_krow(pos & (BLK - 1)) : pos;
 }
 
 // Workgroup id -> (head, query block), so that consecutive logical tiles (same
@@ -461,7 +480,7 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
         // smoothed queries: scores become t = fma(S, alpha, d) in code units;
         // lane group g holds keys 16t+4g..16t+4g+3
         const float alpha = (sQa * sk[kb]) * a.c0;
-        const float4 d4 = *reinterpret_cast<const float4*>(&sbias[kb % NST][wg][16 * t + 4 * g]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sbias[kb % NST][wg][key_pos4<V4>(t, g)]);
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int qs = 0; qs < NS; ++qs)
@@ -475,29 +494,31 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
     const float alpha = (sQa * sk[kb]) * a.c0;
     const int nvalid = a.N - kb * BLK;
     if (nvalid < BLK) {
-      // key 16t + 4g + v is past N when 16t + v >= nvalid - 4g: one register
-      // per lane instead of 32 key indices held through the key loop
-      const int lim = nvalid - 4 * g;
+      // the key of row 16t + 4g + v (position key_pos4 + v) is past N when its
+      // g-free part reaches nvalid minus the g part: one register per lane
+      // instead of 32 key indices held through the key loop
+      const int lim = nvalid - (V4 ? 16 : 4) * g;
 #pragma unroll
       for (int qs = 0; qs < NS; ++qs)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (16 * t + v >= lim) S[qs][t][v] = -INFINITY;
+            if (key_pos4<V4>(t, 0) + v >= lim) S[qs][t][v] = -INFINITY;
     }
     // smoothed queries already hold t in code units: fma(t, 1, beta) = t + beta
 #pragma unroll
     for (int qs = 0; qs < NS; ++qs) pop[qs] = softmax_codes(S[qs], rs[qs], SQ ? 1.0f : alpha, a.bias, a.tau);
     if (a.pcodes) {
-      // lane (g, q) holds keys 16t+4g..16t+4g+3 of query row q: one dword each
+      // lane (g, q) holds the keys of rows 16t+4g..16t+4g+3 of query row q (four
+      // consecutive positions from key_pos4): one dword each
 #pragma unroll
       for (int qs = 0; qs < NS; ++qs) {
         uint8_t* prow = a.pcodes + ((size_t)bh * a.Npad + (size_t)qb * BLK + wq * 16 * NS + qs * 16 + l16) * a.Npad +
-                        (size_t)kb * BLK + 4 * g;
+                        (size_t)kb * BLK;
         if (active) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) *reinterpret_cast<int*>(prow + 16 * t) = pop[qs][t];
+          for (int t = 0; t < 8; ++t) *reinterpret_cast<int*>(prow + key_pos4<V4>(t, g)) = pop[qs][t];
         }
       }
     }
@@ -625,16 +646,16 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
 #pragma unroll
       for (int i = 0; i < 2048 / (64 * NWV); ++i) {
         const int ch = tid + 64 * NWV * i, row = ch >> 4, cc = ch & 15;
-        const int pos = rp[row];
-        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * 256 + cc * 16);
+        const int pos = krow_of<V4>(rp[row]);
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)pos * 256 + cc * 16);
         *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 1024 / (64 * NWV); ++i) {
         const int ch = tid + 64 * NWV * i, row = ch >> 3, cc = ch & 7;
-        const int pos = rp[row];
-        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)(pos < 0 ? 0 : pos) * D + cc * 16);
+        const int pos = krow_of<V4>(rp[row]);
+        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)pos * D + cc * 16);
         *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv;
       }
     }

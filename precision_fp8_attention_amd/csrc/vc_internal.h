@@ -17,6 +17,13 @@ constexpr int KM_CHUNK = 2048;      // tokens per k-means assignment workgroup
 constexpr int MAX_CLUSTERS = 64;    // centroids and bins live in LDS
 constexpr int V4_TILE = D * BLK / 2;  // bytes of one block's E2M1 value tile
 constexpr int V4_SREC = 512;        // bytes of one block's E8M0 exponents
+
+// With the 4-bit residual, row r of a block's K code tile holds the key at block
+// position v4_krow(r): bits 2-3 and 4-5 of r swapped (the map is its own
+// inverse).  The score MFMA's row r = 16t + 4g + v then lands in the P operand
+// at the K index of that position, so the FP4 operand's 32-wide scale groups
+// are 32 consecutive positions and its codes are stored in position order.
+__host__ __device__ constexpr int v4_krow(int r) { return (r & 0x43) | ((r >> 2) & 0x0c) | ((r << 2) & 0x30); }
 constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 
 // Shape derived from the public parameters.

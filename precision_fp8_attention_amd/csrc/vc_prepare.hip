@@ -117,8 +117,8 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return x < -126 ? -126 : (x > 127 ? 127 : x);
 }
 
-// 32-key group of key r of a block (4-bit residual).
-__device__ __forceinline__ int v4_group(int r) { return 2 * (r >> 6) + ((r >> 3) & 1); }
+// 32-key group of key r of a block (4-bit residual): 32 consecutive positions.
+__device__ __forceinline__ int v4_group(int r) { return r >> 5; }
 
 // ---------------------------------------------------------------------------
 // K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; with WITH_V
@@ -629,7 +629,9 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
       w0 = e4m3x2(val(i, 0) * inv, val(i, 1) * inv) | (e4m3x2(val(i, 2) * inv, val(i, 3) * inv) << 16);
       w1 = e4m3x2(val(i, 4) * inv, val(i, 5) * inv) | (e4m3x2(val(i, 6) * inv, val(i, 7) * inv) << 16);
     }
-    uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + p) * D + cg * 8;
+    // with the 4-bit residual a K code row goes to the tile row v4_krow(r)
+    const int prow = (isk && (a.flags & VC_V4)) ? blk * BLK + v4_krow(r) : p;
+    uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + prow) * D + cg * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
     if (isk && (a.flags & VC_EXACT_SCORES)) {
       // the K codes decoded to bf16 (E4M3 values are exact in bf16)
@@ -640,7 +642,7 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
         const uint32_t b0 = (wd >> (16 * (e & 1))) & 0xff, b1 = (wd >> (16 * (e & 1) + 8)) & 0xff;
         h[e] = (__float_as_uint(e4m3_val(b0)) >> 16) | (__float_as_uint(e4m3_val(b1)) & 0xffff0000u);
       }
-      *reinterpret_cast<uint4*>(a.k16 + ((size_t)bh * a.Npad + p) * D + cg * 8) =
+      *reinterpret_cast<uint4*>(a.k16 + ((size_t)bh * a.Npad + prow) * D + cg * 8) =
           make_uint4(h[0], h[1], h[2], h[3]);
     }
   }
@@ -725,15 +727,15 @@ __global__ __launch_bounds__(256) void k_qbias(Args a) {
 
 // ---------------------------------------------------------------------------
 // V block means and block maxima of |V - mu|; with VC_V4 also the maximum of each
-// 32-key group (rows r with 2(r/64) + (r/8)%2 = G) and its E8M0 exponent.
+// 32-key group (rows 32G .. 32G+31) and its E8M0 exponent.
 // grid (nblk, BH), 256 threads: thread = (8-channel chunk t%16, rows t/16 + 16i),
-// so rows i < 4 and i >= 4 of a thread lie in groups (t/128)%2 and 2 + (t/128)%2.
+// so rows 2G and 2G+1 of a thread lie in group G.
 __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
   // the block sums and, after them, the block maxima share one 16 KB buffer, so
   // six workgroups fit a CU
   __shared__ __align__(16) long long sbuf[16 * D];
   long long (*ssum)[D] = reinterpret_cast<long long (*)[D]>(sbuf);
-  float (*smax)[16][D] = reinterpret_cast<float (*)[16][D]>(sbuf);
+  float (*smax)[8][D] = reinterpret_cast<float (*)[8][D]>(sbuf);
   __shared__ float smu[D];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
@@ -773,27 +775,33 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
   // rather than keep 64 floats live across the barrier
 #pragma unroll
   for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
-  float m[2][8];
+  // per group: the thread's two rows, then the neighbour with r0 ^ 1 (lane
+  // t ^ 16, same channels), so 8 partial maxima per group and channel remain
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m[0][e] = m[1][e] = 0.0f;
+  for (int G = 0; G < 4; ++G) {
+    float m[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (r0 + 16 * i < n) {
+    for (int e = 0; e < 8; ++e) m[e] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[i >> 2][e] = fmaxf(m[i >> 2][e], fabsf(val(i, e) - smu[cg * 8 + e]));
+    for (int i = 2 * G; i < 2 * G + 2; ++i)
+      if (r0 + 16 * i < n) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(val(i, e) - smu[cg * 8 + e]));
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], __shfl_xor(m[e], 16, 64));
+    if ((r0 & 1) == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) smax[G][r0 >> 1][cg * 8 + e] = m[e];
     }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    smax[0][r0][cg * 8 + e] = m[0][e];
-    smax[1][r0][cg * 8 + e] = m[1][e];
   }
   __syncthreads();
   if (t < D) {
-    float gm[4];  // group G = 2h + b: rows of half h, threads with (r0/8)%2 = b
+    float gm[4];
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
       float mm = 0.0f;
-      for (int rr = 0; rr < 8; ++rr) mm = fmaxf(mm, smax[G >> 1][8 * (G & 1) + rr][t]);
+      for (int rr = 0; rr < 8; ++rr) mm = fmaxf(mm, smax[G][rr][t]);
       gm[G] = mm;
     }
     const size_t o = ((size_t)bh * a.nblk + blk) * D + t;
@@ -939,7 +947,7 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
   const int k0 = 2 * t;
   const int G = v4_group(k0);
-  const int byte = 16 * G + 8 * ((k0 >> 2) & 1) + 4 * ((k0 >> 5) & 1) + 2 * ((k0 >> 4) & 1) + ((k0 >> 1) & 1);
+  const int byte = t;  // keys 2t, 2t+1: byte t of the channel row (position order)
   // a key past N reads the block's first row (finite input) and is zeroed by the
   // multiply: residual 0, code 0; every load stays unconditional
   const bool ok0 = k0 < n, ok1 = k0 + 1 < n;

@@ -109,25 +109,27 @@ def denoise_schedule(p, qd, kd, vd, ws, o, flops, steps=20, warm_iters=3, drift=
 
 
 def cpu_baseline(wl, q, k, v, P, flops, gpu_out):
-    """Oracle on the host: prepare of 2 heads (one per batch item) and the
-    simulated forward of 8192 query rows per head, scaled to all heads/rows."""
+    """Oracle on the host: prepare of 8 heads spread over the batch (one head
+    per thread) and the simulated forward of every query row of those heads,
+    scaled to all heads; the same rows give the parity sample."""
     import numpy as np
 
     from oracle import oracle as orc
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     B, H, N = wl["B"], wl["H"], wl["N"]
-    heads = [0, B * H - 1]
+    heads = sorted(set(np.linspace(0, B * H - 1, min(8, B * H)).round().astype(int).tolist()))
     t0 = time.perf_counter()
     prep = orc.prepare(P, q, k, v, heads=heads)
     t_prep = time.perf_counter() - t0
-    rows = np.linspace(0, N - 1, 8192).astype(np.int32)
+    rows = np.arange(N, dtype=np.int32)
     slot = np.repeat(np.arange(len(heads)), len(rows)).astype(np.int32)
     idx = np.tile(rows, len(heads)).astype(np.int32)
     t0 = time.perf_counter()
     sim = orc.forward_rows(P, prep, slot, idx)
     t_fwd = time.perf_counter() - t0
-    # prepare ran one head per thread: the full job keeps min(cores, B*H) busy
-    full_prep = t_prep * (B * H) / min(cores, B * H)
+    # prepare runs one head per thread: ceil(heads / cores) rounds of one head each
+    rounds = lambda n: -(-n // max(cores, 1))  # noqa: E731
+    full_prep = t_prep / rounds(len(heads)) * rounds(B * H)
     full_fwd = t_fwd * (B * H * N) / len(idx)
     total = full_prep + full_fwd
     got = gpu_out.reshape(B * H, N, 128)[np.asarray(heads)[slot], idx]
@@ -136,9 +138,96 @@ def cpu_baseline(wl, q, k, v, P, flops, gpu_out):
     base = {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, os.cpu_count() or cores),
             "kind": "oracle",
             "sample": (f"prepare of heads {heads} ({t_prep:.2f} s wall, one head per thread) and "
-                       f"simulated forward of {len(idx)} query rows ({t_fwd:.2f} s wall on {cores} "
-                       f"threads), scaled linearly to {B*H} heads x {N} rows: {total:.0f} s per step")}
-    return base, {"rows": int(len(idx)), "max_abs": mx, "rel_l2": rel}
+                       f"simulated forward of all {N} query rows of those heads ({len(idx)} rows, "
+                       f"{t_fwd:.2f} s wall on {cores} threads), scaled linearly to {B*H} heads: "
+                       f"{total:.0f} s per step")}
+    return base, {"heads": heads, "rows": int(len(idx)), "max_abs": mx, "rel_l2": rel}
+
+
+def fidelity(wl, q, k, v, qd, kd, vd, dev, heads, rows):
+    """Relative L2 distance of GPU outputs to exact fp64 attention on sampled rows
+    of the benchmark workload, for the full method and its ablations (the
+    the benchmark spec's V-Smooth-off figure, repair off, the literal ExpCast offset
+    k = 0, exact scores, the 4-bit residual).  The pages report fidelity against
+    unquantised outputs (noticiai.com.br article, Benchmarks; V-Smooth)."""
+    import numpy as np
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    from oracle import oracle as orc
+    B, H, N = wl["B"], wl["H"], wl["N"]
+    P = orc.make_params(B, H, N, C_=wl["C"], T=wl["T"], rho=wl["rho"])
+    slot = np.repeat(np.asarray(heads), len(rows)).astype(np.int32)
+    idx = np.tile(rows, len(heads)).astype(np.int32)
+    t0 = time.perf_counter()
+    ex = orc.exact_rows(P, q, k, v, slot, idx)
+    t_exact = time.perf_counter() - t0
+    variants = {
+        "full": dict(flags=vc.DEFAULT_FLAGS),
+        "vsmooth_off": dict(flags=0),                        # identity order, no means, no repair
+        "vsmooth_off_repair_on": dict(flags=vc.REPAIR | vc.PERMUTE_Q),
+        "repair_off": dict(flags=vc.VSMOOTH | vc.PERMUTE_Q),
+        "expcast_k0": dict(flags=vc.DEFAULT_FLAGS, expcast_k=0),
+        "exact_scores": dict(flags=vc.DEFAULT_FLAGS | vc.EXACT_SCORES),
+        "v4_residual": dict(flags=vc.DEFAULT_FLAGS | vc.V4),
+    }
+    out = {}
+    for name, kw in variants.items():
+        p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"], **kw)
+        ws = vc.alloc_workspace(p, dev)
+        o = torch.empty_like(qd)
+        vc.prepare(p, qd, kd, vd, ws)
+        vc.forward(p, ws, o)
+        torch.cuda.synchronize()
+        got = o.float().view(B * H, N, 128)[torch.as_tensor(slot, device=dev).long(),
+                                            torch.as_tensor(idx, device=dev).long()]
+        got = got.cpu().numpy().astype(np.float64)
+        out[name] = round(float(np.linalg.norm(got - ex) / np.linalg.norm(ex)), 6)
+        del ws, o
+    return {"reference": "exact fp64 softmax attention of the bf16 inputs", "heads": list(map(int, heads)),
+            "rows_per_head": int(len(rows)), "rel_l2_vs_exact": out,
+            "exact_rows_cpu_s": round(t_exact, 2)}
+
+
+def per_workload(ids, dev, steps=10, warmup=2):
+    """Forward, prepare and step times of the other workloads (all heads, full
+    size): token counts from the FLUX.3 Klein launch article (Vitesse et
+    memoire) and a 5 s 720p video clip."""
+    import numpy as np
+    import torch
+
+    import precision_fp8_attention_amd as vc
+    from synthetic import inputs
+    res = {}
+    for i in ids:
+        wl = inputs.WORKLOADS[i]
+        B, H, N = wl["B"], wl["H"], wl["N"]
+        q, k, v = inputs.make_inputs(i)
+        qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+        del q, k, v
+        p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"])
+        ws = vc.alloc_workspace(p, dev)
+        o = torch.empty_like(qd)
+        flops = 4.0 * B * H * N * N * 128
+
+        def step():
+            vc.prepare(p, qd, kd, vd, ws)
+            vc.forward(p, ws, o)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ms_step = _events_ms(step, max(steps // 2, 2))
+        ms_fwd = _events_ms(lambda: vc.forward(p, ws, o), steps)
+        ms_prep = _events_ms(lambda: vc.prepare(p, qd, kd, vd, ws), max(steps // 2, 2))
+        tf = flops / (ms_fwd * 1e-3) / 1e12
+        res[wl["name"]] = {"B": B, "H": H, "N": N, "clusters": wl["C"], "forward_ms": round(ms_fwd, 4),
+                           "forward_tflops": round(tf, 2), "forward_pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                           "prepare_ms": round(ms_prep, 4), "ms_per_step": round(ms_step, 4),
+                           "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2)}
+        del qd, kd, vd, ws, o
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -148,6 +237,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fidelity ablations and the other workloads' timings")
     ap.add_argument("--forward-only", action="store_true",
                     help="time only vc_attn_forward launches (profiling runs)")
     ap.add_argument("--v4", action="store_true",
@@ -322,6 +413,14 @@ def main():
         P = orc.make_params(B, H, N, C_=wl["C"], T=wl["T"], rho=wl["rho"])
         gpu_out = o.float().cpu().numpy().astype(np.float64)
         res["cpu_baseline"], res["parity_sample"] = cpu_baseline(wl, q, k, v, P, flops, gpu_out)
+    if not args.no_extras:
+        print("bench: fidelity ablations", file=sys.stderr, flush=True)
+        res["fidelity"] = fidelity(wl, q, k, v, qd, kd, vd, dev, [0, B * H - 1],
+                                   np.linspace(0, N - 1, 256).astype(np.int32))
+        del ws, o
+        torch.cuda.empty_cache()
+        print("bench: other workloads", file=sys.stderr, flush=True)
+        res["other_workloads"] = per_workload([i for i in (1, 2, 4) if i != args.workload], dev)
     print(json.dumps(res))
 
 

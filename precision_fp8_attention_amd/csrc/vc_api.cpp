@@ -90,6 +90,8 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.centroids = take(BH * C * D * 4);
   out->kmpart = take(BH * (size_t)s.nkm * C * D * 4);
   out->kmcnt = take(BH * (size_t)s.nkm * C * 4);
+  out->kmsum = take(BH * C * D * 8);
+  out->kmn = take(BH * C * 8);
   out->vmaxp = take(BH * (size_t)s.nkc * 4);
   out->kmsh = take(BH * 4);
   out->uhi = take(BH * N * D);
@@ -153,6 +155,8 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.cent = reinterpret_cast<float*>(b + L.centroids);
   a.kmpart = reinterpret_cast<int*>(b + FL.kmpart);
   a.kmcnt = reinterpret_cast<int*>(b + FL.kmcnt);
+  a.kmsum = reinterpret_cast<long long*>(b + FL.kmsum);
+  a.kmn = reinterpret_cast<long long*>(b + FL.kmn);
   a.vmaxp = reinterpret_cast<float*>(b + FL.vmaxp);
   a.kmsh = reinterpret_cast<int*>(b + FL.kmsh);
   a.uhi = reinterpret_cast<int8_t*>(b + FL.uhi);

@@ -62,8 +62,11 @@ struct Args {
   long long* ksum;
   int* init_idx;
   float* cent;
-  int* kmpart;        // [BH][nkm][C][128] partial sums of members (fixed point)
-  int* kmcnt;         // [BH][nkm][C] member counts
+  int* kmpart;        // [BH][nkm][C][128] change of the member sums (fixed point) in one
+                      // Lloyd iteration, per assignment workgroup
+  int* kmcnt;         // [BH][nkm][C] change of the member counts, likewise
+  long long* kmsum;   // [BH][C][128] member sums of the current labels (fixed point)
+  long long* kmn;     // [BH][C] member counts of the current labels
   float* vmaxp;       // [BH][nkc] partial max |V|
   int* kmsh;          // [BH] fixed-point exponent of the head
   int8_t* uhi;        // [BH][N][128] high part (u >> 7) of the fixed-point V
@@ -98,7 +101,7 @@ struct Args {
 // Private extension of the public layout (partial k-means sums).
 struct FullLayout {
   vc_attn_ws_layout pub;
-  size_t kmpart, kmcnt, vmaxp, kmsh, uhi, ulo, centfix, kmcc;
+  size_t kmpart, kmcnt, kmsum, kmn, vmaxp, kmsh, uhi, ulo, centfix, kmcc;
 };
 
 bool shape_of(const vc_attn_params* p, Shape* s);

@@ -226,10 +226,6 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
   }
 }
 
-// Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
-// fixed-point value of token idx[k].  The draws do not depend on the swaps, so
-// lane i computes draw i and then resolves, on its own, which value the swaps
-// leave at position i.  grid BH, 128 threads.
 // Sum of one int64 per lane over a wave (exact).
 __device__ __forceinline__ long long wave_sum_i64(long long x) {
 #pragma unroll
@@ -247,7 +243,11 @@ __device__ __forceinline__ long long sum128_i64(long long x, long long* red) {
   return red[0] + red[1];
 }
 
-__global__ __launch_bounds__(128) void k_km_init(Args a) {
+// Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
+// fixed-point value of token idx[k].  The draws do not depend on the swaps, so
+// lane i computes draw i and then resolves, on its own, which value the swaps
+// leave at position i.  grid BH, 1024 threads.
+__global__ __launch_bounds__(1024) void k_km_init(Args a) {
   __shared__ int jdraw[MAX_CLUSTERS];
   __shared__ int idx[MAX_CLUSTERS];
   const int bh = blockIdx.x, C = a.C, t = threadIdx.x;
@@ -279,17 +279,24 @@ __global__ __launch_bounds__(128) void k_km_init(Args a) {
   __syncthreads();
   const int sh = a.kmsh[bh];
   __shared__ long long part[2][MAX_CLUSTERS];
-  for (int kk = 0; kk < C; ++kk) {
-    const size_t src = ((size_t)bh * a.N + idx[kk]) * D + t;
+  // eight centroids at a time: thread (r, c) = (t / 128, channel t % 128), so the
+  // row loads of eight centroids are in flight together
+  const int c = t & 127;
+#pragma unroll 2
+  for (int kk = t >> 7; kk < C; kk += 8) {
+    const size_t src = ((size_t)bh * a.N + idx[kk]) * D + c;
     const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
-    a.centfix[((size_t)bh * C + kk) * D + t] = u;
-    a.cent[((size_t)bh * C + kk) * D + t] = ldexpf((float)u, -sh);
+    a.centfix[((size_t)bh * C + kk) * D + c] = u;
+    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -sh);
     const long long s2 = wave_sum_i64((long long)u * u);
-    if ((t & 63) == 0) part[t >> 6][kk] = s2;
+    if ((t & 63) == 0) part[c >> 6][kk] = s2;
   }
   __syncthreads();
   if (t < C) a.kmcc[(size_t)bh * C + t] = part[0][t] + part[1][t];
   if (t < C) a.init_idx[(size_t)bh * C + t] = idx[t];
+  // no member yet: the first iteration adds every token
+  for (int e = t; e < C * D; e += 1024) a.kmsum[(size_t)bh * C * D + e] = 0;
+  if (t < C) a.kmn[(size_t)bh * C + t] = 0;
 }
 
 // Warm start: the previous step's centroids (fp32, in the workspace) in the
@@ -310,6 +317,8 @@ __global__ __launch_bounds__(128) void k_km_warm(Args a) {
   }
   __syncthreads();
   if (t < C) a.kmcc[(size_t)bh * C + t] = part[0][t] + part[1][t];
+  for (int e = t; e < C * D; e += 128) a.kmsum[(size_t)bh * C * D + e] = 0;
+  if (t < C) a.kmn[(size_t)bh * C + t] = 0;
 }
 
 // Assignment step on int8 MFMA plus per-workgroup member sums.
@@ -324,13 +333,20 @@ constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
 
 constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measured 13 us
                              // less per Lloyd iteration at N=16544, 48 heads)
-// Member sums: two channels per 64-bit LDS add.  Each half holds u + 16384 (in
-// [8192, 24575]) summed over at most KM_CHUNK = 2048 tokens (< 2^26), so the low
-// half never carries into the high one; the bias is removed with the count.
+// Member sums are kept per head (kmsum, kmn) and changed only by the tokens
+// whose label changes: after the first Lloyd iteration few do, so few LDS adds
+// remain.  A workgroup collects the change of its chunk in packed bins, two
+// channels per 64-bit LDS add: a token entering cluster c adds u + 16384 (in
+// [8192, 24575]) to c's bin, a token leaving c adds 16384 - u (in [8193, 24576]).
+// A bin thus holds sum_in u - sum_out u + 16384 (n_in + n_out); every token adds
+// to a cluster's bin at most once, so a half sums at most KM_CHUNK = 2048 terms
+// (< 2^26) and never carries into the other; the bias is removed with the counts.
 constexpr int BROW2 = D / 2 + 1;  // LDS row of the packed bins (8-byte words)
-static_assert(KM_CHUNK * 24575ll < (1ll << 32), "packed member sums would carry");
-constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 * BROW2 + 4); }
+static_assert(KM_CHUNK * 24576ll < (1ll << 32), "packed member sums would carry");
+constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 * BROW2 + 8); }
 
+// LEAVE: add 16384 - u instead of u + 16384.
+template <bool LEAVE>
 __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, const v4i& h, const v4i& l) {
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
@@ -338,8 +354,12 @@ __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, co
     const uint32_t lb = (uint32_t)l[wd];
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      const uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
-      const uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
+      uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
+      uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
+      if (LEAVE) {
+        ua = 32768u - ua;
+        ub = 32768u - ub;
+      }
       atomicAdd(&bins[base + 2 * wd + pr], (unsigned long long)ua | ((unsigned long long)ub << 32));
     }
   }
@@ -347,14 +367,16 @@ __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, co
 
 // NT = number of 16-centroid tiles (C <= 16 NT).  Centroids beyond C get a norm
 // of 2^62, so their distance never wins and no lane needs a predicate.
+// first: the first iteration of this prepare call, where every token enters its
+// cluster (labels from an earlier call are not read).
 template <int NT>
-__global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
+__global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) {
   extern __shared__ __align__(16) unsigned char km_smem[];
   const int C = a.C;
   int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                       // [C][CROW]
   int8_t* clo = chi + C * CROW;                                           // [C][CROW]
   unsigned long long* bins = reinterpret_cast<unsigned long long*>(clo + C * CROW);  // [C][BROW2]
-  int* cnt = reinterpret_cast<int*>(bins + C * BROW2);                    // [C]
+  int* cnt = reinterpret_cast<int*>(bins + C * BROW2);                    // [2][C]: entering, leaving
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
   const int* cf = a.centfix + (size_t)bh * C * D;
@@ -364,7 +386,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
     clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
   }
   for (int e = t; e < C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
-  if (t < C) cnt[t] = 0;
+  if (t < 2 * C) cnt[t] = 0;
   // this lane's centroid norms: centroid 16kt + 4g + v
   long long ccr[NT][4];
 #pragma unroll
@@ -378,27 +400,35 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
   // wave w takes 16-token subtiles w, w+KM_WAVES, ... of the chunk; the operands
-  // of the next subtile are loaded while the current one is processed
+  // and previous labels of the next subtile are loaded while the current one is
+  // processed (two ahead measured slower: more registers, no latency to hide)
   // chunks of equal size (a multiple of 16 tokens, at most KM_CHUNK)
   const int csz = ((a.N + a.nkm - 1) / a.nkm + 15) & ~15;
-  const int first = chunk * csz, last = min(first + csz, a.N);
-  auto load_sub = [&](int s, v4i& h0, v4i& h1, v4i& l0, v4i& l1) {
-    int jj = first + s * 16 + l16;
-    jj = jj < last ? jj : last - 1;  // tail lanes read a valid row, add nothing
-    h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
-    h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
-    l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
-    l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+  const int first_tok = chunk * csz, last = min(first_tok + csz, a.N);
+  struct Sub {
+    v4i h0, h1, l0, l1;
+    int old;  // the token's label from the previous iteration (-1: none)
   };
-  v4i nh0, nh1, nl0, nl1;
-  if (first + w * 16 < last) load_sub(w, nh0, nh1, nl0, nl1);
+  auto load_sub = [&](int s, Sub& x) {
+    int jj = first_tok + s * 16 + l16;
+    const bool ok = jj < last;
+    jj = ok ? jj : last - 1;  // tail lanes read a valid row, add nothing
+    x.h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
+    x.h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
+    x.l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
+    x.l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+    x.old = (!first && ok) ? a.labels[(size_t)bh * a.N + jj] : -1;
+  };
+  auto has = [&](int s) { return s < KM_CHUNK / 16 && first_tok + s * 16 < last; };  // uniform per wave
+  Sub nx;
+  if (has(w)) load_sub(w, nx);
 #pragma unroll 1
   for (int sub = w; sub < KM_CHUNK / 16; sub += KM_WAVES) {
-    if (first + sub * 16 >= last) break;  // uniform per wave
-    const v4i bh0 = nh0, bh1 = nh1, bl0 = nl0, bl1 = nl1;
-    if (sub + KM_WAVES < KM_CHUNK / 16 && first + (sub + KM_WAVES) * 16 < last)
-      load_sub(sub + KM_WAVES, nh0, nh1, nl0, nl1);
-    const int j = first + sub * 16 + l16;
+    if (!has(sub)) break;
+    const v4i bh0 = nx.h0, bh1 = nx.h1, bl0 = nx.l0, bl1 = nx.l1;
+    const int old = nx.old;
+    if (has(sub + KM_WAVES)) load_sub(sub + KM_WAVES, nx);
+    const int j = first_tok + sub * 16 + l16;
     long long bestD = 0x7fffffffffffffffll;
     int best = 0;
 #pragma unroll
@@ -436,13 +466,20 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
       const int ob = __shfl_xor(best, off, 64);
       if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
     }
-    if (j < last) {
+    // only a token whose label changes touches the bins; a wave with none skips
+    const bool moved = j < last && best != old;
+    if (__ballot(moved) != 0ull && moved) {
       if (g == 0) {
         a.labels[(size_t)bh * a.N + j] = best;
         atomicAdd(&cnt[best], 1);
+        if (old >= 0) atomicAdd(&cnt[C + old], 1);
       }
-      add_bins2(bins, best * BROW2 + 8 * g, bh0, bl0);
-      add_bins2(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
+      add_bins2<false>(bins, best * BROW2 + 8 * g, bh0, bl0);
+      add_bins2<false>(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
+      if (old >= 0) {
+        add_bins2<true>(bins, old * BROW2 + 8 * g, bh0, bl0);
+        add_bins2<true>(bins, old * BROW2 + 32 + 8 * g, bh1, bl1);
+      }
     }
   }
   __syncthreads();
@@ -451,21 +488,26 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a) {
     const int c = e / D, ch = e % D;
     const unsigned long long wv = bins[c * BROW2 + (ch >> 1)];
     const uint32_t half = (ch & 1) ? (uint32_t)(wv >> 32) : (uint32_t)wv;
-    part[e] = (int)half - 16384 * cnt[c];
+    part[e] = (int)half - 16384 * (cnt[c] + cnt[C + c]);
   }
-  if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t];
+  if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t] - cnt[C + t];
 }
 
-// Update step: centroid = member mean rounded to the nearest integer (ties to
-// even; |sum| < 2^34 so the fp64 quotient rounds once), empty clusters stay.
-// grid (C, BH), 128 threads.
+// Update step: the member sums and counts take the iteration's changes; centroid
+// = member mean rounded to the nearest integer (ties to even; |sum| < 2^34 so
+// the fp64 quotient rounds once), empty clusters stay.  grid (C, BH), 128 threads.
 __global__ __launch_bounds__(128) void k_km_update(Args a) {
   const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
-  long long s = 0, n = 0;
+  long long* sum = a.kmsum + ((size_t)bh * C + kk) * D + c;
+  long long s = *sum, n = a.kmn[(size_t)bh * C + kk];
   for (int ch = 0; ch < a.nkm; ++ch) {
     s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
     n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
   }
+  *sum = s;
+  // every thread has read the old count before thread 0 stores the new one
+  __syncthreads();
+  if (c == 0) a.kmn[(size_t)bh * C + kk] = n;
   int u;
   if (n > 0) {
     u = (int)__builtin_rint((double)s / (double)n);
@@ -481,49 +523,67 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
 
 // ---------------------------------------------------------------------------
 // Stable counting sort of positions by cluster id.  grid BH, 1024 threads.
+// Wave w owns one contiguous run of tokens: it counts its run per cluster, the
+// runs' counts give every (wave, cluster) its first position, and the wave then
+// walks its run again in order, ranking tokens of one cluster inside each
+// 64-token step by a ballot match and keeping its running offsets in LDS of its
+// own (no barrier inside the walks).
 __global__ __launch_bounds__(1024) void k_perm(Args a) {
-  __shared__ int base[MAX_CLUSTERS + 1];
-  __shared__ int wcnt[16][MAX_CLUSTERS + 1];
+  __shared__ int wcnt[16][MAX_CLUSTERS + 1];  // per wave: count, then next position
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
   const int* lab = a.labels + (size_t)bh * a.N;
   int* perm = a.perm + (size_t)bh * a.N;
   int* iperm = a.iperm + (size_t)bh * a.N;
-  if (t <= MAX_CLUSTERS) base[t] = 0;
-  __syncthreads();
-  for (int j = t; j < a.N; j += 1024) atomicAdd(&base[lab[j] + 1], 1);
-  __syncthreads();
-  if (t == 0)
-    for (int kk = 0; kk < C; ++kk) base[kk + 1] += base[kk];
-  __syncthreads();
+  const int per = (((a.N + 15) / 16) + 63) & ~63;
+  const int j0 = min(w * per, a.N), j1 = min(j0 + per, a.N);
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int j0 = 0; j0 < a.N; j0 += 1024) {
-    const int j = j0 + t;
-    const int l = j < a.N ? lab[j] : MAX_CLUSTERS;  // sentinel bucket for the tail
+  for (int e = t; e < 16 * (MAX_CLUSTERS + 1); e += 1024) (&wcnt[0][0])[e] = 0;
+  __syncthreads();
+  // lanes with the same label as this lane (ballot over the 7 label bits);
+  // a lane past the run takes the sentinel bucket MAX_CLUSTERS
+  auto peers_of = [&](int l) {
     unsigned long long peers = ~0ull;
 #pragma unroll
     for (int b = 0; b < 7; ++b) {
       const unsigned long long m = __ballot((l >> b) & 1);
       peers &= ((l >> b) & 1) ? m : ~m;
     }
-    const int rank = __popcll(peers & lt);
-    for (int e = t; e < 16 * (MAX_CLUSTERS + 1); e += 1024) (&wcnt[0][0])[e] = 0;
-    __syncthreads();
-    if (rank == 0) wcnt[w][l] = __popcll(peers);
-    __syncthreads();
-    if (j < a.N) {
-      int pre = 0;
-      for (int ww = 0; ww < w; ++ww) pre += wcnt[ww][l];
-      const int pos = base[l] + pre + rank;
+    return peers;
+  };
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = peers_of(l);
+    // the lowest lane of each label adds the label's count (distinct words)
+    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+  }
+  __syncthreads();
+  // first position of (wave, cluster): all tokens of smaller clusters, plus those
+  // of the same cluster in earlier runs
+  if (t < C) {
+    int below = 0;
+    for (int c = 0; c < t; ++c)
+      for (int ww = 0; ww < 16; ++ww) below += wcnt[ww][c];
+    for (int ww = 0; ww < 16; ++ww) {
+      const int n = wcnt[ww][t];
+      wcnt[ww][t] = below;
+      below += n;
+    }
+  }
+  __syncthreads();
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = peers_of(l);
+    if (l < MAX_CLUSTERS) {
+      const int pos = wcnt[w][l] + __popcll(peers & lt);
       perm[pos] = j;
       iperm[j] = pos;
     }
-    __syncthreads();
-    if (t < C) {
-      int tot = 0;
-      for (int ww = 0; ww < 16; ++ww) tot += wcnt[ww][t];
-      base[t] += tot;
-    }
-    __syncthreads();
+    // every lane has read its offset before the lowest lane of each label moves it
+    __builtin_amdgcn_wave_barrier();
+    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1007,33 +1067,46 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
 // Repair set: the m positions with the largest error (ties: lower position),
 // by an exact radix select on the 64-bit key (~err_bits, position), then a
 // compaction in position order.  grid BH, 1024 threads.
+//
+// Most errors share their leading digits (sign and exponent), so one shared
+// 256-bin histogram would see most lanes of an LDS add hit the same word; each
+// of RS_COPIES lanes of a wave counts into its own copy instead (no two lanes
+// of an instruction share an address), and the copies are summed for the scan.
+// The compaction gives each wave one contiguous run of positions, so it needs
+// two barriers rather than four per 1024 positions.
+constexpr int RS_COPIES = 32;
 __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
-  __shared__ int hist[256];
+  __shared__ int hist[256][RS_COPIES];
   __shared__ unsigned long long s_prefix, s_mask;
-  __shared__ int s_kth, s_kth_next, s_base, s_hsel;
+  __shared__ int s_kth, s_kth_next, s_hsel;
   __shared__ int wtot[16];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int cp = lane & (RS_COPIES - 1);
   const float* err = a.err + (size_t)bh * a.N;
+  auto key_of = [&](int j) {
+    return ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
+  };
   if (t == 0) {
     s_prefix = 0ull;
     s_mask = 0ull;
     s_kth = a.m;
   }
   for (int shift = 56; shift >= 0; shift -= 8) {
-    if (t < 256) hist[t] = 0;
+    for (int e = t; e < 256 * RS_COPIES; e += 1024) (&hist[0][0])[e] = 0;
     __syncthreads();
     const unsigned long long pre = s_prefix, msk = s_mask;
     for (int j = t; j < a.N; j += 1024) {
-      const unsigned long long key =
-          ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
-      if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255], 1);
+      const unsigned long long key = key_of(j);
+      if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255][cp], 1);
     }
     __syncthreads();
-    // parallel exclusive scan of the 256 bins (threads 0..255, 4 waves); the one
-    // bin where the running count crosses kth fixes the next digit
+    // bin totals (threads 0..255; copy i of bin t read at (i + t) mod RS_COPIES,
+    // so the lanes of a read hit distinct banks), then a parallel exclusive scan;
+    // the one bin where the running count crosses kth fixes the next digit
     int h = 0, incl = 0;
     if (t < 256) {
-      h = hist[t];
+#pragma unroll 8
+      for (int i = 0; i < RS_COPIES; ++i) h += hist[t][(i + t) & (RS_COPIES - 1)];
       incl = h;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -1069,31 +1142,26 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   const unsigned long long thr = s_prefix;  // the m-th smallest key, or a key
                                             // above it and below the next one
   int* out = a.rep_pos + (size_t)bh * a.mpad;
-  if (t == 0) s_base = 0;
-  __syncthreads();
+  // wave w owns positions [j0, j1): count its selected keys, then write them
+  const int per = (((a.N + 15) / 16) + 63) & ~63;
+  const int j0 = min(w * per, a.N), j1 = min(j0 + per, a.N);
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int j0 = 0; j0 < a.N; j0 += 1024) {
-    const int j = j0 + t;
-    bool sel = false;
-    if (j < a.N) {
-      const unsigned long long key =
-          ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
-      sel = key <= thr;
-    }
+  int cnt = 0;
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    cnt += __popcll(__ballot(j < j1 && key_of(j) <= thr));
+  }
+  if (lane == 0) wtot[w] = cnt;
+  __syncthreads();
+  int slot = 0;
+  for (int ww = 0; ww < w; ++ww) slot += wtot[ww];
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    const bool sel = j < j1 && key_of(j) <= thr;
     const unsigned long long b = __ballot(sel);
-    if (lane == 0) wtot[w] = __popcll(b);
-    __syncthreads();
-    int pre = s_base;
-    for (int ww = 0; ww < w; ++ww) pre += wtot[ww];
-    const int slot = pre + __popcll(b & lt);
-    if (sel && slot < a.mpad) out[slot] = j;  // exactly m keys are <= thr
-    __syncthreads();
-    if (t == 0) {
-      int tot = 0;
-      for (int ww = 0; ww < 16; ++ww) tot += wtot[ww];
-      s_base += tot;
-    }
-    __syncthreads();
+    const int s = slot + __popcll(b & lt);
+    if (sel && s < a.mpad) out[s] = j;  // exactly m keys are <= thr
+    slot += __popcll(b);
   }
   for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
 }
@@ -1180,18 +1248,19 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
       if (mode == ClusterMode::Warm)
         hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
       else
-        hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(128), 0, st, a);
+        hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(1024), 0, st, a);
       for (int it = 0; it < a.T; ++it) {
         const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
         const size_t sm = km_smem_bytes(a.C);
+        const int first = it == 0 ? 1 : 0;
         if (a.C <= 16)
-          hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a);
+          hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a, first);
         else if (a.C <= 32)
-          hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a);
+          hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a, first);
         else if (a.C <= 48)
-          hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a);
+          hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a, first);
         else
-          hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a);
+          hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a, first);
         hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
       }
       hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);

@@ -88,8 +88,9 @@ void layout_of(const Shape& s, FullLayout* out) {
   L.ksum = take(BH * (size_t)s.nkc * D * 8);
   L.init_idx = take(BH * C * 4);
   L.centroids = take(BH * C * D * 4);
-  out->kmpart = take(BH * (size_t)s.nkm * C * D * 4);
-  out->kmcnt = take(BH * (size_t)s.nkm * C * 4);
+  // prepare may cut a head into up to four times the fewest k-means chunks
+  out->kmpart = take(BH * (size_t)(4 * s.nkm) * C * D * 4);
+  out->kmcnt = take(BH * (size_t)(4 * s.nkm) * C * 4);
   out->kmsum = take(BH * C * D * 8);
   out->kmn = take(BH * C * 8);
   out->vmaxp = take(BH * (size_t)s.nkc * 4);

@@ -28,6 +28,8 @@ constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 
 // Shape derived from the public parameters.
 struct Shape {
+  // nkm: the fewest k-means chunks per head (chunks of at most KM_CHUNK tokens);
+  // the workspace holds partial sums for up to 4 * nkm
   int B, H, N, BH, nblk, Npad, C, T, m, mpad, nkc, nkm, nch16;
   bool v4;  // 4-bit value residual (VC_V4)
   bool smooth_q;  // query smoothing (VC_SMOOTH_Q)
@@ -63,7 +65,8 @@ struct Args {
   int* init_idx;
   float* cent;
   int* kmpart;        // [BH][nkm][C][128] change of the member sums (fixed point) in one
-                      // Lloyd iteration, per assignment workgroup
+                      // Lloyd iteration, per assignment workgroup (prepare sets nkm
+                      // for the device, between the shape's nkm and four times that)
   int* kmcnt;         // [BH][nkm][C] change of the member counts, likewise
   long long* kmsum;   // [BH][C][128] member sums of the current labels (fixed point)
   long long* kmn;     // [BH][C] member counts of the current labels

@@ -1232,9 +1232,34 @@ __global__ void k_header(Args a, uint32_t clustered) {
   }
 }
 
+// Number of k-means chunks per head for a device with cus compute units.  The
+// assignment moves every token's 256 bytes once per iteration, and a CU's
+// resident workgroups share its bandwidth, so with all workgroups resident at
+// once the time is set by the CU holding the most: ceil(BH * n / cus) chunks of
+// ceil16(N / n) tokens.  Among the n in [nkm, 4 nkm] whose BH * n workgroups
+// are all resident (two per CU up to 48 clusters, else one: registers), the
+// smallest n that minimises that count; nkm itself when none fits (measured:
+// letting workgroups wait for a second pass is slower than larger chunks).
+int km_chunks(const Args& a, int cus) {
+  const long long slots = (long long)cus * (a.C <= 48 ? 2 : 1);
+  long long best = -1;
+  int pick = a.nkm;
+  for (int n = a.nkm; n <= 4 * a.nkm; ++n) {
+    if ((long long)a.BH * n > slots) break;
+    const long long per_cu = ((long long)a.BH * n + cus - 1) / cus;
+    const long long csz = (((long long)a.N + n - 1) / n + 15) / 16 * 16;
+    if (best < 0 || per_cu * csz < best) {
+      best = per_cu * csz;
+      pick = n;
+    }
+  }
+  return pick;
+}
+
 }  // namespace
 
-hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
+hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
+  Args a = a_in;
   const unsigned BH = (unsigned)a.BH;
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
   if (vs && mode != ClusterMode::Reuse)
@@ -1249,6 +1274,12 @@ hipError_t launch_prepare(const Args& a, ClusterMode mode, hipStream_t st) {
         hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
       else
         hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(1024), 0, st, a);
+      hipDevice_t dev = 0;  // the device the stream runs on
+      int cus = 0;
+      if (hipStreamGetDevice(st, &dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return hipErrorInvalidDevice;
+      a.nkm = km_chunks(a, cus);
       for (int it = 0; it < a.T; ++it) {
         const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
         const size_t sm = km_smem_bytes(a.C);

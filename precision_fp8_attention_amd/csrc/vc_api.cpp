@@ -93,7 +93,9 @@ void layout_of(const Shape& s, FullLayout* out) {
   out->kmcnt = take(BH * (size_t)(4 * s.nkm) * C * 4);
   out->kmsum = take(BH * C * D * 8);
   out->kmn = take(BH * C * 8);
-  out->vmaxp = take(BH * (size_t)s.nkc * 4);
+  out->ktot = take(BH * D * 8);
+  out->vmaxh = take(BH * 4);
+  out->vamax = take(BH * D * 4);
   out->kmsh = take(BH * 4);
   out->uhi = take(BH * N * D);
   out->ulo = take(BH * N * D);
@@ -158,7 +160,9 @@ Args make_args(const vc_attn_params* p, const Shape& s, const FullLayout& FL, vo
   a.kmcnt = reinterpret_cast<int*>(b + FL.kmcnt);
   a.kmsum = reinterpret_cast<long long*>(b + FL.kmsum);
   a.kmn = reinterpret_cast<long long*>(b + FL.kmn);
-  a.vmaxp = reinterpret_cast<float*>(b + FL.vmaxp);
+  a.ktot = reinterpret_cast<long long*>(b + FL.ktot);
+  a.vmaxh = reinterpret_cast<unsigned*>(b + FL.vmaxh);
+  a.vamax = reinterpret_cast<unsigned*>(b + FL.vamax);
   a.kmsh = reinterpret_cast<int*>(b + FL.kmsh);
   a.uhi = reinterpret_cast<int8_t*>(b + FL.uhi);
   a.ulo = reinterpret_cast<int8_t*>(b + FL.ulo);

@@ -70,7 +70,9 @@ struct Args {
   int* kmcnt;         // [BH][nkm][C] change of the member counts, likewise
   long long* kmsum;   // [BH][C][128] member sums of the current labels (fixed point)
   long long* kmn;     // [BH][C] member counts of the current labels
-  float* vmaxp;       // [BH][nkc] partial max |V|
+  long long* ktot;    // [BH][128] fixed-point channel sums of K (atomic adds of the chunks)
+  unsigned* vmaxh;    // [BH] max |V| of the head as fp32 bits (atomic max; values >= 0)
+  unsigned* vamax;    // [BH][128] max over blocks of |V - mu| per channel, fp32 bits
   int* kmsh;          // [BH] fixed-point exponent of the head
   int8_t* uhi;        // [BH][N][128] high part (u >> 7) of the fixed-point V
   int8_t* ulo;        // [BH][N][128] low part (u & 127)
@@ -104,7 +106,7 @@ struct Args {
 // Private extension of the public layout (partial k-means sums).
 struct FullLayout {
   vc_attn_ws_layout pub;
-  size_t kmpart, kmcnt, kmsum, kmn, vmaxp, kmsh, uhi, ulo, centfix, kmcc;
+  size_t kmpart, kmcnt, kmsum, kmn, ktot, vmaxh, vamax, kmsh, uhi, ulo, centfix, kmcc;
 };
 
 bool shape_of(const vc_attn_params* p, Shape* s);

@@ -121,9 +121,10 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 __device__ __forceinline__ int v4_group(int r) { return r >> 5; }
 
 // ---------------------------------------------------------------------------
-// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens; with WITH_V
-// the same workgroup records max|V| of the chunk (the k-means fixed-point scale,
-// needed only when k-means runs).
+// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens, added into
+// the head's sums; with WITH_V the same workgroup takes max|V| of the chunk into
+// the head's maximum (the k-means fixed-point scale, needed only when k-means
+// runs).
 // grid (nkc, BH), 256 threads: thread = (row r = t/16, 8-channel group t%16).
 template <bool WITH_V>
 __global__ __launch_bounds__(256) void k_ksum(Args a) {
@@ -168,17 +169,22 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
     long long tot = 0;
     for (int rr = 0; rr < 16; ++rr) tot += red[rr][t];
     a.ksum[((size_t)bh * a.nkc + ch) * D + t] = tot;
+    // the head's sums: integer adds, so their order cannot change them
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.ktot) + (size_t)bh * D + t, (unsigned long long)tot);
   }
-  if (WITH_V && t == 0) a.vmaxp[(size_t)bh * a.nkc + ch] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  // max |V| >= 0, so its fp32 bits order like the values
+  if (WITH_V && t == 0) atomicMax(a.vmaxh + bh, __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
 }
 
-// K channel mean.  grid BH, 128 threads.
-__global__ __launch_bounds__(128) void k_kbar(Args a) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  long long tot = 0;
-  for (int ch = 0; ch < a.nkc; ++ch) tot += a.ksum[((size_t)bh * a.nkc + ch) * D + c];
-  a.kbar[(size_t)bh * D + c] = fixed_mean(tot, a.N);
+// Clears the per-head accumulators that later kernels add into.  grid BH, 128
+// threads.
+__global__ __launch_bounds__(128) void k_prep_zero(Args a) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  a.ktot[(size_t)bh * D + t] = 0;
+  a.vamax[(size_t)bh * D + t] = 0u;
+  if (t == 0) a.vmaxh[bh] = 0u;
 }
+
 
 // ---------------------------------------------------------------------------
 // k-means on fixed-point values ("lightweight" clustering): per head every V
@@ -194,14 +200,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // grid (ceil(N/256), BH), 256 threads: 16 threads per token row (8 channels
 // each, 16-byte loads), 16 rows per step.
 __global__ __launch_bounds__(256) void k_vfix(Args a) {
-  __shared__ float wm[4];
   const int bh = blockIdx.y, t = threadIdx.x;
-  float am = 0.0f;
-  for (int i = t; i < a.nkc; i += 256) am = fmaxf(am, a.vmaxp[(size_t)bh * a.nkc + i]);
-  am = wave_max(am);
-  if ((t & 63) == 0) wm[t >> 6] = am;
-  __syncthreads();
-  am = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  const float am = __uint_as_float(a.vmaxh[bh]);
   int e = 0;
   if (am > 0.0f) frexpf(am, &e);
   const int sh = am > 0.0f ? 13 - e : 0;
@@ -233,15 +233,6 @@ __device__ __forceinline__ long long wave_sum_i64(long long x) {
   return x;
 }
 
-// Sum of one int64 per thread over a 128-thread block (exact).  red: 2 slots of
-// shared memory.  Every thread gets the total.
-__device__ __forceinline__ long long sum128_i64(long long x, long long* red) {
-  x = wave_sum_i64(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return red[0] + red[1];
-}
 
 // Forgy initialisation: seeded partial Fisher-Yates over [0, N), centroid k =
 // fixed-point value of token idx[k].  The draws do not depend on the swaps, so
@@ -367,6 +358,43 @@ __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, co
 
 // NT = number of 16-centroid tiles (C <= 16 NT).  Centroids beyond C get a norm
 // of 2^62, so their distance never wins and no lane needs a predicate.
+// Update step: the member sums and counts take the iteration's changes;
+// centroid = member mean rounded to the nearest integer (ties to even; |sum| <
+// 2^34 so the fp64 quotient rounds once), empty clusters stay; then the squared
+// norm.  A separate launch: handing the update to the last assignment workgroup
+// of each head needs a device-scope release fence in every workgroup, which
+// writes back the XCD's L2 (measured 4x slower per iteration).  grid (C, BH),
+// 128 threads (one per channel); the chunk loops are unrolled so that their
+// loads are in flight together.
+__global__ __launch_bounds__(128) void k_km_update(Args a) {
+  __shared__ long long red[2];
+  const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
+  long long* sum = a.kmsum + ((size_t)bh * C + kk) * D + c;
+  long long s = *sum, n = a.kmn[(size_t)bh * C + kk];
+#pragma unroll 8
+  for (int ch = 0; ch < a.nkm; ++ch) {
+    s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
+    n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
+  }
+  *sum = s;
+  int u;
+  if (n > 0) {
+    u = (int)__builtin_rint((double)s / (double)n);
+    a.centfix[((size_t)bh * C + kk) * D + c] = u;
+    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -a.kmsh[bh]);
+  } else {
+    u = a.centfix[((size_t)bh * C + kk) * D + c];
+  }
+  const long long sq = wave_sum_i64((long long)u * u);
+  if ((c & 63) == 0) red[c >> 6] = sq;
+  // every thread has read the old count before thread 0 stores the new one
+  __syncthreads();
+  if (c == 0) {
+    a.kmn[(size_t)bh * C + kk] = n;
+    a.kmcc[(size_t)bh * C + kk] = red[0] + red[1];
+  }
+}
+
 // first: the first iteration of this prepare call, where every token enters its
 // cluster (labels from an earlier call are not read).
 template <int NT>
@@ -387,14 +415,20 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   }
   for (int e = t; e < C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
   if (t < 2 * C) cnt[t] = 0;
-  // this lane's centroid norms: centroid 16kt + 4g + v
-  long long ccr[NT][4];
+  // Distances as exact fp64 keys.  For centroid k, D = ||c||^2 - 2 u.c with
+  // |D| < 2^35, and key = 64 (D + 2^35) + k is an integer below 2^42, exact in
+  // fp64 at every step (fp64 fma runs at the fp32 rate here, 64-bit integer
+  // arithmetic takes several instructions per operation).  The smallest key
+  // gives the smallest D and, among equal D, the lowest id; k is its low 6 bits.
+  // This lane's base keys 64 (||c||^2 + 2^35) + k for centroids 16kt + 4g + v;
+  // centroids beyond C get 2^50, above every real key.
+  double kbase[NT][4];
 #pragma unroll
   for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int k = 16 * kt + 4 * g + v;
-      ccr[kt][v] = k < C ? a.kmcc[(size_t)bh * C + k] : (1ll << 62);
+      kbase[kt][v] = k < C ? ((double)a.kmcc[(size_t)bh * C + k] + 0x1p35) * 64.0 + (double)k : 0x1p50;
     }
   __syncthreads();
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
@@ -429,8 +463,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     const int old = nx.old;
     if (has(sub + KM_WAVES)) load_sub(sub + KM_WAVES, nx);
     const int j = first_tok + sub * 16 + l16;
-    long long bestD = 0x7fffffffffffffffll;
-    int best = 0;
+    double bestK = 0x1p52;
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
       const int kr = 16 * kt + l16;
@@ -440,32 +473,30 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
       const v4i al0 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 16 * g);
       const v4i al1 = *reinterpret_cast<const v4i*>(clo + krow * CROW + 64 + 16 * g);
       const v4i z = {0, 0, 0, 0};
+      // u.c = 2^14 HH + 2^7 M + LL with M = hi.lo + lo.hi (one accumulator;
+      // |M| < 2^22, |LL| < 2^21, so 2^7 M + LL fits an int32)
       v4i HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bh0, z, 0, 0, 0);
       HH = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bh1, HH, 0, 0, 0);
-      v4i HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bl0, z, 0, 0, 0);
-      HL = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bl1, HL, 0, 0, 0);
-      v4i LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bh0, z, 0, 0, 0);
-      LH = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, LH, 0, 0, 0);
+      v4i M = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah0, bl0, z, 0, 0, 0);
+      M = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah1, bl1, M, 0, 0, 0);
+      M = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bh0, M, 0, 0, 0);
+      M = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bh1, M, 0, 0, 0);
       v4i LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al0, bl0, z, 0, 0, 0);
       LL = __builtin_amdgcn_mfma_i32_16x16x64_i8(al1, bl1, LL, 0, 0, 0);
-      // lane (g, token l16) holds centroids 16kt + 4g + v; ||c||^2 - 2 u.c with
-      // u.c = 2^14 HH + 2^7 (HL + LH) + LL, exact in int64
+      // lane (g, token l16) holds centroids 16kt + 4g + v:
+      // key = base - 64 * 2 u.c = base - 2^21 HH - 2^7 (2^7 M + LL)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const long long Dk = ccr[kt][v] - (long long)HH[v] * 32768 - (long long)(HL[v] + LH[v]) * 256 -
-                             (long long)LL[v] * 2;
-        const int k = 16 * kt + 4 * g + v;
-        best = Dk < bestD ? k : best;
-        bestD = Dk < bestD ? Dk : bestD;
+        const int X = M[v] * 128 + LL[v];
+        const double key = __builtin_fma(-0x1p21, (double)HH[v], __builtin_fma(-128.0, (double)X, kbase[kt][v]));
+        bestK = __builtin_fmin(bestK, key);
       }
     }
-    // argmin across the four lane groups; ties go to the lower id
+    // smallest key across the four lane groups
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const long long oD = __shfl_xor(bestD, off, 64);
-      const int ob = __shfl_xor(best, off, 64);
-      if (oD < bestD || (oD == bestD && ob < best)) { bestD = oD; best = ob; }
-    }
+    for (int off = 16; off <= 32; off <<= 1) bestK = __builtin_fmin(bestK, __shfl_xor(bestK, off, 64));
+    const double hi = __builtin_floor(bestK * 0x1p-6);
+    const int best = (int)__builtin_fma(-64.0, hi, bestK);
     // only a token whose label changes touches the bins; a wave with none skips
     const bool moved = j < last && best != old;
     if (__ballot(moved) != 0ull && moved) {
@@ -493,33 +524,6 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   if (t < C) a.kmcnt[((size_t)bh * a.nkm + chunk) * C + t] = cnt[t] - cnt[C + t];
 }
 
-// Update step: the member sums and counts take the iteration's changes; centroid
-// = member mean rounded to the nearest integer (ties to even; |sum| < 2^34 so
-// the fp64 quotient rounds once), empty clusters stay.  grid (C, BH), 128 threads.
-__global__ __launch_bounds__(128) void k_km_update(Args a) {
-  const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
-  long long* sum = a.kmsum + ((size_t)bh * C + kk) * D + c;
-  long long s = *sum, n = a.kmn[(size_t)bh * C + kk];
-  for (int ch = 0; ch < a.nkm; ++ch) {
-    s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
-    n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
-  }
-  *sum = s;
-  // every thread has read the old count before thread 0 stores the new one
-  __syncthreads();
-  if (c == 0) a.kmn[(size_t)bh * C + kk] = n;
-  int u;
-  if (n > 0) {
-    u = (int)__builtin_rint((double)s / (double)n);
-    a.centfix[((size_t)bh * C + kk) * D + c] = u;
-    a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -a.kmsh[bh]);
-  } else {
-    u = a.centfix[((size_t)bh * C + kk) * D + c];
-  }
-  __shared__ long long red[2];
-  const long long cc = sum128_i64((long long)u * u, red);
-  if (c == 0) a.kmcc[(size_t)bh * C + kk] = cc;
-}
 
 // ---------------------------------------------------------------------------
 // Stable counting sort of positions by cluster id.  grid BH, 1024 threads.
@@ -528,9 +532,21 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
 // walks its run again in order, ranking tokens of one cluster inside each
 // 64-token step by a ballot match and keeping its running offsets in LDS of its
 // own (no barrier inside the walks).
+__device__ __forceinline__ void write_header(const Args& a, uint32_t clustered) {
+  a.header->magic = MAGIC;
+  a.header->clustered = clustered;
+  a.header->B = a.B;
+  a.header->H = a.H;
+  a.header->N = a.N;
+  a.header->C = a.C;
+}
+
 __global__ __launch_bounds__(1024) void k_perm(Args a) {
   __shared__ int wcnt[16][MAX_CLUSTERS + 1];  // per wave: count, then next position
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
+  // the workspace now holds clusters for this shape (read back by later calls
+  // that reuse them, after this launch has completed)
+  if (bh == 0 && t == 0) write_header(a, 1u);
   const int* lab = a.labels + (size_t)bh * a.N;
   int* perm = a.perm + (size_t)bh * a.N;
   int* iperm = a.iperm + (size_t)bh * a.N;
@@ -590,6 +606,7 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
 // Identity permutation (V-Smooth off).  grid (ceil(N/256), BH), 256 threads.
 __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
   const int j = blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
+  if (j == 0 && bh == 0) write_header(a, 0u);
   if (j < a.N) {
     a.perm[(size_t)bh * a.N + j] = j;
     a.iperm[(size_t)bh * a.N + j] = j;
@@ -616,11 +633,6 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
   const bool smooth = SMOOTH && !isk;  // uniform over the workgroup
   const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
   const int nrow = a.N - blk * BLK;  // rows r < nrow of the block are tokens
-  // value subtracted from channel e: the K channel mean, or (smoothed queries)
-  // the block mean once it is known
-  float sub[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sub[e] = isk ? a.kbar[(size_t)bh * D + cg * 8 + e] : 0.0f;
   uint4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -632,6 +644,22 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
       raw[i] = *reinterpret_cast<const uint4*>(src + (size_t)j * D + cg * 8);
     }
   }
+  // K channel mean from the head's fixed-point sums (while the rows load); the
+  // first block's workgroup also stores it
+  __shared__ float skbar[D];
+  if (isk) {  // uniform over the workgroup
+    if (t < D) {
+      const float kb = fixed_mean(a.ktot[(size_t)bh * D + t], a.N);
+      skbar[t] = kb;
+      if (blk == 0) a.kbar[(size_t)bh * D + t] = kb;
+    }
+    __syncthreads();
+  }
+  // value subtracted from channel e: the K channel mean, or (smoothed queries)
+  // the block mean once it is known
+  float sub[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sub[e] = isk ? skbar[cg * 8 + e] : 0.0f;
   // element e of row i as fp32, minus sub[e] (exact order of the reference: one
   // fp32 subtraction)
   auto val = [&](int i, int e) {
@@ -866,7 +894,10 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
     }
     const size_t o = ((size_t)bh * a.nblk + blk) * D + t;
     a.mu[o] = smu[t];
-    a.bamax[o] = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+    const float bm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+    a.bamax[o] = bm;
+    // the channel's maximum over the head's blocks (bm >= 0: bits order like values)
+    atomicMax(a.vamax + (size_t)bh * D + t, __float_as_uint(bm));
     if (a.flags & VC_V4) {
       uint8_t* rec = a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC;
 #pragma unroll
@@ -875,59 +906,38 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
   }
 }
 
-// Per-channel residual scales.  grid BH, 128 threads (one per channel).
-__global__ __launch_bounds__(128) void k_v_scale(Args a) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const float* bm = a.bamax + (size_t)bh * a.nblk * D + c;
-  float A[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  int b = 0;
-  for (; b + 8 <= a.nblk; b += 8) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) A[i] = fmaxf(A[i], bm[(size_t)(b + i) * D]);
-  }
-  for (; b < a.nblk; ++b) A[0] = fmaxf(A[0], bm[(size_t)b * D]);
-  const float amax = fmaxf(fmaxf(fmaxf(A[0], A[1]), fmaxf(A[2], A[3])),
-                           fmaxf(fmaxf(A[4], A[5]), fmaxf(A[6], A[7])));
+// Channel c's residual scale, set by the head's largest |V - mu| (one per
+// channel: sv = max/448, inv = 448/max; 1 with the 4-bit residual), and block
+// blk's mean in V code units (mu * inv), in fp32 and as the bf16 high/low pair
+// the restore MFMA reads (groups of 16 blocks, channel-major).  Block 0 also
+// stores the scales; the last block clears its group's slots past the last block.
+__device__ __forceinline__ void v_channel(const Args& a, int bh, int blk, int c, float* mu_out, float* s_out,
+                                          float* inv_out) {
   float s, inv;
-  scale_from_amax(amax, &s, &inv);
+  scale_from_amax(__uint_as_float(a.vamax[(size_t)bh * D + c]), &s, &inv);
   if (a.flags & VC_V4) s = inv = 1.0f;  // the 4-bit residual carries its own powers of two
-  a.sv[(size_t)bh * D + c] = s;
-  a.inv[(size_t)bh * D + c] = inv;
-}
-
-// Block means in V code units (mu * inv), fp32 and as a bf16 high/low pair in
-// groups of 16 blocks, channel-major (the restore MFMA reads 4 blocks of one
-// channel per lane).  grid (nch16, BH), 128 threads (one per channel).
-__global__ __launch_bounds__(128) void k_v_mup(Args a) {
-  const int grp = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
-  const float inv = a.inv[(size_t)bh * D + c];
-  uint32_t hi[8], lo[8];
-#pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    float x[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int b = grp * 16 + j + e;
-      x[e] = 0.0f;
-      if (b < a.nblk) {
-        const size_t o = ((size_t)bh * a.nblk + b) * D + c;
-        x[e] = a.mu[o] * inv;
-        a.mup[o] = x[e];
-      }
-    }
-    const uint16_t h0 = f2bf_rne(x[0]), h1 = f2bf_rne(x[1]);
-    const uint16_t l0 = f2bf_rne(x[0] - __uint_as_float((uint32_t)h0 << 16));
-    const uint16_t l1 = f2bf_rne(x[1] - __uint_as_float((uint32_t)h1 << 16));
-    hi[j / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[j / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  if (blk == 0) {
+    a.sv[(size_t)bh * D + c] = s;
+    a.inv[(size_t)bh * D + c] = inv;
   }
-  uint16_t* base = a.mupt + (((size_t)bh * a.nch16 + grp) * 2) * D * 16;
-  uint4* dh = reinterpret_cast<uint4*>(base + (size_t)c * 16);
-  uint4* dl = reinterpret_cast<uint4*>(base + (size_t)D * 16 + (size_t)c * 16);
-  dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-  dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+  const size_t o = ((size_t)bh * a.nblk + blk) * D + c;
+  const float mu = a.mu[o];
+  const float x = mu * inv;
+  a.mup[o] = x;
+  const uint16_t h = f2bf_rne(x);
+  const uint16_t l = f2bf_rne(x - __uint_as_float((uint32_t)h << 16));
+  uint16_t* base = a.mupt + (((size_t)bh * a.nch16 + (blk >> 4)) * 2) * D * 16 + (size_t)c * 16;
+  const int j = blk & 15;
+  base[j] = h;
+  base[D * 16 + j] = l;
+  if (blk == a.nblk - 1)
+    for (int jj = j + 1; jj < 16; ++jj) {
+      base[jj] = 0;
+      base[D * 16 + jj] = 0;
+    }
+  *mu_out = mu;
+  *s_out = s;
+  *inv_out = inv;
 }
 
 // Residual codes (channel-major, interleaved) and the repair criterion.
@@ -940,9 +950,7 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
   __shared__ __align__(16) uint8_t tile[D * BLK];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
-  smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
-  sinv[t] = a.inv[(size_t)bh * D + t];
-  ssv[t] = a.sv[(size_t)bh * D + t];
+  v_channel(a, bh, blk, t, &smu[t], &ssv[t], &sinv[t]);
   const int r = t, col = v_col(r), p = p0 + r;
   uint4 row[16];
   if (r < n) {
@@ -997,8 +1005,11 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
   __shared__ __align__(16) uint8_t sx[4][D];  // [group][channel] E8M0 exponents
   __shared__ __align__(16) float smu[D];
   const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  smu[t] = a.mu[((size_t)bh * a.nblk + blk) * D + t];
-  smu[t + 64] = a.mu[((size_t)bh * a.nblk + blk) * D + t + 64];
+  {
+    float sc, iv;  // 1 with the 4-bit residual
+    v_channel(a, bh, blk, t, &smu[t], &sc, &iv);
+    v_channel(a, bh, blk, t + 64, &smu[t + 64], &sc, &iv);
+  }
   {
     // the record is [group][channel % 16][channel / 16]: transpose to channel order
     const uint8_t* rec = a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC;
@@ -1221,16 +1232,6 @@ __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
 }
 
 // Header: marks the clusters valid for this shape.  grid 1, 64 threads.
-__global__ void k_header(Args a, uint32_t clustered) {
-  if (threadIdx.x == 0) {
-    a.header->magic = MAGIC;
-    a.header->clustered = clustered;
-    a.header->B = a.B;
-    a.header->H = a.H;
-    a.header->N = a.N;
-    a.header->C = a.C;
-  }
-}
 
 // Number of k-means chunks per head for a device with cus compute units.  The
 // assignment moves every token's 256 bytes once per iteration, and a CU's
@@ -1262,44 +1263,45 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   Args a = a_in;
   const unsigned BH = (unsigned)a.BH;
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
-  if (vs && mode != ClusterMode::Reuse)
+  const bool kmeans = vs && mode != ClusterMode::Reuse;
+  if (kmeans) {
+    // k-means chunks for the device the stream runs on (before any launch, so a
+    // failure leaves nothing enqueued)
+    hipDevice_t dev = 0;
+    int cus = 0;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return hipErrorInvalidDevice;
+    a.nkm = km_chunks(a, cus);
+  }
+  hipLaunchKernelGGL(k_prep_zero, dim3(BH), dim3(128), 0, st, a);
+  if (kmeans)
     hipLaunchKernelGGL(k_ksum<true>, dim3(a.nkc, BH), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_ksum<false>, dim3(a.nkc, BH), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_kbar, dim3(BH), dim3(128), 0, st, a);
-  if (vs) {
-    if (mode != ClusterMode::Reuse) {
-      hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
-      if (mode == ClusterMode::Warm)
-        hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
+  if (kmeans) {
+    hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
+    if (mode == ClusterMode::Warm)
+      hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(1024), 0, st, a);
+    for (int it = 0; it < a.T; ++it) {
+      const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
+      const size_t sm = km_smem_bytes(a.C);
+      const int first = it == 0 ? 1 : 0;
+      if (a.C <= 16)
+        hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a, first);
+      else if (a.C <= 32)
+        hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a, first);
+      else if (a.C <= 48)
+        hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a, first);
       else
-        hipLaunchKernelGGL(k_km_init, dim3(BH), dim3(1024), 0, st, a);
-      hipDevice_t dev = 0;  // the device the stream runs on
-      int cus = 0;
-      if (hipStreamGetDevice(st, &dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        return hipErrorInvalidDevice;
-      a.nkm = km_chunks(a, cus);
-      for (int it = 0; it < a.T; ++it) {
-        const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
-        const size_t sm = km_smem_bytes(a.C);
-        const int first = it == 0 ? 1 : 0;
-        if (a.C <= 16)
-          hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a, first);
-        else if (a.C <= 32)
-          hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a, first);
-        else if (a.C <= 48)
-          hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a, first);
-        else
-          hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a, first);
-        hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
-      }
-      hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);
-      hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 1u);
+        hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a, first);
+      hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
     }
-  } else {
+    hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);
+  } else if (!vs) {
     hipLaunchKernelGGL(k_perm_identity, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, st, a, 0u);
   }
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qk_quant<true>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
@@ -1308,8 +1310,6 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 15) / 16, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_v_scale, dim3(BH), dim3(128), 0, st, a);
-  hipLaunchKernelGGL(k_v_mup, dim3(a.nch16, BH), dim3(128), 0, st, a);
   if (a.flags & VC_V4)
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else

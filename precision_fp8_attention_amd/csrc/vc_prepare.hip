@@ -633,6 +633,9 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
   const bool smooth = SMOOTH && !isk;  // uniform over the workgroup
   const uint16_t* src = (isk ? a.k : a.q) + (size_t)bh * a.N * D;
   const int nrow = a.N - blk * BLK;  // rows r < nrow of the block are tokens
+  // Rows are read once and codes written once: non-temporal accesses keep them
+  // from displacing other lines in L2 (measured 24 us less at 2x24x16544; the
+  // 16 lanes of a row make each access two whole 128-byte lines).
   uint4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -641,7 +644,8 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
     if (r < nrow) {
       const int p = blk * BLK + r;
       const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
-      raw[i] = *reinterpret_cast<const uint4*>(src + (size_t)j * D + cg * 8);
+      const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (size_t)j * D + cg * 8));
+      raw[i] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
     }
   }
   // K channel mean from the head's fixed-point sums (while the rows load); the
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
     // with the 4-bit residual a K code row goes to the tile row v4_krow(r)
     const int prow = (isk && (a.flags & VC_V4)) ? blk * BLK + v4_krow(r) : p;
     uint8_t* dst = (isk ? a.k8 : a.q8) + ((size_t)bh * a.Npad + prow) * D + cg * 8;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    __builtin_nontemporal_store(((unsigned long long)w1 << 32) | w0, reinterpret_cast<unsigned long long*>(dst));
     if (isk && (a.flags & VC_EXACT_SCORES)) {
       // the K codes decoded to bf16 (E4M3 values are exact in bf16)
       uint32_t h[4];

@@ -753,37 +753,49 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
 // channels 0..127 of qbar_b[c] * (k[c] - kbar[c]), the same fp32 values the K
 // codes are made from; 0 for positions past N.  A product of a (nblk x 128) and
 // a (128 x Npad) matrix whose every output accumulates in channel order, so it
-// runs on VALU fma, register-tiled: a workgroup computes 16 query blocks x 256
-// keys, each thread 4 x 4 outputs; 32 channels at a time pass through LDS
+// runs on VALU fma, register-tiled: a workgroup computes 32 query blocks x 256
+// keys, each thread 8 x 4 outputs; 32 channels at a time pass through LDS
 // (k - kbar channel-major, the means channel-major), and per channel a thread
-// reads two float4 and issues 16 fma.  grid (ceil(nblk/16), ceil(Npad/256), BH),
-// 256 threads; the block groups of one key tile are neighbours, so the key rows
-// are fetched from HBM about once.
+// reads three float4 (two of them the same across its wave) and issues 32 fma.
+// The next 32 channels of each key row are loaded while the current ones are
+// used.  grid (ceil(nblk/32), ceil(Npad/256), BH), 256 threads; the block groups
+// of one key tile are neighbours, so the key rows are fetched from HBM about
+// once.
 __global__ __launch_bounds__(256) void k_qbias(Args a) {
-  constexpr int QB = 16, KT = 256, CC = 32;
+  constexpr int QB = 32, KT = 256, CC = 32;
   __shared__ __align__(16) float skt[CC][KT];  // k - kbar, [channel][key]
   __shared__ __align__(16) float sqm[CC][QB];  // qbar, [channel][block]
   const int bh = blockIdx.z, t = threadIdx.x;
   const int b0 = blockIdx.x * QB, nb = min(QB, a.nblk - b0);
   const int p0 = blockIdx.y * KT;
-  const int bq = t >> 6, kq = t & 63;  // outputs: blocks 4bq..4bq+3, keys 4kq..4kq+3
-  // loader role: key p0 + t of the tile
+  const int bq = t >> 6, kq = t & 63;  // outputs: blocks 8bq..8bq+7, keys 4kq..4kq+3
+  // loader role: key p0 + t of the tile; the next chunk of its row is loaded
+  // while the current one is used
   const int pl = p0 + t;
   const bool vl = pl < a.N;
   const uint4* row = reinterpret_cast<const uint4*>(a.k + ((size_t)bh * a.N + (vl ? a.perm[(size_t)bh * a.N + pl] : 0)) * D);
   const float* kbar = a.kbar + (size_t)bh * D;
-  float acc[4][4];
+  float acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  uint4 nxt[CC / 8];
+#pragma unroll
+  for (int i = 0; i < CC / 8; ++i) nxt[i] = row[i];
 #pragma unroll 1
   for (int c0 = 0; c0 < D; c0 += CC) {
+    uint4 cur[CC / 8];
+#pragma unroll
+    for (int i = 0; i < CC / 8; ++i) cur[i] = nxt[i];
+    if (c0 + CC < D) {
+#pragma unroll
+      for (int i = 0; i < CC / 8; ++i) nxt[i] = row[(c0 + CC) / 8 + i];
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CC / 8; ++i) {
-      const uint4 u = row[c0 / 8 + i];
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t h[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = 8 * i + e;
@@ -795,13 +807,14 @@ __global__ __launch_bounds__(256) void k_qbias(Args a) {
       sqm[c][bb] = bb < nb ? a.qbar[((size_t)bh * a.nblk + b0 + bb) * D + c0 + c] : 0.0f;
     }
     __syncthreads();
-#pragma unroll 8
+#pragma unroll 4
     for (int c = 0; c < CC; ++c) {
-      const float4 qv = *reinterpret_cast<const float4*>(&sqm[c][4 * bq]);
+      const float4 q0 = *reinterpret_cast<const float4*>(&sqm[c][8 * bq]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&sqm[c][8 * bq + 4]);
       const float4 kv = *reinterpret_cast<const float4*>(&skt[c][4 * kq]);
-      const float qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
+      const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(qa[i], ka[j], acc[i][j]);
     }
@@ -809,8 +822,8 @@ __global__ __launch_bounds__(256) void k_qbias(Args a) {
   const int pk = p0 + 4 * kq;
   if (pk < a.Npad) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * bq + i;
+    for (int i = 0; i < 8; ++i) {
+      const int b = 8 * bq + i;
       if (b < nb) {
         float4 o;
         o.x = pk + 0 < a.N ? a.c0 * acc[i][0] : 0.0f;
@@ -1318,7 +1331,7 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   else
     hipLaunchKernelGGL(k_qk_quant<false>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
   if (a.flags & VC_SMOOTH_Q)
-    hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 15) / 16, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 31) / 32, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   if (a.flags & VC_V4)
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);

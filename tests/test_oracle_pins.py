@@ -410,6 +410,42 @@ def test_constant_keys_are_smoothed_away():
                                rtol=1e-12, atol=1e-12)
 
 
+def test_shifting_every_key_by_one_vector_changes_nothing():
+    """Softmax ignores a per-channel constant added to every key, and the method
+    removes it exactly by the K channel mean.  Integer keys in [-60, 60], a
+    shift of +-64 per channel (exact in bf16) and N a power of two keep the
+    sums, means and K - kbar exact in fp32, so the simulated output and every
+    code are bit-identical with and without the shift.  A dropped smoothing
+    term, a wrong sign or a mean over the wrong axis fails it."""
+    N = 256
+    q, _, v = inputs.make_custom(1, 2, N, seed=14)
+    rng = np.random.default_rng(15)
+    kf = rng.integers(-60, 61, (1, 2, N, 128)).astype(np.float32)
+    shift = rng.choice([-64.0, 64.0], (1, 2, 1, 128)).astype(np.float32)
+    to_bits = lambda x: (x.view(np.uint32) >> 16).astype(np.uint16)  # noqa: E731 (exact values)
+    k0, k1 = to_bits(kf), to_bits(kf + shift)
+    assert np.array_equal(inputs.bf16_bits_to_f32(k1), kf + shift)
+    P = orc.make_params(1, 2, N, C_=4, T=3, rho=0.02, sm_scale=0.01)
+    (o0, pc0), pr0, _, _ = _sim(P, q, k0, v, pcodes=True)
+    (o1, pc1), pr1, _, _ = _sim(P, q, k1, v, pcodes=True)
+    assert not np.array_equal(pr0["kbar"], pr1["kbar"])
+    assert np.array_equal(pr0["k8"], pr1["k8"]) and np.array_equal(pr0["sk"], pr1["sk"])
+    assert np.array_equal(pc0, pc1)
+    assert np.array_equal(o0, o1)
+
+
+def test_zero_repair_budget_equals_repair_off():
+    """rho = 0 leaves no token to repair: the same output as the repair flag off,
+    bit for bit, and an empty repair set."""
+    q, k, v = inputs.make_custom(1, 2, 300, seed=16, rate=0.02, sigma=20.0)
+    Pa = orc.make_params(1, 2, 300, C_=4, T=3, rho=0.0)
+    Pb = orc.make_params(1, 2, 300, C_=4, T=3, rho=0.3, flags=orc.VSMOOTH | orc.PERMUTE_Q)
+    oa, pra, _, _ = _sim(Pa, q, k, v)
+    ob, prb, _, _ = _sim(Pb, q, k, v)
+    assert pra["m"] == 0 and prb["m"] == 0
+    assert np.array_equal(oa, ob)
+
+
 def test_row_max_code_is_bias():
     q, k, v = inputs.make_custom(1, 1, 400, seed=4)
     for tau, lo, hi in ((0.0, 120, 120), (6.0, 120, 126)):

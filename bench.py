@@ -144,25 +144,60 @@ def cpu_baseline(wl, q, k, v, P, flops, gpu_out):
     return base, {"heads": heads, "rows": int(len(idx)), "max_abs": mx, "rel_l2": rel}
 
 
-def fidelity(wl, q, k, v, qd, kd, vd, dev, heads, rows):
+def _exact_rows(qd, kd, vd, heads, rows, scale):
+    """Exact softmax attention in fp64 of the bf16 inputs on the given rows of the
+    given heads (plain torch fp64 on the device; the reference of the fidelity
+    figures).  Returns [len(heads) * len(rows), 128] float64."""
+    import torch
+    B, H, N, d = qd.shape
+    r = torch.as_tensor(rows, device=qd.device).long()
+    out = []
+    for h in heads:
+        b_, h_ = divmod(int(h), H)
+        qh = qd[b_, h_, r].double()
+        kh = kd[b_, h_].double().t().contiguous()
+        vh = vd[b_, h_].double().contiguous()
+        out.append(torch.softmax(torch.matmul(qh, kh) * scale, dim=-1).matmul(vh))
+    return torch.cat(out).cpu().numpy()
+
+
+def fidelity(wl, qd, kd, vd, dev, heads, rows):
     """Relative L2 distance of GPU outputs to exact fp64 attention on sampled rows
-    of the benchmark workload, for the full method and its ablations (the
-    the benchmark spec's V-Smooth-off figure, repair off, the literal ExpCast offset
-    k = 0, exact scores, the 4-bit residual).  The pages report fidelity against
-    unquantised outputs (noticiai.com.br article, Benchmarks; V-Smooth)."""
+    of the benchmark workload, for the full method and its ablations (V-Smooth
+    off, repair off, the literal ExpCast offset k = 0, exact scores, the 4-bit
+    residual).  Two more sets repeat the V-Smooth ablations on structured V: a
+    large per-channel offset and a few outlier tokens (what V-Smooth's grouping
+    and block means are for).  The pages report fidelity against unquantised
+    outputs (noticiai.com.br article, Benchmarks and V-Smooth sections)."""
     import numpy as np
     import torch
 
     import precision_fp8_attention_amd as vc
-    from oracle import oracle as orc
     B, H, N = wl["B"], wl["H"], wl["N"]
-    P = orc.make_params(B, H, N, C_=wl["C"], T=wl["T"], rho=wl["rho"])
+    scale = 1.0 / np.sqrt(128.0)
     slot = np.repeat(np.asarray(heads), len(rows)).astype(np.int32)
     idx = np.tile(rows, len(heads)).astype(np.int32)
-    t0 = time.perf_counter()
-    ex = orc.exact_rows(P, q, k, v, slot, idx)
-    t_exact = time.perf_counter() - t0
-    variants = {
+    sl = torch.as_tensor(slot, device=dev).long()
+    ix = torch.as_tensor(idx, device=dev).long()
+
+    def run(vv, variants):
+        t0 = time.perf_counter()
+        ex = _exact_rows(qd, kd, vv, heads, rows, scale)
+        t_exact = time.perf_counter() - t0
+        out = {}
+        for name, kw in variants.items():
+            p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"], **kw)
+            ws = vc.alloc_workspace(p, dev)
+            o = torch.empty_like(qd)
+            vc.prepare(p, qd, kd, vv, ws)
+            vc.forward(p, ws, o)
+            torch.cuda.synchronize()
+            got = o.float().view(B * H, N, 128)[sl, ix].cpu().numpy().astype(np.float64)
+            out[name] = round(float(np.linalg.norm(got - ex) / np.linalg.norm(ex)), 6)
+            del ws, o
+        return out, t_exact
+
+    base, t_exact = run(vd, {
         "full": dict(flags=vc.DEFAULT_FLAGS),
         "vsmooth_off": dict(flags=0),                        # identity order, no means, no repair
         "vsmooth_off_repair_on": dict(flags=vc.REPAIR | vc.PERMUTE_Q),
@@ -170,23 +205,33 @@ def fidelity(wl, q, k, v, qd, kd, vd, dev, heads, rows):
         "expcast_k0": dict(flags=vc.DEFAULT_FLAGS, expcast_k=0),
         "exact_scores": dict(flags=vc.DEFAULT_FLAGS | vc.EXACT_SCORES),
         "v4_residual": dict(flags=vc.DEFAULT_FLAGS | vc.V4),
-    }
-    out = {}
-    for name, kw in variants.items():
-        p = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"], **kw)
-        ws = vc.alloc_workspace(p, dev)
-        o = torch.empty_like(qd)
-        vc.prepare(p, qd, kd, vd, ws)
-        vc.forward(p, ws, o)
-        torch.cuda.synchronize()
-        got = o.float().view(B * H, N, 128)[torch.as_tensor(slot, device=dev).long(),
-                                            torch.as_tensor(idx, device=dev).long()]
-        got = got.cpu().numpy().astype(np.float64)
-        out[name] = round(float(np.linalg.norm(got - ex) / np.linalg.norm(ex)), 6)
-        del ws, o
-    return {"reference": "exact fp64 softmax attention of the bf16 inputs", "heads": list(map(int, heads)),
-            "rows_per_head": int(len(rows)), "rel_l2_vs_exact": out,
-            "exact_rows_cpu_s": round(t_exact, 2)}
+    })
+    # structured V, seeded on the device: (a) a per-(head, channel) offset
+    # N(0, 30^2); (b) outlier tokens: 1% of the tokens of each head carry +40 in
+    # two channels drawn per head (value outliers sit on few tokens, in channels
+    # that change from head to head: noticiai.com.br article, V-Smooth section)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    offs = 30.0 * torch.randn((B, H, 1, 128), generator=g, device=dev)
+    tok = torch.rand((B, H, N, 1), generator=g, device=dev) < 0.01
+    ch = torch.randint(0, 128, (B, H, 1, 2), generator=g, device=dev)
+    spike = torch.zeros((B, H, 1, 128), device=dev).scatter_(3, ch, 40.0)
+    cases = {"channel_offsets": ("per (head, channel) N(0, 30^2) added to V", offs),
+             "outlier_tokens": ("1% of tokens per head +40 in two channels drawn per head", tok * spike)}
+    structured = {}
+    for cname, (desc, add) in cases.items():
+        vo = (vd.float() + add).to(torch.bfloat16)
+        r, _ = run(vo, {
+            "full": dict(flags=vc.DEFAULT_FLAGS),
+            "vsmooth_off": dict(flags=0),
+            "vsmooth_off_repair_on": dict(flags=vc.REPAIR | vc.PERMUTE_Q),
+            "repair_off": dict(flags=vc.VSMOOTH | vc.PERMUTE_Q),
+        })
+        structured[cname] = {"v": desc, "rel_l2_vs_exact": r}
+        del vo, add
+    return {"reference": "exact fp64 softmax attention of the bf16 inputs (torch fp64 on the device)",
+            "heads": list(map(int, heads)), "rows_per_head": int(len(rows)), "rel_l2_vs_exact": base,
+            "structured_v": structured, "exact_rows_s": round(t_exact, 2)}
 
 
 def per_workload(ids, dev, steps=10, warmup=2):
@@ -415,7 +460,7 @@ def main():
         res["cpu_baseline"], res["parity_sample"] = cpu_baseline(wl, q, k, v, P, flops, gpu_out)
     if not args.no_extras:
         print("bench: fidelity ablations", file=sys.stderr, flush=True)
-        res["fidelity"] = fidelity(wl, q, k, v, qd, kd, vd, dev, [0, B * H - 1],
+        res["fidelity"] = fidelity(wl, qd, kd, vd, dev, [0, B * H - 1],
                                    np.linspace(0, N - 1, 256).astype(np.int32))
         del ws, o
         torch.cuda.empty_cache()

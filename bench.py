@@ -290,6 +290,9 @@ def main():
                     help="with --forward-only: the 4-bit value residual variant")
     ap.add_argument("--smooth-q", action="store_true",
                     help="with --forward-only: the smoothed-query variant")
+    ap.add_argument("--prepare-only", action="store_true",
+                    help="time only vc_attn_prepare launches, cold (k-means) then reusing the clusters "
+                         "(profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -327,6 +330,18 @@ def main():
     def step():
         vc.prepare(p, qd, kd, vd, ws)
         vc.forward(p, ws, o)
+
+    if args.prepare_only:
+        preuse = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                                   flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
+        for _ in range(args.warmup):
+            vc.prepare(p, qd, kd, vd, ws)
+        torch.cuda.synchronize()
+        ms_cold = _events_ms(lambda: vc.prepare(p, qd, kd, vd, ws), args.steps)
+        ms_reuse = _events_ms(lambda: vc.prepare(preuse, qd, kd, vd, ws), args.steps)
+        print(json.dumps({"prepare_ms": round(ms_cold, 4), "prepare_reuse_clusters_ms": round(ms_reuse, 4),
+                          "launches": args.warmup + 2 * args.steps}))
+        return
 
     if args.forward_only:
         if args.v4 or args.smooth_q:

@@ -71,10 +71,39 @@ __device__ __forceinline__ uint64_t splitmix(uint64_t& st) {
   return z ^ (z >> 31);
 }
 
+// Cross-lane exchanges without LDS.  v_permlane16_swap with both operands x
+// leaves rows (0, 2) of x in the first result and rows (1, 3) in the second, so
+// every lane holds its own value and that of lane ^ 16, one in each result (the
+// order depends on the row); v_permlane32_swap does the same for lane ^ 32.
+__device__ __forceinline__ float xmax16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// min of x over lanes l, l ^ 16 (SHIFT 16) or l, l ^ 32 (SHIFT 32), fp64
+template <int SHIFT>
+__device__ __forceinline__ double xmin_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto pl = SHIFT == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                              : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto ph = SHIFT == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                              : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double a = __builtin_bit_cast(double, (uint64_t)pl[0] | ((uint64_t)ph[0] << 32));
+  const double c = __builtin_bit_cast(double, (uint64_t)pl[1] | ((uint64_t)ph[1] << 32));
+  return __builtin_fmin(a, c);
+}
+// max over the wave: rotations inside each 16-lane row (DPP row_ror 8, 4, 2, 1
+// leave the row's maximum in every lane), then rows by the swaps above
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
+  return xmax32(xmax16(x));
 }
 
 // Column of key r inside a 128-key block of the channel-major V codes: the fused
@@ -340,7 +369,13 @@ constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measure
 // (< 2^26) and never carries into the other; the bias is removed with the counts.
 constexpr int BROW2 = D / 2 + 1;  // LDS row of the packed bins (8-byte words)
 static_assert(KM_CHUNK * 24576ll < (1ll << 32), "packed member sums would carry");
-constexpr size_t km_smem_bytes(int C) { return (size_t)C * (2 * CROW + 8 * BROW2 + 8); }
+// Per-wave ring of the tokens whose label changed (chunk token index, and old <<
+// 8 | new label), drained 16 at a time so that the member-sum adds run on full
+// waves rather than on every subtile that holds one moved token.
+constexpr int KM_QUEUE = 32;
+constexpr size_t km_smem_bytes(int C) {
+  return (size_t)C * (2 * CROW + 8 * BROW2 + 8) + (size_t)KM_WAVES * KM_QUEUE * 8;
+}
 
 // LEAVE: add 16384 - u instead of u + 16384.
 template <bool LEAVE>
@@ -358,6 +393,26 @@ __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, co
         ub = 32768u - ub;
       }
       atomicAdd(&bins[base + 2 * wd + pr], (unsigned long long)ua | ((unsigned long long)ub << 32));
+    }
+  }
+}
+
+// A token moving from cluster old to cluster nw: adds u + 16384 to nw's bins and
+// 16384 - u to old's, with the channel pairs formed once.
+__device__ __forceinline__ void move_bins2(unsigned long long* bins, int nbase, int obase, const v4i& h,
+                                           const v4i& l) {
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t hb = (uint32_t)h[wd] ^ 0x80808080u;
+    const uint32_t lb = (uint32_t)l[wd];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
+      const uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
+      const unsigned long long x = (unsigned long long)ua | ((unsigned long long)ub << 32);
+      atomicAdd(&bins[nbase + 2 * wd + pr], x);
+      // (32768 - ua) | (32768 - ub) << 32: no borrow between the halves (ua, ub < 32768)
+      atomicAdd(&bins[obase + 2 * wd + pr], 0x0000800000008000ull - x);
     }
   }
 }
@@ -413,6 +468,8 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   int* cnt = reinterpret_cast<int*>(bins + C * BROW2);                    // [2][C]: entering, leaving
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
+  int* mq = cnt + 2 * C + w * 2 * KM_QUEUE;  // this wave's ring: token indices
+  int* ml = mq + KM_QUEUE;                  // old << 8 | new label
   const int* cf = a.centfix + (size_t)bh * C * D;
   for (int e = t; e < C * D; e += 64 * KM_WAVES) {
     const int u = cf[e];
@@ -460,6 +517,26 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     x.old = (!first && ok) ? a.labels[(size_t)bh * a.N + jj] : -1;
   };
   auto has = [&](int s) { return s < KM_CHUNK / 16 && first_tok + s * 16 < last; };  // uniform per wave
+  // moved tokens of later iterations: lane (g, q) of a drain takes ring entry
+  // qh + q, reloads channels 16g.. and 64+16g.. of that token (read by this wave
+  // a few subtiles earlier, normally still in L2) and moves its bins
+  int qh = 0, qn = 0;  // ring head and fill, uniform over the wave
+  auto drain = [&](int count) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (l16 < count) {
+      const int e = (qh + l16) & (KM_QUEUE - 1);
+      const int jj = mq[e], lab = ml[e];
+      const v4i h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
+      const v4i h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
+      const v4i l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
+      const v4i l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+      const int ob = (lab >> 8) * BROW2, nb = (lab & 0xff) * BROW2;
+      move_bins2(bins, nb + 8 * g, ob + 8 * g, h0, l0);
+      move_bins2(bins, nb + 32 + 8 * g, ob + 32 + 8 * g, h1, l1);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
   Sub nx;
   if (has(w)) load_sub(w, nx);
 #pragma unroll 1
@@ -499,26 +576,43 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
       }
     }
     // smallest key across the four lane groups
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) bestK = __builtin_fmin(bestK, __shfl_xor(bestK, off, 64));
+    bestK = xmin_f64<32>(xmin_f64<16>(bestK));
     const double hi = __builtin_floor(bestK * 0x1p-6);
     const int best = (int)__builtin_fma(-64.0, hi, bestK);
-    // only a token whose label changes touches the bins; a wave with none skips
+    // only a token whose label changes touches the bins
     const bool moved = j < last && best != old;
-    if (__ballot(moved) != 0ull && moved) {
-      if (g == 0) {
-        a.labels[(size_t)bh * a.N + j] = best;
-        atomicAdd(&cnt[best], 1);
-        if (old >= 0) atomicAdd(&cnt[C + old], 1);
+    if (first) {
+      // every token enters: the adds run on the subtile's own operands
+      if (__ballot(moved) != 0ull && moved) {
+        if (g == 0) {
+          a.labels[(size_t)bh * a.N + j] = best;
+          atomicAdd(&cnt[best], 1);
+        }
+        add_bins2<false>(bins, best * BROW2 + 8 * g, bh0, bl0);
+        add_bins2<false>(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
       }
-      add_bins2<false>(bins, best * BROW2 + 8 * g, bh0, bl0);
-      add_bins2<false>(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
-      if (old >= 0) {
-        add_bins2<true>(bins, old * BROW2 + 8 * g, bh0, bl0);
-        add_bins2<true>(bins, old * BROW2 + 32 + 8 * g, bh1, bl1);
+    } else {
+      // the four lane groups of a token agree on moved: bits 0-15 are the tokens
+      const uint32_t tm = (uint32_t)__ballot(moved) & 0xffffu;
+      if (tm != 0u) {
+        if (moved && g == 0) {
+          a.labels[(size_t)bh * a.N + j] = best;
+          atomicAdd(&cnt[best], 1);
+          atomicAdd(&cnt[C + old], 1);
+          const int e = (qh + qn + __popc(tm & ((1u << l16) - 1u))) & (KM_QUEUE - 1);
+          mq[e] = j;
+          ml[e] = (old << 8) | best;
+        }
+        qn += __popc(tm);
+        if (qn >= 16) {
+          drain(16);
+          qh = (qh + 16) & (KM_QUEUE - 1);
+          qn -= 16;
+        }
       }
     }
   }
+  if (qn > 0) drain(qn);
   __syncthreads();
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
   for (int e = t; e < C * D; e += 64 * KM_WAVES) {
@@ -900,7 +994,7 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
         for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(val(i, e) - smu[cg * 8 + e]));
       }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], __shfl_xor(m[e], 16, 64));
+    for (int e = 0; e < 8; ++e) m[e] = xmax16(m[e]);
     if ((r0 & 1) == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) smax[G][r0 >> 1][cg * 8 + e] = m[e];

@@ -1025,9 +1025,9 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
 
 // Channel c's residual scale, set by the head's largest |V - mu| (one per
 // channel: sv = max/448, inv = 448/max; 1 with the 4-bit residual), and block
-// blk's mean in V code units (mu * inv), in fp32 and as the bf16 high/low pair
-// the restore MFMA reads (groups of 16 blocks, channel-major).  Block 0 also
-// stores the scales; the last block clears its group's slots past the last block.
+// blk's mean in V code units (mu * inv).  Block 0 also stores the scales.  The
+// bf16 high/low pairs of the means that the restore MFMA reads are formed from
+// these by k_rep_select, which writes them in whole rows.
 __device__ __forceinline__ void v_channel(const Args& a, int bh, int blk, int c, float* mu_out, float* s_out,
                                           float* inv_out) {
   float s, inv;
@@ -1041,17 +1041,6 @@ __device__ __forceinline__ void v_channel(const Args& a, int bh, int blk, int c,
   const float mu = a.mu[o];
   const float x = mu * inv;
   a.mup[o] = x;
-  const uint16_t h = f2bf_rne(x);
-  const uint16_t l = f2bf_rne(x - __uint_as_float((uint32_t)h << 16));
-  uint16_t* base = a.mupt + (((size_t)bh * a.nch16 + (blk >> 4)) * 2) * D * 16 + (size_t)c * 16;
-  const int j = blk & 15;
-  base[j] = h;
-  base[D * 16 + j] = l;
-  if (blk == a.nblk - 1)
-    for (int jj = j + 1; jj < 16; ++jj) {
-      base[jj] = 0;
-      base[D * 16 + jj] = 0;
-    }
   *mu_out = mu;
   *s_out = s;
   *inv_out = inv;
@@ -1192,9 +1181,10 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Repair set: the m positions with the largest error (ties: lower position),
-// by an exact radix select on the 64-bit key (~err_bits, position), then a
-// compaction in position order.  grid BH, 1024 threads.
+// Restore operand and repair set.  First the bf16 high/low block means for the
+// restore MFMA; then (m > 0) the m positions with the largest error (ties:
+// lower position), by an exact radix select on the 64-bit key (~err_bits,
+// position), then a compaction in position order.  grid BH, 1024 threads.
 //
 // Most errors share their leading digits (sign and exponent), so one shared
 // 256-bin histogram would see most lanes of an LDS add hit the same word; each
@@ -1209,6 +1199,36 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   __shared__ int s_kth, s_kth_next, s_hsel;
   __shared__ int wtot[16];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  // the restore operand first: the bf16 high/low pair of every block mean in V
+  // code units, [group of 16 blocks][high, low][channel][block in group], slots
+  // past the last block 0.  A thread forms one (group, channel) row of 16
+  // blocks and stores it whole (the quantisation workgroups, one per block,
+  // would each write 2 bytes into every row).
+  for (int e = t; e < a.nch16 * D; e += 1024) {
+    const int grp = e / D, c = e % D;
+    const float* mp = a.mup + ((size_t)bh * a.nblk + grp * 16) * D + c;
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      uint32_t h2 = 0u, l2 = 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float x = grp * 16 + j + u < a.nblk ? mp[(size_t)(j + u) * D] : 0.0f;
+        const uint32_t h = f2bf_rne(x);
+        const uint32_t l = f2bf_rne(x - __uint_as_float(h << 16));
+        h2 |= h << (16 * u);
+        l2 |= l << (16 * u);
+      }
+      hw[j / 2] = h2;
+      lw[j / 2] = l2;
+    }
+    uint16_t* dst = a.mupt + (((size_t)bh * a.nch16 + grp) * 2) * D * 16 + (size_t)c * 16;
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    reinterpret_cast<uint4*>(dst + D * 16)[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    reinterpret_cast<uint4*>(dst + D * 16)[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  }
+  if (a.m == 0) return;  // no repair set (uniform)
   const int cp = lane & (RS_COPIES - 1);
   const float* err = a.err + (size_t)bh * a.N;
   auto key_of = [&](int j) {
@@ -1431,10 +1451,9 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
-  if (a.m > 0) {
-    hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);
-  }
+  // the restore operand always; the repair set when there is one
+  hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
+  if (a.m > 0) hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -351,10 +351,12 @@ __global__ __launch_bounds__(128) void k_km_warm(Args a) {
 // grid (nkm, BH), KM_WAVES waves (each takes every KM_WAVES-th 16-token subtile);
 // the head's tokens are cut into nkm chunks of equal size (a multiple of 16, at
 // most KM_CHUNK), one per workgroup, so that no workgroup is left with a short
-// tail chunk while the others run full ones.  Lane (g, j) of a 16-token subtile loads the
-// hi/lo bytes of channels 16g..16g+15 and 64+16g..64+16g+15 of token j as its
-// MFMA B operand; after the argmin the same registers are added to the LDS bins
-// of the token's cluster, so the planes are read once per iteration.
+// tail chunk while the others run full ones.  Lane (g, j) of a 16-token subtile
+// loads the hi/lo bytes of channels 16g..16g+15 and 64+16g..64+16g+15 of token j
+// as its MFMA B operand.  In the first iteration every token enters its cluster
+// and the same registers are added to the LDS bins; later, only moved tokens
+// touch the bins, through a per-wave ring that reloads their planes 16 at a time
+// (a few percent of the plane bytes once most labels have settled).
 constexpr int CROW = D + 16;  // padded LDS row (bytes): spreads rows over banks
 
 constexpr int KM_WAVES = 8;  // 8 waves: twice the loads in flight of 4 (measured 13 us
@@ -377,8 +379,8 @@ constexpr size_t km_smem_bytes(int C) {
   return (size_t)C * (2 * CROW + 8 * BROW2 + 8) + (size_t)KM_WAVES * KM_QUEUE * 8;
 }
 
-// LEAVE: add 16384 - u instead of u + 16384.
-template <bool LEAVE>
+// A token entering a cluster: adds u + 16384 to the cluster's bins, two channels
+// (16 of the token's, bytes of h and l) per 64-bit word.
 __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, const v4i& h, const v4i& l) {
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
@@ -386,12 +388,8 @@ __device__ __forceinline__ void add_bins2(unsigned long long* bins, int base, co
     const uint32_t lb = (uint32_t)l[wd];
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
-      uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
-      if (LEAVE) {
-        ua = 32768u - ua;
-        ub = 32768u - ub;
-      }
+      const uint32_t ua = (((hb >> (16 * pr)) & 0xffu) << 7) + ((lb >> (16 * pr)) & 0xffu);
+      const uint32_t ub = (((hb >> (16 * pr + 8)) & 0xffu) << 7) + ((lb >> (16 * pr + 8)) & 0xffu);
       atomicAdd(&bins[base + 2 * wd + pr], (unsigned long long)ua | ((unsigned long long)ub << 32));
     }
   }
@@ -588,8 +586,8 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
           a.labels[(size_t)bh * a.N + j] = best;
           atomicAdd(&cnt[best], 1);
         }
-        add_bins2<false>(bins, best * BROW2 + 8 * g, bh0, bl0);
-        add_bins2<false>(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
+        add_bins2(bins, best * BROW2 + 8 * g, bh0, bl0);
+        add_bins2(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
       }
     } else {
       // the four lane groups of a token agree on moved: bits 0-15 are the tokens

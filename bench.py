@@ -161,14 +161,16 @@ def _exact_rows(qd, kd, vd, heads, rows, scale):
     return torch.cat(out).cpu().numpy()
 
 
-def fidelity(wl, qd, kd, vd, dev, heads, rows):
+def fidelity(wl, qd, kd, vd, dev, heads, rows, light=False):
     """Relative L2 distance of GPU outputs to exact fp64 attention on sampled rows
     of the benchmark workload, for the full method and its ablations (V-Smooth
     off, repair off, the literal ExpCast offset k = 0, exact scores, the 4-bit
     residual).  Two more sets repeat the V-Smooth ablations on structured V: a
     large per-channel offset and a few outlier tokens (what V-Smooth's grouping
     and block means are for).  The pages report fidelity against unquantised
-    outputs (noticiai.com.br article, Benchmarks and V-Smooth sections)."""
+    outputs (noticiai.com.br article, Benchmarks and V-Smooth sections).  light:
+    only the full method, V-Smooth off, repair off and k = 0, without the
+    structured sets."""
     import numpy as np
     import torch
 
@@ -197,6 +199,14 @@ def fidelity(wl, qd, kd, vd, dev, heads, rows):
             del ws, o
         return out, t_exact
 
+    if light:
+        base, t_exact = run(vd, {
+            "full": dict(flags=vc.DEFAULT_FLAGS),
+            "vsmooth_off": dict(flags=0),
+            "repair_off": dict(flags=vc.VSMOOTH | vc.PERMUTE_Q),
+            "expcast_k0": dict(flags=vc.DEFAULT_FLAGS, expcast_k=0),
+        })
+        return {"heads": list(map(int, heads)), "rows_per_head": int(len(rows)), "rel_l2_vs_exact": base}
     base, t_exact = run(vd, {
         "full": dict(flags=vc.DEFAULT_FLAGS),
         "vsmooth_off": dict(flags=0),                        # identity order, no means, no repair
@@ -235,9 +245,11 @@ def fidelity(wl, qd, kd, vd, dev, heads, rows):
 
 
 def per_workload(ids, dev, steps=10, warmup=2):
-    """Forward, prepare and step times of the other workloads (all heads, full
-    size): token counts from the FLUX.3 Klein launch article (Vitesse et
-    memoire) and a 5 s 720p video clip."""
+    """Forward, prepare (cold and reusing the clusters) and step times of the
+    other workloads (all heads, full size), and their relative L2 distance to
+    exact attention for the full method and its ablations: token counts from
+    the FLUX.3 Klein launch article (Vitesse et memoire) and a 5 s 720p video
+    clip."""
     import numpy as np
     import torch
 
@@ -265,12 +277,21 @@ def per_workload(ids, dev, steps=10, warmup=2):
         ms_step = _events_ms(step, max(steps // 2, 2))
         ms_fwd = _events_ms(lambda: vc.forward(p, ws, o), steps)
         ms_prep = _events_ms(lambda: vc.prepare(p, qd, kd, vd, ws), max(steps // 2, 2))
+        preuse = vc.default_params(B, H, N, n_clusters=wl["C"], kmeans_iters=wl["T"], rho=wl["rho"],
+                                   flags=vc.DEFAULT_FLAGS | vc.REUSE_CLUSTERS)
+        ms_reuse = _events_ms(lambda: vc.prepare(preuse, qd, kd, vd, ws), max(steps // 2, 2))
         tf = flops / (ms_fwd * 1e-3) / 1e12
         res[wl["name"]] = {"B": B, "H": H, "N": N, "clusters": wl["C"], "forward_ms": round(ms_fwd, 4),
                            "forward_tflops": round(tf, 2), "forward_pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
-                           "prepare_ms": round(ms_prep, 4), "ms_per_step": round(ms_step, 4),
+                           "prepare_ms": round(ms_prep, 4), "prepare_reuse_clusters_ms": round(ms_reuse, 4),
+                           "ms_per_step": round(ms_step, 4),
                            "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2)}
-        del qd, kd, vd, ws, o
+        del ws, o
+        torch.cuda.empty_cache()
+        # relative L2 to exact fp64 attention on 128 rows of the first and last head
+        res[wl["name"]]["fidelity"] = fidelity(wl, qd, kd, vd, dev, [0, B * H - 1],
+                                               np.linspace(0, N - 1, 128).astype(np.int32), light=True)
+        del qd, kd, vd
         torch.cuda.empty_cache()
     return res
 

@@ -375,8 +375,13 @@ static_assert(KM_CHUNK * 24576ll < (1ll << 32), "packed member sums would carry"
 // 8 | new label), drained 16 at a time so that the member-sum adds run on full
 // waves rather than on every subtile that holds one moved token.
 constexpr int KM_QUEUE = 32;
+// Tokens of one cluster in a 16-lane group add to the same bin words, and those
+// atomics serialise; up to 32 clusters the bins are kept twice (even and odd
+// lanes), halving the collisions (the dynamic LDS stays within 64 KB for every
+// cluster count).
+__host__ __device__ constexpr int km_copies(int C) { return C <= 32 ? 2 : 1; }
 constexpr size_t km_smem_bytes(int C) {
-  return (size_t)C * (2 * CROW + 8 * BROW2 + 8) + (size_t)KM_WAVES * KM_QUEUE * 8;
+  return (size_t)C * (2 * CROW + 8 * BROW2 * km_copies(C) + 8) + (size_t)KM_WAVES * KM_QUEUE * 8;
 }
 
 // A token entering a cluster: adds u + 16384 to the cluster's bins, two channels
@@ -462,10 +467,12 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   const int C = a.C;
   int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                       // [C][CROW]
   int8_t* clo = chi + C * CROW;                                           // [C][CROW]
-  unsigned long long* bins = reinterpret_cast<unsigned long long*>(clo + C * CROW);  // [C][BROW2]
-  int* cnt = reinterpret_cast<int*>(bins + C * BROW2);                    // [2][C]: entering, leaving
+  const int ncopy = km_copies(C);
+  unsigned long long* bins = reinterpret_cast<unsigned long long*>(clo + C * CROW);  // [ncopy][C][BROW2]
+  int* cnt = reinterpret_cast<int*>(bins + ncopy * C * BROW2);            // [2][C]: entering, leaving
   const int bh = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, l16 = lane & 15;
+  unsigned long long* mybins = bins + (ncopy == 2 ? (l16 & 1) * C * BROW2 : 0);  // this lane's copy
   int* mq = cnt + 2 * C + w * 2 * KM_QUEUE;  // this wave's ring: token indices
   int* ml = mq + KM_QUEUE;                  // old << 8 | new label
   const int* cf = a.centfix + (size_t)bh * C * D;
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     chi[(e / D) * CROW + (e % D)] = (int8_t)(u >> 7);
     clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
   }
-  for (int e = t; e < C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
+  for (int e = t; e < ncopy * C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
   if (t < 2 * C) cnt[t] = 0;
   // Distances as exact fp64 keys.  For centroid k, D = ||c||^2 - 2 u.c with
   // |D| < 2^35, and key = 64 (D + 2^35) + k is an integer below 2^42, exact in
@@ -530,8 +537,8 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
       const v4i l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
       const v4i l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
       const int ob = (lab >> 8) * BROW2, nb = (lab & 0xff) * BROW2;
-      move_bins2(bins, nb + 8 * g, ob + 8 * g, h0, l0);
-      move_bins2(bins, nb + 32 + 8 * g, ob + 32 + 8 * g, h1, l1);
+      move_bins2(mybins, nb + 8 * g, ob + 8 * g, h0, l0);
+      move_bins2(mybins, nb + 32 + 8 * g, ob + 32 + 8 * g, h1, l1);
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -586,8 +593,8 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
           a.labels[(size_t)bh * a.N + j] = best;
           atomicAdd(&cnt[best], 1);
         }
-        add_bins2(bins, best * BROW2 + 8 * g, bh0, bl0);
-        add_bins2(bins, best * BROW2 + 32 + 8 * g, bh1, bl1);
+        add_bins2(mybins, best * BROW2 + 8 * g, bh0, bl0);
+        add_bins2(mybins, best * BROW2 + 32 + 8 * g, bh1, bl1);
       }
     } else {
       // the four lane groups of a token agree on moved: bits 0-15 are the tokens
@@ -615,7 +622,9 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
   for (int e = t; e < C * D; e += 64 * KM_WAVES) {
     const int c = e / D, ch = e % D;
-    const unsigned long long wv = bins[c * BROW2 + (ch >> 1)];
+    // the copies' halves each stay below 2^26, so their sum cannot carry
+    unsigned long long wv = bins[c * BROW2 + (ch >> 1)];
+    if (ncopy == 2) wv += bins[(C + c) * BROW2 + (ch >> 1)];
     const uint32_t half = (ch & 1) ? (uint32_t)(wv >> 32) : (uint32_t)wv;
     part[e] = (int)half - 16384 * (cnt[c] + cnt[C + c]);
   }

@@ -216,6 +216,29 @@ def test_kmeans_fixed_point_larger_head():
     assert np.array_equal(pr["centroids"][0].astype(np.float64), cent)
 
 
+def test_kmeans_fixed_point_quality_matches_real_valued_lloyd():
+    """At head sizes like the workloads', the fixed-point Lloyd (R1) clusters as
+    well as a real-valued fp64 Lloyd from the same initial centroids: the
+    within-cluster sum of squares after ten rounds is within 2% of it (the
+    labels themselves drift apart from ties on the 2^-13 max|v| grid)."""
+    for (N, C_, T, seed) in [(2048, 32, 10, 3), (1024, 8, 10, 0)]:
+        q, k, v = inputs.make_custom(1, 1, N, seed=seed, rate=0.01, sigma=20.0)
+        P = orc.make_params(1, 1, N, C_=C_, T=T, seed=seed, rho=0.0)
+        pr = orc.prepare(P, q, k, v)
+        vf = inputs.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+        cent = vf[orc.kmeans_init_indices(seed, 0, N, C_)].copy()
+        for _ in range(T):
+            d2 = (vf * vf).sum(1)[:, None] + (cent * cent).sum(1)[None, :] - 2 * vf @ cent.T
+            lab = np.argmin(d2, axis=1)
+            for kk in range(C_):
+                if np.any(lab == kk):
+                    cent[kk] = vf[lab == kk].mean(0)
+        sse_real = ((vf - cent[lab]) ** 2).sum()
+        cf = pr["centroids"][0].astype(np.float64)
+        sse_fixed = ((vf - cf[pr["labels"][0]]) ** 2).sum()
+        assert abs(sse_fixed - sse_real) <= 0.02 * sse_real, (N, C_, sse_fixed, sse_real)
+
+
 def test_kmeans_recovers_planted_blobs():
     rng = np.random.default_rng(3)
     N, C_ = 600, 4

@@ -514,11 +514,11 @@ def _sweep_cases(n=40, seed=7):
                   tau=float(rng.choice([0.0, 0.0, 3.0, 6.0])), expcast_k=int(rng.choice([8, 8, 0, 4])),
                   T=int(rng.choice([1, 3, 10])), sm_scale=float(rng.choice([0.0, 0.0, 0.02, 0.2])),
                   seed=int(rng.integers(0, 1 << 30)))
-        cases.append((f"s{i}_B{B}H{H}N{N}C{C_}f{flags}", B, H, N, C_, kw))
+        cases.append((f"r{seed}s{i}_B{B}H{H}N{N}C{C_}f{flags}", B, H, N, C_, kw))
     return cases
 
 
-SWEEP = _sweep_cases()
+SWEEP = _sweep_cases() + _sweep_cases(seed=404)
 
 
 @pytest.mark.parametrize("label,B,H,N,C_,kw", SWEEP, ids=[c[0] for c in SWEEP])
@@ -560,11 +560,11 @@ def _warm_cases(n=12, seed=99):
         kw = dict(flags=flags, Tc=int(rng.choice([1, 3, 10])), Tw=int(rng.choice([1, 2, 3, 5])),
                   rho=float(rng.choice([0.0, 0.005, 0.05, 1.0])), step=int(rng.integers(1, 4)),
                   seed=int(rng.integers(0, 1 << 30)))
-        cases.append((f"w{i}_B{B}H{H}N{N}C{C_}f{flags}", B, H, N, C_, kw))
+        cases.append((f"w{seed}_{i}_B{B}H{H}N{N}C{C_}f{flags}", B, H, N, C_, kw))
     return cases
 
 
-WARM = _warm_cases()
+WARM = _warm_cases() + _warm_cases(seed=11)
 
 
 @pytest.mark.parametrize("label,B,H,N,C_,kw", WARM, ids=[c[0] for c in WARM])

@@ -20,6 +20,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "vc_oracle.c")
 LIB = os.path.join(HERE, "libvcoracle.so")
+# Test hook: a prebuilt variant of the oracle to load instead (the mutation
+# test plants one mistake per build and checks that the pins catch it).
+LIB_OVERRIDE = os.environ.get("VC_ORACLE_LIB")
 
 # Flag bits of the oracle's own parameter block (the same meaning as the
 # library's public flags, defined here independently).
@@ -65,8 +68,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
-        L = C.CDLL(LIB)
+        if LIB_OVERRIDE:
+            L = C.CDLL(LIB_OVERRIDE)
+        else:
+            build(force=False)
+            L = C.CDLL(LIB)
         vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.oc_prepare.argtypes = [C.POINTER(Params), vp, vp, vp, vp, i32, C.POINTER(_Prep)]
         L.oc_forward_rows.argtypes = [C.POINTER(Params), C.POINTER(_Prep), vp, vp, i32, vp, vp, vp]

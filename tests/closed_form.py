@@ -67,6 +67,38 @@ def rescale_case(jump: int, seed: int = 0):
     return q.reshape(shp), k.reshape(shp), v.reshape(shp), row, want
 
 
+def lazy_max_case(seed: int = 0):
+    """The online case with a jump of 4 code units, below a lazy-maximum slack
+    tau = 6 (R11: M moves only when a block maximum exceeds it by more than
+    tau).  M stays at block 0's maximum, so block 0's codes are 56+8k = 120
+    (E4M3 256) and block 1's are 124 (E4M3 384), with no rescale:
+    O = (256 mu0 + 384 mu1) / 640 = 0.4 mu0 + 0.6 mu1.  Without the slack M
+    would move and the weights would be 1 : 2^(-1/2) instead.  Returns bf16-exact
+    float32 q, k, v [1, 1, 256, 128], the row and its expected output (k = 8)."""
+    N, d = 256, 128
+    a = -7
+    b = -15 - a                                  # 2^16 * 2^(a+b) = 2 = jump / 2
+    q = np.zeros((N, d), np.float32)
+    k = np.zeros((N, d), np.float32)
+    row = 5
+    q[row, 0] = 256.0 * 2.0 ** a
+    q[7, 1] = 448.0 * 2.0 ** a
+    k[:128, 0] = -256.0 * 2.0 ** b
+    k[128:, 0] = 256.0 * 2.0 ** b
+    for j0 in (10, 140):
+        k[j0, 1] = 448.0 * 2.0 ** b
+        k[j0 + 1, 1] = -448.0 * 2.0 ** b
+    rng = np.random.default_rng(seed)
+    mu0 = rng.integers(-4, 5, d).astype(np.float32)
+    mu1 = rng.integers(-4, 5, d).astype(np.float32)
+    v = np.zeros((N, d), np.float32)
+    v[:128] = mu0
+    v[128:] = mu1
+    want = (256.0 * mu0.astype(np.float64) + 384.0 * mu1.astype(np.float64)) / 640.0
+    shp = (1, 1, N, d)
+    return q.reshape(shp), k.reshape(shp), v.reshape(shp), row, want
+
+
 def block_constant_values(N: int, seed: int = 0) -> np.ndarray:
     """float32 V [N, 128] constant inside every 128-token block (rows of small
     multiples of 1/4, exact in bf16)."""

@@ -186,6 +186,24 @@ def test_online_rescale_closed_form(jump, extra):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("extra", [0, 256], ids=["exact", "fp8"])
+def test_lazy_maximum_closed_form(extra):
+    """The lazy-maximum case (tests/closed_form.py): with tau = 6 a jump of 4
+    code units leaves M in place, block 1's codes are 124 and the output is
+    0.4 mu0 + 0.6 mu1, here within O's bf16 rounding."""
+    import closed_form
+    import precision_fp8_attention_amd as vc
+    qf, kf, vf, row, want = closed_form.lazy_max_case(seed=3)
+    q, k, v = (inputs.to_bf16_bits(x) for x in (qf, kf, vf))
+    p = G.lib_params(1, 1, 256, 1, T=2, flags=vc.DEFAULT_FLAGS | extra, tau=6.0,
+                     sm_scale=closed_form.unit_gain_scale())
+    G.log(f"[case] closed-form lazy maximum flags={p.flags}")
+    qd, kd, vd = G.to_device(q, k, v)
+    ws, o = G.run(p, qd, kd, vd)
+    got = G.out_f64(o).reshape(256, 128)[row]
+    np.testing.assert_allclose(got, want, rtol=2.0 ** -8, atol=1e-6)
+
+
 def test_workload3_exact_scores_sampled():
     """The benchmark workload with exact scores (bf16 score MFMA), one head."""
     import precision_fp8_attention_amd as vc

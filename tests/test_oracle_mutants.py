@@ -49,6 +49,26 @@ MUTANTS = [
     ("mx_exponent_off", "int x = e - 3;", "int x = e - 2;"),
     ("smoothq_kbar_dropped", "delta = fmaf(qm[c], k[(size_t)perm[p] * d + c] - kbar[c], delta);",
      "delta = fmaf(qm[c], k[(size_t)perm[p] * d + c], delta);"),
+    ("score_fp32_sum", "  double s = 0.0;\n  for (int c = 0; c < d; ++c) s += DEC[a[c]] * DEC[b[c]];",
+     "  float s = 0.0f;\n  for (int c = 0; c < d; ++c) s += (float)(DEC[a[c]] * DEC[b[c]]);"),
+    ("mean_denominator", "return (float)(((double)sum * 0x1p-24) / (double)n);",
+     "return (float)(((double)sum * 0x1p-24) / (double)(n + 1));"),
+    ("fx24_truncated", "static int64_t fx24(float x) { return llrintf(x * 16777216.0f); }",
+     "static int64_t fx24(float x) { return (int64_t)(x * 16777216.0f); }"),
+    ("repair_count_floor", "m = ceil((double)P->rho * (double)P->N);", "m = floor((double)P->rho * (double)P->N);"),
+    ("lazy_max_ignored", "Mn = (isinf(M) || (tmax - M) > P->tau) ? tmax : M;", "Mn = (isinf(M) || tmax > M) ? tmax : M;"),
+    ("warm_start_truncated", "int64_t x = llrintf(ldexpf(cent[i], sh));", "int64_t x = (int64_t)(ldexpf(cent[i], sh));"),
+    ("repair_without_max", "DEC[oc_expcast(s, alpha, bias - M)];", "DEC[oc_expcast(s, alpha, bias)];"),
+    ("repair_first_block_scale", "    float alpha = (sq[a] * sk[b]) * c0;\n    float s = raw_score",
+     "    float alpha = (sq[a] * sk[0]) * c0;\n    float s = raw_score"),
+    ("output_row_perm", "const int p = (P->flags & OC_PERMUTE_Q) ? o->iperm[(size_t)slot * N + row] : row;",
+     "const int p = (P->flags & OC_PERMUTE_Q) ? o->perm[(size_t)slot * N + row] : row;"),
+    ("forgy_duplicates", "int32_t j = i + (int32_t)(r % (uint64_t)(N - i));", "int32_t j = (int32_t)(r % (uint64_t)N);"),
+    ("code_clamp_127", "if (y > 126.0f) return 126;", "if (y > 127.0f) return 127;"),
+    ("e4m3_saturate_nan", "    code = 0x7e;\n  } else if (a < ldexp(1.0, -6)) {", "    code = 0x7f;\n  } else if (a < ldexp(1.0, -6)) {"),
+    ("mx_exponent_floor", "return x < -126 ? -126 : (x > 127 ? 127 : x);", "return x < -127 ? -127 : (x > 127 ? 127 : x);"),
+    ("kmeans_ties_high", "if (k == 0 || D < bestD) {", "if (k == 0 || D <= bestD) {"),
+    ("e4m3_subnormal_scale", "    v = ldexp((double)m, -9);", "    v = ldexp((double)m, -10);"),
 ]
 
 

@@ -239,6 +239,68 @@ def test_kmeans_fixed_point_quality_matches_real_valued_lloyd():
         assert abs(sse_fixed - sse_real) <= 0.02 * sse_real, (N, C_, sse_fixed, sse_real)
 
 
+def _one_channel_head(vals, N_extra=0):
+    """bf16 bits [1, 1, N, 128] whose channel 0 holds vals (fixed-point units of
+    2^-12: the first value 1.0 sets max|v| = 1, so sh = 12) and the rest 0."""
+    v = np.zeros((len(vals), 128), np.float64)
+    v[:, 0] = np.asarray(vals, np.float64) / 4096.0
+    return inputs.to_bf16_bits(v)[None, None]
+
+
+def test_kmeans_ties_go_to_the_lowest_id():
+    """R1: a token at the same integer distance from two centroids joins the
+    one with the lower id.  Tokens 4096, -8, 8, 0 (fixed-point units, sh = 12);
+    a seed whose Forgy draw picks tokens -8 and 8 leaves token 0 exactly between
+    them, and after one assignment it carries the smaller of their ids."""
+    vb = _one_channel_head([4096, -8, 8, 0])
+    z = np.zeros_like(vb)
+    for seed in range(200):
+        init = orc.kmeans_init_indices(seed, 0, 4, 2)
+        if sorted(init.tolist()) == [1, 2]:
+            break
+    else:
+        raise AssertionError("no seed draws tokens 1 and 2")
+    P = orc.make_params(1, 1, 4, C_=2, T=1, seed=seed, rho=0.0)
+    lab = orc.prepare(P, z, z, vb)["labels"][0]
+    id_of = {int(init[0]): 0, int(init[1]): 1}
+    assert lab[1] == id_of[1] and lab[2] == id_of[2]
+    assert lab[3] == 0            # the tie: the lower id
+    assert lab[0] == id_of[2]     # 4096 is nearer to 8
+
+
+def test_warm_start_rounds_centroids_to_nearest():
+    """R17: warm-start centroids are scaled to the current fixed point and
+    rounded to the nearest integer.  Centroids 2.6 and 7.6 (units of 2^-12)
+    become 3 and 8, so token 5 (distance 2 against 3) joins the first and token
+    4096 the second; truncation (2 and 7) would send token 5 to the second."""
+    vb = _one_channel_head([4096, 5, 0])
+    z = np.zeros_like(vb)
+    cent = np.zeros((1, 2, 128), np.float32)
+    cent[0, 0, 0] = 2.6 / 4096.0
+    cent[0, 1, 0] = 7.6 / 4096.0
+    P = orc.make_params(1, 1, 3, C_=2, T=1, rho=0.0)
+    P.flags |= orc.WARM_START
+    lab = orc.prepare(P, z, z, vb, init_centroids=cent)["labels"][0]
+    assert lab.tolist() == [1, 0, 0]
+
+
+def test_fixed_point_means_round_to_nearest():
+    """R8: means are exact sums of values rounded to the 2^-24 grid.  Every K
+    (and V) value of channel 0 is +-1.5 * 2^-25, i.e. +-0.75 grid steps, which
+    rounds to +-1 step: the K channel mean and the V block means are then
+    exactly +-2^-24 (truncation would give 0)."""
+    N = 256
+    for sgn in (1.0, -1.0):
+        x = np.zeros((N, 128), np.float64)
+        x[:, 0] = sgn * 1.5 * 2.0 ** -25
+        x[:, 1] = np.linspace(-1, 1, N)            # a nonzero head, ordinary values elsewhere
+        xb = inputs.to_bf16_bits(x)[None, None]
+        P = orc.make_params(1, 1, N, C_=1, T=1, rho=0.0)
+        pr = orc.prepare(P, xb, xb, xb)
+        assert pr["kbar"][0][0] == np.float32(sgn * 2.0 ** -24)
+        assert np.all(pr["mu"][0][:, 0] == np.float32(sgn * 2.0 ** -24))
+
+
 def test_kmeans_recovers_planted_blobs():
     rng = np.random.default_rng(3)
     N, C_ = 600, 4
@@ -623,6 +685,51 @@ def test_online_rescale_closed_form(jump, tau):
     np.testing.assert_array_equal(out[0], want)
     ex = orc.exact_rows(P, q, k, v, np.zeros(1), np.array([row]))
     np.testing.assert_allclose(ex[0], want, rtol=1e-6, atol=1e-6)
+
+
+def test_repair_restores_coherent_residuals_with_their_own_block_scales():
+    """R14: repaired keys are coded with their own block's scale.  V is 17/32
+    everywhere but one token at 1 (which sets each channel's scale), so every
+    other value lands 2 code units from its E4M3 code, the same error on every
+    key; K's second block is 8x larger, so its keys dominate the softmax.
+    Without repair the output is off by 0.8%; repairing every key (rho = 1)
+    restores V and the output equals exact attention to 1e-5.  A repaired key
+    coded with another block's scale would weight its correction wrongly."""
+    N = 384
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((N, 128))
+    k = rng.standard_normal((N, 128))
+    k[128:256] *= 8.0
+    k[256:] /= 8.0
+    v = np.full((N, 128), 17.0 / 32.0)
+    v[17, :] = 1.0
+    qb, kb, vb = (inputs.to_bf16_bits(x)[None, None] for x in (q, k, v))
+    rows = np.arange(0, N, 3).astype(np.int32)
+    rel = {}
+    for rho in (0.0, 1.0):
+        P = orc.make_params(1, 1, N, C_=1, T=1, rho=rho, sm_scale=0.2)
+        P.flags = orc.REPAIR | orc.PERMUTE_Q  # V-Smooth off: the residual codes carry V
+        pr = orc.prepare(P, qb, kb, vb)
+        out = orc.forward_rows(P, pr, np.zeros(len(rows), np.int32), rows)
+        ex = orc.exact_rows(P, qb, kb, vb, np.zeros(len(rows), np.int32), rows)
+        rel[rho] = np.linalg.norm(out - ex) / np.linalg.norm(ex)
+    assert rel[0.0] > 5e-3 and rel[1.0] < 1e-5, rel
+
+
+def test_lazy_maximum_closed_form():
+    """R11 with tau = 6: block 1's maximum exceeds block 0's by 4 code units,
+    within the slack, so M stays, block 1's codes are 124 and the output is
+    0.4 mu0 + 0.6 mu1 (tests/closed_form.py).  With tau = 0 the same inputs move
+    M and give codes of 120 in both blocks."""
+    q, k, v, row, want = closed_form.lazy_max_case(seed=3)
+    q, k, v = (inputs.to_bf16_bits(x) for x in (q, k, v))
+    P = orc.make_params(1, 1, 256, C_=1, T=2, tau=6.0, sm_scale=closed_form.unit_gain_scale())
+    (out, pc), pr, _, _ = _sim(P, q, k, v, rows=[row], pcodes=True)
+    assert np.all(pc[0][:128] == 120) and np.all(pc[0][128:] == 124)
+    np.testing.assert_allclose(out[0], want, rtol=1e-12, atol=1e-12)
+    P0 = orc.make_params(1, 1, 256, C_=1, T=2, tau=0.0, sm_scale=closed_form.unit_gain_scale())
+    (out0, pc0), _, _, _ = _sim(P0, q, k, v, rows=[row], pcodes=True)
+    assert np.all(pc0[0] == 120)
 
 
 def test_online_equals_two_pass_when_the_maximum_never_moves():

@@ -69,6 +69,27 @@ MUTANTS = [
     ("mx_exponent_floor", "return x < -126 ? -126 : (x > 127 ? 127 : x);", "return x < -127 ? -127 : (x > 127 ? 127 : x);"),
     ("kmeans_ties_high", "if (k == 0 || D < bestD) {", "if (k == 0 || D <= bestD) {"),
     ("e4m3_subnormal_scale", "    v = ldexp((double)m, -9);", "    v = ldexp((double)m, -10);"),
+    ("exact_scale_dropped", "      s[j] = t * scale;", "      s[j] = t;"),
+    ("exact_weight_squared", "      double w = exp(s[j] - mx);", "      double w = exp(2.0 * (s[j] - mx));"),
+    ("empty_cluster_zeroed", "    for (int k = 0; k < C; ++k)\n      if (cnt[k] > 0)",
+     "    for (int k = 0; k < C; ++k)\n      if (cnt[k] == 0) for (int ch = 0; ch < d; ++ch) c[(size_t)k * d + ch] = 0; else if (cnt[k] > 0)"),
+    ("forgy_head_index", "uint64_t st = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(head + 1));",
+     "uint64_t st = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(head + 2));"),
+    ("tail_mean_full_block", "        mu[(size_t)b * d + c] = fixed_mean(s, p1 - p0);", "        mu[(size_t)b * d + c] = fixed_mean(s, 128);"),
+    ("zero_amax_scale", "    *s = 1.0f;\n    *inv = 1.0f;", "    *s = 0.0f;\n    *inv = 1.0f;"),
+    ("expcast_floor_code_1", "  if (!(y > 0.0f)) return 0; /* also maps -inf (masked keys) to 0 */",
+     "  if (!(y > 0.0f)) return 1;"),
+    ("e4m3_sign_dropped", "  uint8_t sign = signbit(xf) ? 0x80 : 0x00;", "  uint8_t sign = (xf < 0.0f) ? 0x80 : 0x00;"),
+    ("repair_ties_later", "if (best < 0 || err[p] > err[best]) best = p;", "if (best < 0 || err[p] >= err[best]) best = p;"),
+    ("smoothq_mean_unpermuted", "for (int p = p0; p < p1; ++p) sum += fx24(q[(size_t)((P->flags & OC_PERMUTE_Q) ? perm[p] : p) * d + c]);",
+     "for (int p = p0; p < p1; ++p) sum += fx24(q[(size_t)p * d + c]);"),
+    ("smoothq_code_alpha", "code[j - j0] = dq ? oc_expcast(S[j - j0], 1.0f, beta) : oc_expcast(S[j - j0], alpha, beta);",
+     "code[j - j0] = dq ? oc_expcast(S[j - j0], alpha, beta) : oc_expcast(S[j - j0], alpha, beta);"),
+    ("q_unpermuted_codes", "      int jq = (P->flags & OC_PERMUTE_Q) ? perm[p] : p, jk = perm[p];",
+     "      int jq = p, jk = perm[p];"),
+    ("v4_repair_delta_unscaled", "  if (!v4) return (float)oc_e4m3_decode(code);", "  if (!v4 || p >= 0) return (float)oc_e4m3_decode(code);"),
+    ("bf16_round_truncated", "  u += 0x7fffu + ((u >> 16) & 1u);\n  return (uint16_t)(u >> 16);\n}",
+     "  return (uint16_t)(u >> 16);\n}"),
 ]
 
 

@@ -268,6 +268,46 @@ def test_kmeans_ties_go_to_the_lowest_id():
     assert lab[0] == id_of[2]     # 4096 is nearer to 8
 
 
+def test_empty_cluster_keeps_its_centroid():
+    """R1: a cluster left without members keeps its centroid.  Tokens 4096,
+    100, 100, 50 (fixed-point units); a Forgy draw of the two tokens at 100
+    puts both centroids there, every token ties and joins the lower id, so
+    cluster 1 is empty: it stays at 100 while cluster 0 moves to the rounded
+    mean 1086 (4346 / 4 = 1086.5, ties to even)."""
+    vb = _one_channel_head([4096, 100, 100, 50])
+    z = np.zeros_like(vb)
+    for seed in range(400):
+        if sorted(orc.kmeans_init_indices(seed, 0, 4, 2).tolist()) == [1, 2]:
+            break
+    else:
+        raise AssertionError("no seed draws tokens 1 and 2")
+    P = orc.make_params(1, 1, 4, C_=2, T=1, seed=seed, rho=0.0)
+    pr = orc.prepare(P, z, z, vb)
+    assert pr["labels"][0].tolist() == [0, 0, 0, 0]
+    cent = pr["centroids"][0][:, 0].astype(np.float64) * 4096.0
+    assert cent.tolist() == [1086.0, 100.0]
+
+
+def test_repair_ties_go_to_lower_positions():
+    """R14: among equal errors the lower position is repaired first.  Every V
+    row is the same, so every token has the same error (0 after demeaning, or the
+    same quantisation error without V-Smooth): the repair set is the first m
+    positions."""
+    N = 300
+    rng = np.random.default_rng(2)
+    q = inputs.to_bf16_bits(rng.standard_normal((N, 128)))[None, None]
+    k = inputs.to_bf16_bits(rng.standard_normal((N, 128)))[None, None]
+    row = rng.standard_normal(128) * 3.0
+    v = inputs.to_bf16_bits(np.tile(row, (N, 1)))[None, None]
+    for flags in (orc.DEFAULT_FLAGS, orc.REPAIR | orc.PERMUTE_Q):
+        P = orc.make_params(1, 1, N, C_=1, T=1, rho=0.02)
+        P.flags = flags
+        pr = orc.prepare(P, q, k, v)
+        m = pr["m"]
+        assert m == 6
+        assert pr["rep_pos"][0][:m].tolist() == list(range(m))
+
+
 def test_warm_start_rounds_centroids_to_nearest():
     """R17: warm-start centroids are scaled to the current fixed point and
     rounded to the nearest integer.  Centroids 2.6 and 7.6 (units of 2^-12)

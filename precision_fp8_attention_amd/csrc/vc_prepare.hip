@@ -730,7 +730,9 @@ __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
 // as raw bf16 (32 registers, not 64 floats) and converts them where they are
 // used, which doubles the waves a CU holds and the rows in flight.
 template <bool SMOOTH>
-__global__ __launch_bounds__(256, SMOOTH ? 4 : 8) void k_qk_quant(Args a) {
+// Seven workgroups per CU: 72 VGPRs; at eight the compiler spills to scratch
+// (measured the same time, or 3 us slower with clusters reused).
+__global__ __launch_bounds__(256, SMOOTH ? 4 : 7) void k_qk_quant(Args a) {
   __shared__ float wmax[4];
   __shared__ long long qsum[16][D];
   __shared__ float qmean[D];

@@ -90,6 +90,21 @@ MUTANTS = [
     ("v4_repair_delta_unscaled", "  if (!v4) return (float)oc_e4m3_decode(code);", "  if (!v4 || p >= 0) return (float)oc_e4m3_decode(code);"),
     ("bf16_round_truncated", "  u += 0x7fffu + ((u >> 16) & 1u);\n  return (uint16_t)(u >> 16);\n}",
      "  return (uint16_t)(u >> 16);\n}"),
+    ("code_gain_ln", "return (float)(8.0 * 1.4426950408889634074 * (double)sm_scale_of(P));",
+     "return (float)(8.0 * (double)sm_scale_of(P));"),
+    ("default_scale_inverse_d", "return P->sm_scale > 0.0f ? P->sm_scale : (float)(1.0 / sqrt((double)P->d));",
+     "return P->sm_scale > 0.0f ? P->sm_scale : (float)(1.0 / (double)P->d);"),
+    ("warm_clamp_narrow", "c[i] = x < -8192 ? -8192 : (x > 8191 ? 8191 : x);", "c[i] = x < -4096 ? -4096 : (x > 4095 ? 4095 : x);"),
+    ("v4_value_exponent_off", "  return ldexpf((float)oc_e2m1_decode(code), X);", "  return ldexpf((float)oc_e2m1_decode(code), X + 1);"),
+    ("smoothq_repair_term_dropped",
+     "double pw = dq ? DEC[oc_expcast(fmaf(s, alpha, dq[j]), 1.0f, bias - M)] : DEC[oc_expcast(s, alpha, bias - M)];",
+     "double pw = dq ? DEC[oc_expcast(s, alpha, bias - M)] : DEC[oc_expcast(s, alpha, bias - M)];"),
+    ("mup_unscaled", "    for (int c = 0; c < d; ++c) mup[(size_t)b * d + c] = mu[(size_t)b * d + c] * inv[c];",
+     "    for (int c = 0; c < d; ++c) mup[(size_t)b * d + c] = mu[(size_t)b * d + c];"),
+    ("output_scale_dropped", "  for (int c = 0; c < d; ++c) out[c] = (double)sv[c] * acc[c] / ell;",
+     "  for (int c = 0; c < d; ++c) out[c] = acc[c] / ell;"),
+    ("qblock_scale_of_key", "    float alpha = (sq[a] * sk[b]) * c0;\n    float smax",
+     "    float alpha = (sk[a] * sk[b]) * c0;\n    float smax"),
 ]
 
 

@@ -324,6 +324,23 @@ def test_warm_start_rounds_centroids_to_nearest():
     assert lab.tolist() == [1, 0, 0]
 
 
+def test_warm_start_clamp_decides_the_labels():
+    """R17: scaled warm-start centroids are clamped to [-2^13, 2^13 - 1].
+    Tokens 7936 and 4512 (fixed-point units; max|v| = 1.9375 gives sh = 12).  The
+    warm centroid 2.5 scales to 10240 and is clamped to 8191; the other sits at
+    1000.  Token 7936 joins the first (255 against 6936), token 4512 the second
+    (3512 against 3679).  A clamp at 4095 would pull token 4512 to the first
+    (417 against 3512)."""
+    vb = _one_channel_head([7936, 4512])
+    z = np.zeros_like(vb)
+    cent = np.zeros((1, 2, 128), np.float32)
+    cent[0, 0, 0] = 2.5
+    cent[0, 1, 0] = 1000.0 / 4096.0
+    P = orc.make_params(1, 1, 2, C_=2, T=1, rho=0.0)
+    P.flags |= orc.WARM_START
+    assert orc.prepare(P, z, z, vb, init_centroids=cent)["labels"][0].tolist() == [0, 1]
+
+
 def test_fixed_point_means_round_to_nearest():
     """R8: means are exact sums of values rounded to the 2^-24 grid.  Every K
     (and V) value of channel 0 is +-1.5 * 2^-25, i.e. +-0.75 grid steps, which
@@ -743,17 +760,20 @@ def test_repair_restores_coherent_residuals_with_their_own_block_scales():
     k[256:] /= 8.0
     v = np.full((N, 128), 17.0 / 32.0)
     v[17, :] = 1.0
-    qb, kb, vb = (inputs.to_bf16_bits(x)[None, None] for x in (q, k, v))
     rows = np.arange(0, N, 3).astype(np.int32)
-    rel = {}
-    for rho in (0.0, 1.0):
-        P = orc.make_params(1, 1, N, C_=1, T=1, rho=rho, sm_scale=0.2)
-        P.flags = orc.REPAIR | orc.PERMUTE_Q  # V-Smooth off: the residual codes carry V
-        pr = orc.prepare(P, qb, kb, vb)
-        out = orc.forward_rows(P, pr, np.zeros(len(rows), np.int32), rows)
-        ex = orc.exact_rows(P, qb, kb, vb, np.zeros(len(rows), np.int32), rows)
-        rel[rho] = np.linalg.norm(out - ex) / np.linalg.norm(ex)
-    assert rel[0.0] > 5e-3 and rel[1.0] < 1e-5, rel
+    # plain, and with smoothed queries around a query mean offset of 2 (R20:
+    # repaired keys then carry the per-key score term too)
+    for extra, qoff in ((0, 0.0), (orc.SMOOTH_Q, 2.0)):
+        qb, kb, vb = (inputs.to_bf16_bits(x)[None, None] for x in (q + qoff, k, v))
+        rel = {}
+        for rho in (0.0, 1.0):
+            P = orc.make_params(1, 1, N, C_=1, T=1, rho=rho, sm_scale=0.2)
+            P.flags = orc.REPAIR | orc.PERMUTE_Q | extra  # V-Smooth off: the residual codes carry V
+            pr = orc.prepare(P, qb, kb, vb)
+            out = orc.forward_rows(P, pr, np.zeros(len(rows), np.int32), rows)
+            ex = orc.exact_rows(P, qb, kb, vb, np.zeros(len(rows), np.int32), rows)
+            rel[rho] = np.linalg.norm(out - ex) / np.linalg.norm(ex)
+        assert rel[0.0] > 5e-3 and rel[1.0] < 1e-5, (extra, rel)
 
 
 def test_lazy_maximum_closed_form():

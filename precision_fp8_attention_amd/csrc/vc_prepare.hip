@@ -26,6 +26,13 @@ __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float((h & 
 
 typedef int nt_v4 __attribute__((ext_vector_type(4)));  // 16-byte operand of non-temporal loads
 
+// An empty asm that reads and writes the loaded words.  A load whose value only
+// feeds a select (row in range ? value : 0) is otherwise moved under a per-row
+// branch, and each such branch then waits for its load before the next one is
+// issued; with the value pinned here, a thread issues all of its loads first.
+__device__ __forceinline__ void pin_loaded(uint4& x) { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); }
+__device__ __forceinline__ void pin_loaded(int& x) { asm volatile("" : "+v"(x)); }
+
 // x rounded to the 2^-24 grid, in units of 2^-24, as a double (exact: an
 // integer-valued float).  Sums of up to 2^7 such values stay below 2^53 for
 // inputs |x| < 2^22, so fp64 adds of them are exact and equal integer sums;
@@ -152,16 +159,16 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 __device__ __forceinline__ int v4_group(int r) { return r >> 5; }
 
 // ---------------------------------------------------------------------------
-// K channel sums: fixed-point partial sums over KSUM_CHUNK tokens, added into
-// the head's sums; with WITH_V the same workgroup takes max|V| of the chunk into
-// the head's maximum (the k-means fixed-point scale, needed only when k-means
-// runs).
-// grid (nkc, BH), 256 threads: thread = (row r = t/16, 8-channel group t%16).
-template <bool WITH_V>
-__global__ __launch_bounds__(256) void k_ksum(Args a) {
-  __shared__ long long red[16][D];
-  __shared__ float wm[4];
-  const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
+// One of two sweeps over a chunk of KSUM_CHUNK tokens.  With WITH_K, the K
+// channel sums: fixed-point partial sums over the chunk, added into the head's
+// sums.  With WITH_V, max|V| of the chunk, taken into the head's maximum (the
+// k-means fixed-point scale, needed only when k-means runs).
+// One workgroup of 256 threads per chunk: thread = (row r = t/16, 8-channel
+// group t%16); red is a 16 x 128 LDS buffer, wm four floats of LDS.
+template <bool WITH_K, bool WITH_V>
+__device__ __forceinline__ void ksum_chunk(const Args& a, int ch, int bh, long long (*red)[D], float* wm) {
+  static_assert(WITH_K != WITH_V, "one sweep: the K sums or max|V|");
+  const int t = threadIdx.x;
   const int cg = t & 15, r = t >> 4;
   const int j0 = ch * KSUM_CHUNK, j1 = min(j0 + KSUM_CHUNK, a.N);
   const uint16_t* kh = a.k + (size_t)bh * a.N * D;
@@ -171,36 +178,55 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
   float vm = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = 0.0;
-  // K (and V) rows are streamed once here: non-temporal loads (measured 20 us
-  // less over the cold prepare at 2x24x16544)
-  for (int j = j0 + r; j < j1; j += 16) {
-    const nt_v4 ku = __builtin_nontemporal_load(reinterpret_cast<const nt_v4*>(kh + (size_t)j * D + cg * 8));
-    const uint4 u = make_uint4((uint32_t)ku[0], (uint32_t)ku[1], (uint32_t)ku[2], (uint32_t)ku[3]);
-    s[0] += fx24d(bf2f(u.x));
-    s[1] += fx24d(bf2f(u.x >> 16));
-    s[2] += fx24d(bf2f(u.y));
-    s[3] += fx24d(bf2f(u.y >> 16));
-    s[4] += fx24d(bf2f(u.z));
-    s[5] += fx24d(bf2f(u.z >> 16));
-    s[6] += fx24d(bf2f(u.w));
-    s[7] += fx24d(bf2f(u.w >> 16));
-    if constexpr (WITH_V) {
-      const nt_v4 vw = __builtin_nontemporal_load(reinterpret_cast<const nt_v4*>(vh + (size_t)j * D + cg * 8));
-      const uint4 w = make_uint4((uint32_t)vw[0], (uint32_t)vw[1], (uint32_t)vw[2], (uint32_t)vw[3]);
-      vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
-                           fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
-      vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
-                           fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
+  // The rows are streamed once: non-temporal loads (measured 20 us less over
+  // the cold prepare at 2x24x16544).  A thread takes its rows 8 at a time and
+  // issues the 8 loads before it waits on any: rows at or past the chunk's end
+  // read the chunk's last row and count as zero (which adds nothing to the sums
+  // and the maximum), so no branch stands between the loads.
+  for (int jb = j0 + r; jb < j1; jb += 16 * 8) {
+    uint4 u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(jb + 16 * i, j1 - 1);
+      const nt_v4 x = __builtin_nontemporal_load(
+          reinterpret_cast<const nt_v4*>((WITH_K ? kh : vh) + (size_t)j * D + cg * 8));
+      u[i] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pin_loaded(u[i]);
+      if (jb + 16 * i >= j1) u[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (WITH_K) {
+        s[0] += fx24d(bf2f(u[i].x));
+        s[1] += fx24d(bf2f(u[i].x >> 16));
+        s[2] += fx24d(bf2f(u[i].y));
+        s[3] += fx24d(bf2f(u[i].y >> 16));
+        s[4] += fx24d(bf2f(u[i].z));
+        s[5] += fx24d(bf2f(u[i].z >> 16));
+        s[6] += fx24d(bf2f(u[i].w));
+        s[7] += fx24d(bf2f(u[i].w >> 16));
+      } else {
+        const uint4 w = u[i];
+        vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.x)), fabsf(bf2f(w.x >> 16))),
+                             fmaxf(fabsf(bf2f(w.y)), fabsf(bf2f(w.y >> 16)))));
+        vm = fmaxf(vm, fmaxf(fmaxf(fabsf(bf2f(w.z)), fabsf(bf2f(w.z >> 16))),
+                             fmaxf(fabsf(bf2f(w.w)), fabsf(bf2f(w.w >> 16)))));
+      }
     }
   }
+  if constexpr (WITH_K) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = (long long)s[i];
+    for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = (long long)s[i];
+  }
   if constexpr (WITH_V) {
     vm = wave_max(vm);
     if ((t & 63) == 0) wm[t >> 6] = vm;
   }
   __syncthreads();
-  if (t < D) {
+  if (WITH_K && t < D) {
     long long tot = 0;
     for (int rr = 0; rr < 16; ++rr) tot += red[rr][t];
     a.ksum[((size_t)bh * a.nkc + ch) * D + t] = tot;
@@ -209,6 +235,13 @@ __global__ __launch_bounds__(256) void k_ksum(Args a) {
   }
   // max |V| >= 0, so its fp32 bits order like the values
   if (WITH_V && t == 0) atomicMax(a.vmaxh + bh, __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
+}
+
+// max|V| of every head alone, for the k-means scale; the K sums come later,
+// beside the V block statistics.  grid (nkc, BH), 256 threads.
+__global__ __launch_bounds__(256) void k_vmax(Args a) {
+  __shared__ float wm[4];
+  ksum_chunk<false, true>(a, blockIdx.x, blockIdx.y, nullptr, wm);
 }
 
 // Clears the per-head accumulators that later kernels add into.  grid BH, 128
@@ -242,22 +275,31 @@ __global__ __launch_bounds__(256) void k_vfix(Args a) {
   const int sh = am > 0.0f ? 13 - e : 0;
   if (blockIdx.x == 0 && t == 0) a.kmsh[bh] = sh;
   const int cg = t & 15;
-  for (int r = t >> 4; r < 256; r += 16) {
-    const int j = blockIdx.x * 256 + r;
-    if (j >= a.N) break;
-    const size_t o = ((size_t)bh * a.N + j) * D + cg * 8;
-    const uint4 u = *reinterpret_cast<const uint4*>(a.v + o);
-    const uint32_t h[4] = {u.x, u.y, u.z, u.w};
-    uint32_t ph[2] = {0u, 0u}, pl[2] = {0u, 0u};
+  // the thread's 16 rows in two batches of 8 whose loads are all issued before
+  // any is waited on (rows past N read row N-1 and store nothing)
+  for (int b = 0; b < 2; ++b) {
+    const int jb = blockIdx.x * 256 + (t >> 4) + 128 * b;
+    uint4 u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      u[i] = *reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.N + min(jb + 16 * i, a.N - 1)) * D + cg * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t bits = (i & 1) ? (h[i >> 1] >> 16) : h[i >> 1];
-      const int q = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
-      ph[i >> 2] |= (uint32_t)((q >> 7) & 0xff) << (8 * (i & 3));
-      pl[i >> 2] |= (uint32_t)(q & 127) << (8 * (i & 3));
+      const int j = jb + 16 * i;
+      if (j >= a.N) break;
+      const size_t o = ((size_t)bh * a.N + j) * D + cg * 8;
+      const uint32_t h[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+      uint32_t ph[2] = {0u, 0u}, pl[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (h[e >> 1] >> 16) : h[e >> 1];
+        const int q = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
+        ph[e >> 2] |= (uint32_t)((q >> 7) & 0xff) << (8 * (e & 3));
+        pl[e >> 2] |= (uint32_t)(q & 127) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(a.uhi + o) = make_uint2(ph[0], ph[1]);
+      *reinterpret_cast<uint2*>(a.ulo + o) = make_uint2(pl[0], pl[1]);
     }
-    *reinterpret_cast<uint2*>(a.uhi + o) = make_uint2(ph[0], ph[1]);
-    *reinterpret_cast<uint2*>(a.ulo + o) = make_uint2(pl[0], pl[1]);
   }
 }
 
@@ -745,17 +787,29 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 7) void k_qk_quant(Args a) {
   // Rows are read once and codes written once: non-temporal accesses keep them
   // from displacing other lines in L2 (measured 24 us less at 2x24x16544; the
   // 16 lanes of a row make each access two whole 128-byte lines).
+  // All 8 positions, then all 8 rows, are loaded before any is waited on: rows
+  // past N read the last position's row and are cleared after, so no branch
+  // stands between the loads (a load under a per-row branch waits for the one
+  // before it).
+  int j[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) j[i] = min(blk * BLK + r0 + 16 * i, a.N - 1);
+  if (follow) {  // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < 8; ++i) j[i] = a.perm[(size_t)bh * a.N + j[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pin_loaded(j[i]);
   uint4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 16 * i;
-    raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nrow) {
-      const int p = blk * BLK + r;
-      const int j = follow ? a.perm[(size_t)bh * a.N + p] : p;
-      const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (size_t)j * D + cg * 8));
-      raw[i] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
-    }
+    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (size_t)j[i] * D + cg * 8));
+    raw[i] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pin_loaded(raw[i]);
+    if (r0 + 16 * i >= nrow) raw[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   // K channel mean from the head's fixed-point sums (while the rows load); the
   // first block's workgroup also stores it
@@ -942,28 +996,35 @@ __global__ __launch_bounds__(256) void k_qbias(Args a) {
 // ---------------------------------------------------------------------------
 // V block means and block maxima of |V - mu|; with VC_V4 also the maximum of each
 // 32-key group (rows 32G .. 32G+31) and its E8M0 exponent.
-// grid (nblk, BH), 256 threads: thread = (8-channel chunk t%16, rows t/16 + 16i),
-// so rows 2G and 2G+1 of a thread lie in group G.
-__global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
-  // the block sums and, after them, the block maxima share one 16 KB buffer, so
-  // six workgroups fit a CU
-  __shared__ __align__(16) long long sbuf[16 * D];
+// One workgroup of 256 threads per block: thread = (8-channel chunk t%16, rows
+// t/16 + 16i), so rows 2G and 2G+1 of a thread lie in group G.  The block sums
+// and, after them, the block maxima share the 16 KB LDS buffer sbuf; smu holds
+// 128 floats of LDS.
+__device__ __forceinline__ void v_stats_block(const Args& a, int blk, int bh, long long* sbuf, float* smu) {
   long long (*ssum)[D] = reinterpret_cast<long long (*)[D]>(sbuf);
   float (*smax)[8][D] = reinterpret_cast<float (*)[8][D]>(sbuf);
-  __shared__ float smu[D];
-  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
   const bool vs = (a.flags & VC_VSMOOTH) != 0;
   const uint16_t* vh = a.v + (size_t)bh * a.N * D;
   const int* perm = a.perm + (size_t)bh * a.N;
-  // the thread's 8 rows as raw bf16 (32 registers); rows past N hold 0
+  // the thread's 8 rows as raw bf16 (32 registers); rows past N hold 0.  All
+  // 8 positions, then all 8 rows, are loaded before any is waited on: rows past
+  // N read the last position's row and are cleared after, so no branch stands
+  // between the loads.
+  int src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) src[i] = perm[min(p0 + r0 + 16 * i, a.N - 1)];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pin_loaded(src[i]);
   uint4 raw[8];
 #pragma unroll
+  for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(vh + (size_t)src[i] * D + cg * 8);
+#pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 16 * i;
-    raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (r < n) raw[i] = *reinterpret_cast<const uint4*>(vh + (size_t)perm[p0 + r] * D + cg * 8);
+    pin_loaded(raw[i]);
+    if (r0 + 16 * i >= n) raw[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   auto val = [&](int i, int e) {
     const uint32_t w = e < 2 ? raw[i].x : e < 4 ? raw[i].y : e < 6 ? raw[i].z : raw[i].w;
@@ -1030,6 +1091,24 @@ __global__ __launch_bounds__(256, 6) void k_v_stats(Args a) {
       for (int G = 0; G < 4; ++G) rec[(16 * G + (t & 15)) * 8 + (t >> 4)] = (uint8_t)(mx_exponent(gm[G]) + 127);
     }
   }
+}
+
+// The K channel sums and the V block statistics in one launch: they read
+// different tensors and write different outputs, and the V statistics alone
+// leave much of the memory bandwidth unused (a workgroup waits on its gathers,
+// then reduces), so the K stream runs in those gaps.  grid (nkc + nblk, BH), 256
+// threads: workgroups x < nkc sum K chunk x, the others take V block x - nkc;
+// every head's K chunks come just before its V blocks, so the two kinds stay
+// mixed over the whole launch.  Both roles share one 16.5 KB LDS buffer, so six
+// workgroups fit a CU.
+__global__ __launch_bounds__(256, 6) void k_ksum_v_stats(Args a) {
+  __shared__ __align__(16) long long sbuf[16 * D];
+  __shared__ float smu[D];
+  const int x = blockIdx.x, bh = blockIdx.y;
+  if (x < a.nkc)  // uniform over the workgroup
+    ksum_chunk<true, false>(a, x, bh, reinterpret_cast<long long (*)[D]>(sbuf), smu);
+  else
+    v_stats_block(a, x - a.nkc, bh, sbuf, smu);
 }
 
 // Channel c's residual scale, set by the head's largest |V - mu| (one per
@@ -1107,7 +1186,7 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
 }
 
 // 4-bit residual codes (VC_V4) and the repair criterion.  The group exponents
-// come from k_v_stats.  Thread t owns the key pair 2t, 2t+1 of a block, whose
+// come from k_ksum_v_stats.  Thread t owns the key pair 2t, 2t+1 of a block, whose
 // two codes share one byte of every channel row of the block's tile.  Per
 // channel, gfx950's v_cvt_scalef32_pk_fp4_f32 rounds the pair's two residuals
 // by their group's power of two into that byte (nearest, ties to the even code,
@@ -1421,11 +1500,8 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
     a.nkm = km_chunks(a, cus);
   }
   hipLaunchKernelGGL(k_prep_zero, dim3(BH), dim3(128), 0, st, a);
-  if (kmeans)
-    hipLaunchKernelGGL(k_ksum<true>, dim3(a.nkc, BH), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_ksum<false>, dim3(a.nkc, BH), dim3(256), 0, st, a);
   if (kmeans) {
+    hipLaunchKernelGGL(k_vmax, dim3(a.nkc, BH), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
     if (mode == ClusterMode::Warm)
       hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
@@ -1449,13 +1525,14 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   } else if (!vs) {
     hipLaunchKernelGGL(k_perm_identity, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
   }
+  // the K channel sums (needed by the K codes) with the V block statistics
+  hipLaunchKernelGGL(k_ksum_v_stats, dim3(a.nkc + a.nblk, BH), dim3(256), 0, st, a);
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qk_quant<true>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_qk_quant<false>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 31) / 32, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_v_stats, dim3(a.nblk, BH), dim3(256), 0, st, a);
   if (a.flags & VC_V4)
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else

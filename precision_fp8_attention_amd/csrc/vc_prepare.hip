@@ -715,12 +715,26 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
     }
     return peers;
   };
-  for (int jb = j0; jb < j1; jb += 64) {
-    const int j = jb + lane;
-    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
-    const unsigned long long peers = peers_of(l);
-    // the lowest lane of each label adds the label's count (distinct words)
-    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+  // the labels of the wave's positions jb + lane, jb + 64 + lane, ..., 8 at a
+  // time: all 8 loads are issued before the first wait (positions at or past N
+  // read position N - 1; the callers skip them)
+  auto load8 = [&](int jb, int (&l)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l[u] = lab[min(jb + 64 * u + lane, a.N - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pin_loaded(l[u]);
+  };
+  for (int jb = j0; jb < j1; jb += 64 * 8) {
+    int lb[8];
+    load8(jb, lb);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jb + 64 * u + lane;
+      const int l = j < j1 ? lb[u] : MAX_CLUSTERS;
+      const unsigned long long peers = peers_of(l);
+      // the lowest lane of each label adds the label's count (distinct words)
+      if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+    }
   }
   __syncthreads();
   // first position of (wave, cluster): all tokens of smaller clusters, plus those
@@ -736,19 +750,24 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
     }
   }
   __syncthreads();
-  for (int jb = j0; jb < j1; jb += 64) {
-    const int j = jb + lane;
-    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
-    const unsigned long long peers = peers_of(l);
-    if (l < MAX_CLUSTERS) {
-      const int pos = wcnt[w][l] + __popcll(peers & lt);
-      perm[pos] = j;
-      iperm[j] = pos;
+  for (int jb = j0; jb < j1; jb += 64 * 8) {
+    int lb[8];
+    load8(jb, lb);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jb + 64 * u + lane;
+      const int l = j < j1 ? lb[u] : MAX_CLUSTERS;
+      const unsigned long long peers = peers_of(l);
+      if (l < MAX_CLUSTERS) {
+        const int pos = wcnt[w][l] + __popcll(peers & lt);
+        perm[pos] = j;
+        iperm[j] = pos;
+      }
+      // every lane has read its offset before the lowest lane of each label moves it
+      __builtin_amdgcn_wave_barrier();
+      if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
     }
-    // every lane has read its offset before the lowest lane of each label moves it
-    __builtin_amdgcn_wave_barrier();
-    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1205,9 +1224,16 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
     v_channel(a, bh, blk, t + 64, &smu[t + 64], &sc, &iv);
   }
   {
-    // the record is [group][channel % 16][channel / 16]: transpose to channel order
+    // the record is [group][channel % 16][channel / 16]: transpose to channel
+    // order; thread t loads bytes 8t .. 8t+7 at once
+    static_assert(V4_SREC == 8 * 64, "one 8-byte load per thread covers the record");
     const uint8_t* rec = a.v4s + ((size_t)bh * a.nblk + blk) * V4_SREC;
-    for (int q = t; q < V4_SREC; q += 64) sx[q >> 7][16 * (q & 7) + ((q >> 3) & 15)] = rec[q];
+    const uint2 rb = *reinterpret_cast<const uint2*>(rec + 8 * t);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = 8 * t + k;
+      sx[q >> 7][16 * (q & 7) + ((q >> 3) & 15)] = (uint8_t)(((k < 4 ? rb.x : rb.y) >> (8 * (k & 3))) & 0xffu);
+    }
   }
   const int p0 = blk * BLK, n = min(BLK, a.N - p0);
   const int k0 = 2 * t;
@@ -1319,8 +1345,15 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   if (a.m == 0) return;  // no repair set (uniform)
   const int cp = lane & (RS_COPIES - 1);
   const float* err = a.err + (size_t)bh * a.N;
-  auto key_of = [&](int j) {
-    return ((unsigned long long)(~__float_as_uint(err[j])) << 32) | (unsigned)j;
+  auto key_of = [&](int j, int e) { return ((unsigned long long)(~(unsigned)e) << 32) | (unsigned)j; };
+  // the error bits of positions j0, j0 + step, ..., 8 at a time: all 8 loads
+  // are issued before the first wait (positions at or past N read position
+  // N - 1; the callers skip them)
+  auto load8 = [&](int j0, int step, int (&e)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) e[u] = __float_as_int(err[min(j0 + step * u, a.N - 1)]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pin_loaded(e[u]);
   };
   if (t == 0) {
     s_prefix = 0ull;
@@ -1331,9 +1364,15 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
     for (int e = t; e < 256 * RS_COPIES; e += 1024) (&hist[0][0])[e] = 0;
     __syncthreads();
     const unsigned long long pre = s_prefix, msk = s_mask;
-    for (int j = t; j < a.N; j += 1024) {
-      const unsigned long long key = key_of(j);
-      if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255][cp], 1);
+    for (int jb = t; jb < a.N; jb += 1024 * 8) {
+      int e[8];
+      load8(jb, 1024, e);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = jb + 1024 * u;
+        const unsigned long long key = key_of(j, e[u]);
+        if (j < a.N && (key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255][cp], 1);
+      }
     }
     __syncthreads();
     // bin totals (threads 0..255; copy i of bin t read at (i + t) mod RS_COPIES,
@@ -1383,21 +1422,31 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
   const int j0 = min(w * per, a.N), j1 = min(j0 + per, a.N);
   const unsigned long long lt = (1ull << lane) - 1ull;
   int cnt = 0;
-  for (int jb = j0; jb < j1; jb += 64) {
-    const int j = jb + lane;
-    cnt += __popcll(__ballot(j < j1 && key_of(j) <= thr));
+  for (int jb = j0; jb < j1; jb += 64 * 8) {
+    int e[8];
+    load8(jb + lane, 64, e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jb + 64 * u + lane;
+      cnt += __popcll(__ballot(j < j1 && key_of(j, e[u]) <= thr));
+    }
   }
   if (lane == 0) wtot[w] = cnt;
   __syncthreads();
   int slot = 0;
   for (int ww = 0; ww < w; ++ww) slot += wtot[ww];
-  for (int jb = j0; jb < j1; jb += 64) {
-    const int j = jb + lane;
-    const bool sel = j < j1 && key_of(j) <= thr;
-    const unsigned long long b = __ballot(sel);
-    const int s = slot + __popcll(b & lt);
-    if (sel && s < a.mpad) out[s] = j;  // exactly m keys are <= thr
-    slot += __popcll(b);
+  for (int jb = j0; jb < j1; jb += 64 * 8) {
+    int e[8];
+    load8(jb + lane, 64, e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jb + 64 * u + lane;
+      const bool sel = j < j1 && key_of(j, e[u]) <= thr;
+      const unsigned long long b = __ballot(sel);
+      const int s = slot + __popcll(b & lt);
+      if (sel && s < a.mpad) out[s] = j;  // exactly m keys are <= thr
+      slot += __popcll(b);
+    }
   }
   for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
 }
@@ -1416,8 +1465,15 @@ __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
     const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
     const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
     const uint8_t* xr = a.v4s + ((size_t)bh * a.nblk + p / BLK) * V4_SREC + 16 * v4_group(p % BLK) * 8;
+    // the whole row is loaded before the first wait
+    uint4 rw[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) rw[i] = *reinterpret_cast<const uint4*>(row + i * 8);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) pin_loaded(rw[i]);
+#pragma unroll
     for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      const uint4 u = rw[i];
       const uint32_t h[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1433,8 +1489,15 @@ __global__ __launch_bounds__(128) void k_rep_delta(Args a) {
     const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
     const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
     const float* inv = a.inv + (size_t)bh * D;
+    // the whole row is loaded before the first wait
+    uint4 rw[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) rw[i] = *reinterpret_cast<const uint4*>(row + i * 8);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) pin_loaded(rw[i]);
+#pragma unroll
     for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + i * 8);
+      const uint4 u = rw[i];
       const uint32_t h[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

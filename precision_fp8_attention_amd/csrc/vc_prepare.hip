@@ -517,30 +517,14 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   unsigned long long* mybins = bins + (ncopy == 2 ? (l16 & 1) * C * BROW2 : 0);  // this lane's copy
   int* mq = cnt + 2 * C + w * 2 * KM_QUEUE;  // this wave's ring: token indices
   int* ml = mq + KM_QUEUE;                  // old << 8 | new label
-  const int* cf = a.centfix + (size_t)bh * C * D;
-  for (int e = t; e < C * D; e += 64 * KM_WAVES) {
-    const int u = cf[e];
-    chi[(e / D) * CROW + (e % D)] = (int8_t)(u >> 7);
-    clo[(e / D) * CROW + (e % D)] = (int8_t)(u & 127);
-  }
-  for (int e = t; e < ncopy * C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
-  if (t < 2 * C) cnt[t] = 0;
-  // Distances as exact fp64 keys.  For centroid k, D = ||c||^2 - 2 u.c with
-  // |D| < 2^35, and key = 64 (D + 2^35) + k is an integer below 2^42, exact in
-  // fp64 at every step (fp64 fma runs at the fp32 rate here, 64-bit integer
-  // arithmetic takes several instructions per operation).  The smallest key
-  // gives the smallest D and, among equal D, the lowest id; k is its low 6 bits.
-  // This lane's base keys 64 (||c||^2 + 2^35) + k for centroids 16kt + 4g + v;
-  // centroids beyond C get 2^50, above every real key.
-  double kbase[NT][4];
+  // Every workgroup of the launch runs at once and waits for its set-up loads
+  // before its first token, so the loads of the set-up (centroids, their norms
+  // and the first subtile's operands) are all issued before the first wait.
+  long long cc[NT][4];  // squared centroid norms (centroid C-1 stands in past C)
 #pragma unroll
   for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int k = 16 * kt + 4 * g + v;
-      kbase[kt][v] = k < C ? ((double)a.kmcc[(size_t)bh * C + k] + 0x1p35) * 64.0 + (double)k : 0x1p50;
-    }
-  __syncthreads();
+    for (int v = 0; v < 4; ++v) cc[kt][v] = a.kmcc[(size_t)bh * C + min(16 * kt + 4 * g + v, C - 1)];
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
   // wave w takes 16-token subtiles w, w+KM_WAVES, ... of the chunk; the operands
@@ -586,6 +570,51 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
   };
   Sub nx;
   if (has(w)) load_sub(w, nx);
+  // the centroids, 4 channels per thread and step
+  const int* cf = a.centfix + (size_t)bh * C * D;
+  {
+    constexpr int STEP = 64 * KM_WAVES, MAXS = MAX_CLUSTERS * D / 4 / STEP;
+    const int n4 = C * D / 4;
+    uint4 cv[MAXS];
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) cv[i] = reinterpret_cast<const uint4*>(cf)[min(t + STEP * i, n4 - 1)];
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) pin_loaded(cv[i]);
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int e = 4 * (t + STEP * i);  // channels e .. e+3 of one centroid
+      if (e < C * D) {
+        const int u[4] = {(int)cv[i].x, (int)cv[i].y, (int)cv[i].z, (int)cv[i].w};
+        uint32_t h = 0u, l = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h |= (uint32_t)((u[k] >> 7) & 0xff) << (8 * k);
+          l |= (uint32_t)(u[k] & 127) << (8 * k);
+        }
+        *reinterpret_cast<uint32_t*>(chi + (e / D) * CROW + (e % D)) = h;
+        *reinterpret_cast<uint32_t*>(clo + (e / D) * CROW + (e % D)) = l;
+      }
+    }
+  }
+  for (int e = t; e < ncopy * C * BROW2; e += 64 * KM_WAVES) bins[e] = 0ull;
+  if (t < 2 * C) cnt[t] = 0;
+  // Distances as exact fp64 keys.  For centroid k, D = ||c||^2 - 2 u.c with
+  // |D| < 2^35, and key = 64 (D + 2^35) + k is an integer below 2^42, exact in
+  // fp64 at every step (fp64 fma runs at the fp32 rate here, 64-bit integer
+  // arithmetic takes several instructions per operation).  The smallest key
+  // gives the smallest D and, among equal D, the lowest id; k is its low 6 bits.
+  // This lane's base keys 64 (||c||^2 + 2^35) + k for centroids 16kt + 4g + v;
+  // centroids beyond C get 2^50, above every real key.
+  double kbase[NT][4];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      asm volatile("" : "+v"(cc[kt][v]));
+      const int k = 16 * kt + 4 * g + v;
+      kbase[kt][v] = k < C ? ((double)cc[kt][v] + 0x1p35) * 64.0 + (double)k : 0x1p50;
+    }
+  __syncthreads();
 #pragma unroll 1
   for (int sub = w; sub < KM_CHUNK / 16; sub += KM_WAVES) {
     if (!has(sub)) break;

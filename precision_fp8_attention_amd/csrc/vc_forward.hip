@@ -642,44 +642,84 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
   for (int grp = 0; grp < a.mpad / BLK; ++grp) {
     uint8_t* Ks = ksm[0];
     const int* rp = a.rep_pos + (size_t)bh * a.mpad + (size_t)grp * BLK;
-    if constexpr (EXACT) {
+    // The K rows of the group's tokens and their score terms.  The positions
+    // are loaded together, then the rows and block scales together: two waits.
+    // A K row is 16 chunks of 16 bytes (bf16, exact scores) or 8 (E4M3).
+    constexpr int RSH = EXACT ? 4 : 3, NIT = BLK * (EXACT ? 256 : 128) / 16 / (64 * NWV);
+    int gpos[NIT];
 #pragma unroll
-      for (int i = 0; i < 2048 / (64 * NWV); ++i) {
-        const int ch = tid + 64 * NWV * i, row = ch >> 4, cc = ch & 15;
-        const int pos = krow_of<V4>(rp[row]);
-        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)pos * 256 + cc * 16);
-        *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv;
-      }
-    } else {
+    for (int i = 0; i < NIT; ++i) gpos[i] = rp[(tid + 64 * NWV * i) >> RSH];
+    int tpos = rp[tid & (BLK - 1)];  // threads tid < BLK use it
 #pragma unroll
-      for (int i = 0; i < 1024 / (64 * NWV); ++i) {
-        const int ch = tid + 64 * NWV * i, row = ch >> 3, cc = ch & 7;
-        const int pos = krow_of<V4>(rp[row]);
-        const uint4 kv = *reinterpret_cast<const uint4*>(kg + (size_t)pos * D + cc * 16);
-        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv;
-      }
+    for (int i = 0; i < NIT; ++i) pin_loaded(gpos[i]);
+    pin_loaded(tpos);
+    uint4 kv[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int cc = (tid + 64 * NWV * i) & ((1 << RSH) - 1);
+      kv[i] = *reinterpret_cast<const uint4*>(kg + (size_t)krow_of<V4>(gpos[i]) * (16 << RSH) + cc * 16);
+    }
+    const int qb1 = min(qb0 + 1, a.nblk - 1);
+    const size_t tcol = (size_t)(tpos < 0 ? 0 : tpos);
+    int skb = __float_as_int(sk[tcol / BLK]);
+    int db0 = 0, db1 = 0;
+    if constexpr (SQ) {
+      db0 = __float_as_int(a.qbias[((size_t)bh * a.nblk + qb0) * a.Npad + tcol]);
+      db1 = __float_as_int(a.qbias[((size_t)bh * a.nblk + qb1) * a.Npad + tcol]);
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) pin_loaded(kv[i]);
+    pin_loaded(skb);
+    if constexpr (SQ) {
+      pin_loaded(db0);
+      pin_loaded(db1);
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int ch = tid + 64 * NWV * i, row = ch >> RSH, cc = ch & ((1 << RSH) - 1);
+      if constexpr (EXACT)
+        *reinterpret_cast<uint4*>(Ks + row * 256 + ((cc ^ (row & 15)) << 4)) = kv[i];
+      else
+        *reinterpret_cast<uint4*>(Ks + row * 128 + ((cc ^ row_swz(row)) << 4)) = kv[i];
     }
     if (tid < BLK) {
-      const int pos = rp[tid];
-      const float sk_pos = sk[pos < 0 ? 0 : pos / BLK];
+      const float sk_pos = __int_as_float(skb);
       alpha_s[0][tid] = (a.sq[(size_t)bh * a.nblk + qb0] * sk_pos) * a.c0;
-      const int qb1 = min(qb0 + 1, a.nblk - 1);
       alpha_s[1][tid] = (a.sq[(size_t)bh * a.nblk + qb1] * sk_pos) * a.c0;
       if constexpr (SQ) {
-        const size_t col = (size_t)(pos < 0 ? 0 : pos);
-        dsel_s[0][tid] = a.qbias[((size_t)bh * a.nblk + qb0) * a.Npad + col];
-        dsel_s[1][tid] = a.qbias[((size_t)bh * a.nblk + qb1) * a.Npad + col];
+        dsel_s[0][tid] = __int_as_float(db0);
+        dsel_s[1][tid] = __int_as_float(db1);
       }
     }
     __syncthreads();
     const float* al = alpha_s[wg];
     const float* dsl = dsel_s[SQ ? wg : 0];
     const uint16_t* dt = a.rep_dt + (size_t)bh * D * a.mpad + (size_t)grp * BLK;
+    // the A operands of chunk u (eight channel tiles), shared by the subtiles and
+    // loaded together; with FP8 scores the next chunk's are loaded while this one
+    // is used (the exact-score kernel has no registers to spare for them)
+    auto load_dt = [&](int u, uint4 (&av)[8]) {
 #pragma unroll
-    for (int qs = 0; qs < NS; ++qs) {
-      const float beta = a.bias - rs[qs].M;
+      for (int ct = 0; ct < 8; ++ct)
+        av[ct] = *reinterpret_cast<const uint4*>(dt + (size_t)(16 * ct + l16) * a.mpad + 32 * u + 8 * g);
+    };
+    uint4 avn[8];
+    if constexpr (!EXACT) load_dt(0, avn);
 #pragma unroll 1
-      for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      uint4 av[8];
+      if constexpr (EXACT) {
+        load_dt(u, av);
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) av[ct] = avn[ct];
+      }
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) pin_loaded(av[ct]);
+      if (!EXACT && u < 3) load_dt(u + 1, avn);
+#pragma unroll
+      for (int qs = 0; qs < NS; ++qs) {
+        const float beta = a.bias - rs[qs].M;
         // key tiles 2u and 2u+1 feed the 32-key chunk u of the bf16 MFMA: lane
         // group g holds slots 16(2u+t')+4g+v at K positions 8g+4t'+v
         v8bf bop;
@@ -701,28 +741,39 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
           }
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const uint4 av = *reinterpret_cast<const uint4*>(dt + (size_t)(16 * ct + l16) * a.mpad + 32 * u + 8 * g);
-          rs[qs].acc[ct] = mfma_bf16_k32(__builtin_bit_cast(v8bf, av), bop, rs[qs].acc[ct]);
-        }
+        for (int ct = 0; ct < 8; ++ct) rs[qs].acc[ct] = mfma_bf16_k32(__builtin_bit_cast(v8bf, av[ct]), bop, rs[qs].acc[ct]);
       }
     }
     __syncthreads();
   }
 
-  // Epilogue: O = sV * acc / l, bf16, scattered back to the original row.
+  // Epilogue: O = sV * acc / l, bf16, scattered back to the original row.  The
+  // channel scales are loaded together first: a load after a store would also
+  // wait for the store.
   const float* sv = a.sv + (size_t)bh * D;
+  uint4 svw[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) svw[ct] = *reinterpret_cast<const uint4*>(sv + 16 * ct + 4 * g);
+  int orig[NS];  // each subtile row's original position (rows past N: any valid one)
+#pragma unroll
+  for (int qs = 0; qs < NS; ++qs) {
+    const int p = min(qb * BLK + wq * 16 * NS + qs * 16 + l16, a.N - 1);
+    orig[qs] = (a.flags & VC_PERMUTE_Q) ? a.perm[(size_t)bh * a.N + p] : p;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) pin_loaded(svw[ct]);
+#pragma unroll
+  for (int qs = 0; qs < NS; ++qs) pin_loaded(orig[qs]);
 #pragma unroll
   for (int qs = 0; qs < NS; ++qs) {
     const int p = qb * BLK + wq * 16 * NS + qs * 16 + l16;
     if (active && p < a.N) {
-      const int orig = (a.flags & VC_PERMUTE_Q) ? a.perm[(size_t)bh * a.N + p] : p;
       const float il = 1.0f / rs[qs].ell;
-      uint16_t* orow = a.o + ((size_t)bh * a.N + orig) * D;
+      uint16_t* orow = a.o + ((size_t)bh * a.N + orig[qs]) * D;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
         const int c = 16 * ct + 4 * g;
-        const float4 s4 = *reinterpret_cast<const float4*>(sv + c);
+        const float4 s4 = __builtin_bit_cast(float4, svw[ct]);
         uint2 pk;
         pk.x = (uint32_t)f2bf_rne(s4.x * rs[qs].acc[ct][0] * il) |
                ((uint32_t)f2bf_rne(s4.y * rs[qs].acc[ct][1] * il) << 16);

@@ -24,6 +24,15 @@ constexpr int V4_SREC = 512;        // bytes of one block's E8M0 exponents
 // at the K index of that position, so the FP4 operand's 32-wide scale groups
 // are 32 consecutive positions and its codes are stored in position order.
 __host__ __device__ constexpr int v4_krow(int r) { return (r & 0x43) | ((r >> 2) & 0x0c) | ((r << 2) & 0x30); }
+
+// An empty asm that reads and writes loaded words, so that the load that made
+// them is complete here and cannot be moved past this point.  The compiler
+// otherwise moves a load whose value only feeds a select (row in range ? value
+// : 0) under a per-row branch, and each such branch then waits for its load
+// before the next one is issued; it may also delay a prefetch until just before
+// its use.  With the values pinned, a thread issues all of a batch's loads first.
+__device__ __forceinline__ void pin_loaded(uint4& x) { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); }
+__device__ __forceinline__ void pin_loaded(int& x) { asm volatile("" : "+v"(x)); }
 constexpr uint32_t MAGIC = 0x56434154u;  // "VCAT"
 
 // Shape derived from the public parameters.

@@ -26,12 +26,6 @@ __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float((h & 
 
 typedef int nt_v4 __attribute__((ext_vector_type(4)));  // 16-byte operand of non-temporal loads
 
-// An empty asm that reads and writes the loaded words.  A load whose value only
-// feeds a select (row in range ? value : 0) is otherwise moved under a per-row
-// branch, and each such branch then waits for its load before the next one is
-// issued; with the value pinned here, a thread issues all of its loads first.
-__device__ __forceinline__ void pin_loaded(uint4& x) { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); }
-__device__ __forceinline__ void pin_loaded(int& x) { asm volatile("" : "+v"(x)); }
 
 // x rounded to the 2^-24 grid, in units of 2^-24, as a double (exact: an
 // integer-valued float).  Sums of up to 2^7 such values stay below 2^53 for

@@ -272,33 +272,48 @@ __device__ __forceinline__ v8i softmax_codes(v4f (&S)[8], RowState& st, float al
 }
 
 // Adds sum_b L[b] * mu'[b] of a finished 16-block group (bf16 hi/lo split, three
-// products) and moves the group's row sums into ell.
-__device__ __forceinline__ void restore_group(RowState& st, const uint16_t* mupt_grp, int l16, int g) {
-  const v4f W = st.L;
-  float s4 = (W[0] + W[1]) + (W[2] + W[3]);
-  s4 = xsum32(xsum16(s4));
-  st.ell += s4;
-  v4s bh, bl;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const uint16_t h = f2bf_rne(W[v]);
-    bh[v] = (short)h;
-    bl[v] = (short)f2bf_rne(W[v] - __uint_as_float((uint32_t)h << 16));
-  }
+// products) to every subtile's accumulator and moves the group's row sums into
+// ell.  The group's 16 mean operands are the same for all subtiles: they are
+// loaded once, together, so the restore waits for one round trip.
+template <int NS>
+__device__ __forceinline__ void restore_group(RowState (&rs)[NS], const uint16_t* mupt_grp, int l16, int g) {
   const uint16_t* hip = mupt_grp;
   const uint16_t* lop = mupt_grp + D * 16;
+  uint2 ah[8], al[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
     const int c = 16 * ct + l16;
-    const v4s ah = *reinterpret_cast<const v4s*>(hip + c * 16 + 4 * g);
-    const v4s al = *reinterpret_cast<const v4s*>(lop + c * 16 + 4 * g);
-    v4f x = st.acc[ct];
-    x = mfma_bf16_k16(ah, bh, x);
-    x = mfma_bf16_k16(ah, bl, x);
-    x = mfma_bf16_k16(al, bh, x);
-    st.acc[ct] = x;
+    ah[ct] = *reinterpret_cast<const uint2*>(hip + c * 16 + 4 * g);
+    al[ct] = *reinterpret_cast<const uint2*>(lop + c * 16 + 4 * g);
   }
-  st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int qs = 0; qs < NS; ++qs) {
+    RowState& st = rs[qs];
+    const v4f W = st.L;
+    float s4 = (W[0] + W[1]) + (W[2] + W[3]);
+    s4 = xsum32(xsum16(s4));
+    st.ell += s4;
+    v4s bh, bl;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint16_t h = f2bf_rne(W[v]);
+      bh[v] = (short)h;
+      bl[v] = (short)f2bf_rne(W[v] - __uint_as_float((uint32_t)h << 16));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      if (qs == 0) {
+        asm volatile("" : "+v"(ah[ct].x), "+v"(ah[ct].y));
+        asm volatile("" : "+v"(al[ct].x), "+v"(al[ct].y));
+      }
+      v4f x = st.acc[ct];
+      x = mfma_bf16_k16(__builtin_bit_cast(v4s, ah[ct]), bh, x);
+      x = mfma_bf16_k16(__builtin_bit_cast(v4s, ah[ct]), bl, x);
+      x = mfma_bf16_k16(__builtin_bit_cast(v4s, al[ct]), bh, x);
+      st.acc[ct] = x;
+    }
+    st.L = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 }
 
 // Query operands of one wave: bf16 codes (exact scores) or E4M3 bytes.
@@ -578,8 +593,7 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
     }
     if (onesrow == 15 || kb + 1 == a.nblk) {
       const uint16_t* grp = mupt + (size_t)(kb >> 4) * 2 * D * 16;
-#pragma unroll
-      for (int qs = 0; qs < NS; ++qs) restore_group(rs[qs], grp, l16, g);
+      restore_group<NS>(rs, grp, l16, g);
     }
   };
 

@@ -738,26 +738,14 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
     }
     return peers;
   };
-  // the labels of the wave's positions jb + lane, jb + 64 + lane, ..., 8 at a
-  // time: all 8 loads are issued before the first wait (positions at or past N
-  // read position N - 1; the callers skip them)
-  auto load8 = [&](int jb, int (&l)[8]) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) l[u] = lab[min(jb + 64 * u + lane, a.N - 1)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) pin_loaded(l[u]);
-  };
-  for (int jb = j0; jb < j1; jb += 64 * 8) {
-    int lb[8];
-    load8(jb, lb);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = jb + 64 * u + lane;
-      const int l = j < j1 ? lb[u] : MAX_CLUSTERS;
-      const unsigned long long peers = peers_of(l);
-      // the lowest lane of each label adds the label's count (distinct words)
-      if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
-    }
+  // (loading 8 steps' labels before the first wait measured 4 us slower here:
+  // the unrolled ballots outweigh the latency they hide)
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = peers_of(l);
+    // the lowest lane of each label adds the label's count (distinct words)
+    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
   }
   __syncthreads();
   // first position of (wave, cluster): all tokens of smaller clusters, plus those
@@ -773,24 +761,19 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
     }
   }
   __syncthreads();
-  for (int jb = j0; jb < j1; jb += 64 * 8) {
-    int lb[8];
-    load8(jb, lb);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = jb + 64 * u + lane;
-      const int l = j < j1 ? lb[u] : MAX_CLUSTERS;
-      const unsigned long long peers = peers_of(l);
-      if (l < MAX_CLUSTERS) {
-        const int pos = wcnt[w][l] + __popcll(peers & lt);
-        perm[pos] = j;
-        iperm[j] = pos;
-      }
-      // every lane has read its offset before the lowest lane of each label moves it
-      __builtin_amdgcn_wave_barrier();
-      if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int j = jb + lane;
+    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = peers_of(l);
+    if (l < MAX_CLUSTERS) {
+      const int pos = wcnt[w][l] + __popcll(peers & lt);
+      perm[pos] = j;
+      iperm[j] = pos;
     }
+    // every lane has read its offset before the lowest lane of each label moves it
+    __builtin_amdgcn_wave_barrier();
+    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 

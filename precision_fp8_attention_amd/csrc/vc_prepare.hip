@@ -258,42 +258,43 @@ __global__ __launch_bounds__(128) void k_prep_zero(Args a) {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Fixed-point exponent of the head and the int8 planes of u (token order).
-// grid (ceil(N/256), BH), 256 threads: 16 threads per token row (8 channels
-// each, 16-byte loads), 16 rows per step.
-__global__ __launch_bounds__(256) void k_vfix(Args a) {
-  const int bh = blockIdx.y, t = threadIdx.x;
+// Fixed-point exponent of head bh: the largest power of two 2^sh that keeps
+// max|V| * 2^sh below 2^13 (0 for an all-zero head).
+__device__ __forceinline__ int head_shift(const Args& a, int bh) {
   const float am = __uint_as_float(a.vmaxh[bh]);
   int e = 0;
   if (am > 0.0f) frexpf(am, &e);
-  const int sh = am > 0.0f ? 13 - e : 0;
-  if (blockIdx.x == 0 && t == 0) a.kmsh[bh] = sh;
-  const int cg = t & 15;
-  // the thread's 16 rows in two batches of 8 whose loads are all issued before
-  // any is waited on (rows past N read row N-1 and store nothing)
-  for (int b = 0; b < 2; ++b) {
-    const int jb = blockIdx.x * 256 + (t >> 4) + 128 * b;
-    uint4 u[8];
+  return am > 0.0f ? 13 - e : 0;
+}
+
+// Fixed-point values u = rint(v * 2^sh) (nearest, ties to even) of 16 bf16 (two
+// 16-byte words, channel order) as the int8 planes hi = u >> 7 and lo = u & 127,
+// so that u = 128 hi + lo.  fma(v * s1, s2, 1.5 * 2^23) with s1 * s2 = 2^sh rounds
+// the exact product once to an integer and leaves u + 2^22 in the low 23 bits of
+// the result (|u| < 2^13): bits 0-6 are u & 127 and bits 7-14 are (u >> 7) & 0xff.
+// s1 = 2^(sh-127) and s2 = 2^127 (BIG) when 2^sh is beyond the fp32 range (heads
+// with max|V| below 2^-114); otherwise s2 = 2^sh alone.
+template <bool BIG>
+__device__ __forceinline__ void fixed_planes16(const v4i& wa, const v4i& wb, float s1, float s2, v4i& hi, v4i& lo) {
+  const uint32_t w[8] = {(uint32_t)wa[0], (uint32_t)wa[1], (uint32_t)wa[2], (uint32_t)wa[3],
+                         (uint32_t)wb[0], (uint32_t)wb[1], (uint32_t)wb[2], (uint32_t)wb[3]};
+  uint32_t q[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      u[i] = *reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.N + min(jb + 16 * i, a.N - 1)) * D + cg * 8);
+  for (int i = 0; i < 16; ++i) {
+    float f = __uint_as_float((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+    if (BIG) f *= s1;
+    q[i] = __float_as_uint(__builtin_fmaf(f, s2, 0x1.8p23f));
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = jb + 16 * i;
-      if (j >= a.N) break;
-      const size_t o = ((size_t)bh * a.N + j) * D + cg * 8;
-      const uint32_t h[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-      uint32_t ph[2] = {0u, 0u}, pl[2] = {0u, 0u};
+  for (int d = 0; d < 4; ++d) {
+    uint32_t h = 0u, l = 0u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (h[e >> 1] >> 16) : h[e >> 1];
-        const int q = (int)__builtin_rintf(ldexpf(bf2f(bits), sh));
-        ph[e >> 2] |= (uint32_t)((q >> 7) & 0xff) << (8 * (e & 3));
-        pl[e >> 2] |= (uint32_t)(q & 127) << (8 * (e & 3));
-      }
-      *reinterpret_cast<uint2*>(a.uhi + o) = make_uint2(ph[0], ph[1]);
-      *reinterpret_cast<uint2*>(a.ulo + o) = make_uint2(pl[0], pl[1]);
+    for (int k = 0; k < 4; ++k) {
+      h |= ((q[4 * d + k] >> 7) & 0xffu) << (8 * k);
+      l |= (q[4 * d + k] & 127u) << (8 * k);
     }
+    hi[d] = (int)h;
+    lo[d] = (int)l;
   }
 }
 
@@ -339,7 +340,8 @@ __global__ __launch_bounds__(1024) void k_km_init(Args a) {
     idx[t] = pos;
   }
   __syncthreads();
-  const int sh = a.kmsh[bh];
+  const int sh = head_shift(a, bh);
+  if (t == 0) a.kmsh[bh] = sh;
   __shared__ long long part[2][MAX_CLUSTERS];
   // eight centroids at a time: thread (r, c) = (t / 128, channel t % 128), so the
   // row loads of eight centroids are in flight together
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(1024) void k_km_init(Args a) {
 #pragma unroll 2
   for (int kk = t >> 7; kk < C; kk += 8) {
     const size_t src = ((size_t)bh * a.N + idx[kk]) * D + c;
-    const int u = 128 * (int)a.uhi[src] + (int)a.ulo[src];
+    const int u = (int)__builtin_rintf(ldexpf(bf2f(a.v[src]), sh));
     a.centfix[((size_t)bh * C + kk) * D + c] = u;
     a.cent[((size_t)bh * C + kk) * D + c] = ldexpf((float)u, -sh);
     const long long s2 = wave_sum_i64((long long)u * u);
@@ -367,7 +369,8 @@ __global__ __launch_bounds__(1024) void k_km_init(Args a) {
 __global__ __launch_bounds__(128) void k_km_warm(Args a) {
   __shared__ long long part[2][MAX_CLUSTERS];
   const int bh = blockIdx.x, C = a.C, t = threadIdx.x;
-  const int sh = a.kmsh[bh];
+  const int sh = head_shift(a, bh);
+  if (t == 0) a.kmsh[bh] = sh;
   for (int kk = 0; kk < C; ++kk) {
     const size_t o = ((size_t)bh * C + kk) * D + t;
     const float x = fminf(fmaxf(__builtin_rintf(ldexpf(a.cent[o], sh)), -8192.0f), 8191.0f);
@@ -495,10 +498,14 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
   }
 }
 
-// first: the first iteration of this prepare call, where every token enters its
-// cluster (labels from an earlier call are not read).
-template <int NT>
-__global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) {
+// FIRST: the first iteration of this prepare call, where every token enters its
+// cluster (labels from an earlier call are not read) and the fixed-point planes
+// are formed from V.
+template <int NT, bool FIRST>
+// Up to 48 clusters two workgroups share a CU (four waves per SIMD), which the
+// chunk count assumes; the first-iteration kernel for 33-48 clusters then spills
+// 16 bytes per lane rather than run in two rounds.
+__global__ __launch_bounds__(64 * KM_WAVES) __attribute__((amdgpu_waves_per_eu(NT <= 3 ? 4 : 2))) void k_km_assign(Args a) {
   extern __shared__ __align__(16) unsigned char km_smem[];
   const int C = a.C;
   int8_t* chi = reinterpret_cast<int8_t*>(km_smem);                       // [C][CROW]
@@ -521,6 +528,14 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     for (int v = 0; v < 4; ++v) cc[kt][v] = a.kmcc[(size_t)bh * C + min(16 * kt + 4 * g + v, C - 1)];
   const int8_t* uhi = a.uhi + (size_t)bh * a.N * D;
   const int8_t* ulo = a.ulo + (size_t)bh * a.N * D;
+  // The first iteration reads V itself, forms the fixed-point planes of each
+  // token where it uses them, and stores them for the later iterations: a lane
+  // loads its token's channels 16g..16g+15 (into h0, h1) and 64+16g..64+16g+15
+  // (into l0, l1) as bf16, the same 64 bytes as the planes.
+  const uint16_t* vh = a.v + (size_t)bh * a.N * D;
+  const int sh = FIRST ? head_shift(a, bh) : 0;
+  const bool big = sh > 127;  // uniform
+  const float s1 = big ? ldexpf(1.0f, sh - 127) : 1.0f, s2 = ldexpf(1.0f, big ? 127 : sh);
   // wave w takes 16-token subtiles w, w+KM_WAVES, ... of the chunk; the operands
   // and previous labels of the next subtile are loaded while the current one is
   // processed (two ahead measured slower: more registers, no latency to hide)
@@ -535,11 +550,19 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     int jj = first_tok + s * 16 + l16;
     const bool ok = jj < last;
     jj = ok ? jj : last - 1;  // tail lanes read a valid row, add nothing
-    x.h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
-    x.h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
-    x.l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
-    x.l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
-    x.old = (!first && ok) ? a.labels[(size_t)bh * a.N + jj] : -1;
+    if constexpr (FIRST) {
+      x.h0 = *reinterpret_cast<const v4i*>(vh + (size_t)jj * D + 16 * g);
+      x.h1 = *reinterpret_cast<const v4i*>(vh + (size_t)jj * D + 16 * g + 8);
+      x.l0 = *reinterpret_cast<const v4i*>(vh + (size_t)jj * D + 64 + 16 * g);
+      x.l1 = *reinterpret_cast<const v4i*>(vh + (size_t)jj * D + 64 + 16 * g + 8);
+      x.old = -1;
+    } else {
+      x.h0 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 16 * g);
+      x.h1 = *reinterpret_cast<const v4i*>(uhi + (size_t)jj * D + 64 + 16 * g);
+      x.l0 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 16 * g);
+      x.l1 = *reinterpret_cast<const v4i*>(ulo + (size_t)jj * D + 64 + 16 * g);
+      x.old = ok ? a.labels[(size_t)bh * a.N + jj] : -1;
+    }
   };
   auto has = [&](int s) { return s < KM_CHUNK / 16 && first_tok + s * 16 < last; };  // uniform per wave
   // moved tokens of later iterations: lane (g, q) of a drain takes ring entry
@@ -612,10 +635,33 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
 #pragma unroll 1
   for (int sub = w; sub < KM_CHUNK / 16; sub += KM_WAVES) {
     if (!has(sub)) break;
-    const v4i bh0 = nx.h0, bh1 = nx.h1, bl0 = nx.l0, bl1 = nx.l1;
-    const int old = nx.old;
+    const Sub cur = nx;
     if (has(sub + KM_WAVES)) load_sub(sub + KM_WAVES, nx);
     const int j = first_tok + sub * 16 + l16;
+    const int old = cur.old;
+    v4i bh0, bh1, bl0, bl1;
+    if constexpr (FIRST) {
+      if (big) {
+        fixed_planes16<true>(cur.h0, cur.h1, s1, s2, bh0, bl0);
+        fixed_planes16<true>(cur.l0, cur.l1, s1, s2, bh1, bl1);
+      } else {
+        fixed_planes16<false>(cur.h0, cur.h1, s1, s2, bh0, bl0);
+        fixed_planes16<false>(cur.l0, cur.l1, s1, s2, bh1, bl1);
+      }
+      if (j < last) {
+        int8_t* ph = a.uhi + ((size_t)bh * a.N + j) * D;
+        int8_t* pl = a.ulo + ((size_t)bh * a.N + j) * D;
+        *reinterpret_cast<v4i*>(ph + 16 * g) = bh0;
+        *reinterpret_cast<v4i*>(ph + 64 + 16 * g) = bh1;
+        *reinterpret_cast<v4i*>(pl + 16 * g) = bl0;
+        *reinterpret_cast<v4i*>(pl + 64 + 16 * g) = bl1;
+      }
+    } else {
+      bh0 = cur.h0;
+      bh1 = cur.h1;
+      bl0 = cur.l0;
+      bl1 = cur.l1;
+    }
     double bestK = 0x1p52;
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
@@ -651,7 +697,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
     const int best = (int)__builtin_fma(-64.0, hi, bestK);
     // only a token whose label changes touches the bins
     const bool moved = j < last && best != old;
-    if (first) {
+    if constexpr (FIRST) {
       // every token enters: the adds run on the subtile's own operands
       if (__ballot(moved) != 0ull && moved) {
         if (g == 0) {
@@ -682,7 +728,7 @@ __global__ __launch_bounds__(64 * KM_WAVES) void k_km_assign(Args a, int first) 
       }
     }
   }
-  if (qn > 0) drain(qn);
+  if (!FIRST && qn > 0) drain(qn);
   __syncthreads();
   int* part = a.kmpart + ((size_t)bh * a.nkm + chunk) * C * D;
   for (int e = t; e < C * D; e += 64 * KM_WAVES) {
@@ -1553,6 +1599,14 @@ int km_chunks(const Args& a, int cus) {
 
 }  // namespace
 
+template <int NT>
+void launch_assign(const Args& a, bool first, dim3 kg, dim3 kb, size_t sm, hipStream_t st) {
+  if (first)
+    hipLaunchKernelGGL((k_km_assign<NT, true>), kg, kb, sm, st, a);
+  else
+    hipLaunchKernelGGL((k_km_assign<NT, false>), kg, kb, sm, st, a);
+}
+
 hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   Args a = a_in;
   const unsigned BH = (unsigned)a.BH;
@@ -1571,7 +1625,6 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   hipLaunchKernelGGL(k_prep_zero, dim3(BH), dim3(128), 0, st, a);
   if (kmeans) {
     hipLaunchKernelGGL(k_vmax, dim3(a.nkc, BH), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_vfix, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
     if (mode == ClusterMode::Warm)
       hipLaunchKernelGGL(k_km_warm, dim3(BH), dim3(128), 0, st, a);
     else
@@ -1579,15 +1632,15 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
     for (int it = 0; it < a.T; ++it) {
       const dim3 kg(a.nkm, BH), kb(64 * KM_WAVES);
       const size_t sm = km_smem_bytes(a.C);
-      const int first = it == 0 ? 1 : 0;
+      const bool first = it == 0;
       if (a.C <= 16)
-        hipLaunchKernelGGL(k_km_assign<1>, kg, kb, sm, st, a, first);
+        launch_assign<1>(a, first, kg, kb, sm, st);
       else if (a.C <= 32)
-        hipLaunchKernelGGL(k_km_assign<2>, kg, kb, sm, st, a, first);
+        launch_assign<2>(a, first, kg, kb, sm, st);
       else if (a.C <= 48)
-        hipLaunchKernelGGL(k_km_assign<3>, kg, kb, sm, st, a, first);
+        launch_assign<3>(a, first, kg, kb, sm, st);
       else
-        hipLaunchKernelGGL(k_km_assign<4>, kg, kb, sm, st, a, first);
+        launch_assign<4>(a, first, kg, kb, sm, st);
       hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
     }
     hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);

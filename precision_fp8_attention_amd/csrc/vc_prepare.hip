@@ -474,10 +474,25 @@ __global__ __launch_bounds__(128) void k_km_update(Args a) {
   const int kk = blockIdx.x, bh = blockIdx.y, c = threadIdx.x, C = a.C;
   long long* sum = a.kmsum + ((size_t)bh * C + kk) * D + c;
   long long s = *sum, n = a.kmn[(size_t)bh * C + kk];
-#pragma unroll 8
-  for (int ch = 0; ch < a.nkm; ++ch) {
-    s += a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
-    n += a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
+  // the chunks' changes 16 at a time, all 16 loads issued before the first wait
+  // (chunks past the last read the last one and add nothing); integer adds, so
+  // the order cannot change the sums
+  for (int ch0 = 0; ch0 < a.nkm; ch0 += 16) {
+    int dp[16], dn[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int ch = min(ch0 + k, a.nkm - 1);
+      dp[k] = a.kmpart[(((size_t)bh * a.nkm + ch) * C + kk) * D + c];
+      dn[k] = a.kmcnt[((size_t)bh * a.nkm + ch) * C + kk];
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      pin_loaded(dp[k]);
+      if (ch0 + k < a.nkm) {
+        s += dp[k];
+        n += dn[k];
+      }
+    }
   }
   *sum = s;
   int u;

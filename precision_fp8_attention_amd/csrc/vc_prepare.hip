@@ -857,14 +857,13 @@ __global__ __launch_bounds__(256) void k_perm_identity(Args a) {
 // t/16 + 16i), so 16 threads cover one 256-byte row.  A thread keeps its 8 rows
 // as raw bf16 (32 registers, not 64 floats) and converts them where they are
 // used, which doubles the waves a CU holds and the rows in flight.
+// One workgroup of 256 threads per (block, head, Q or K).
 template <bool SMOOTH>
-// Seven workgroups per CU: 72 VGPRs; at eight the compiler spills to scratch
-// (measured the same time, or 3 us slower with clusters reused).
-__global__ __launch_bounds__(256, SMOOTH ? 4 : 7) void k_qk_quant(Args a) {
+__device__ __forceinline__ void qk_quant_block(const Args& a, int blk, int bh, int isk) {
   __shared__ float wmax[4];
   __shared__ long long qsum[16][D];
   __shared__ float qmean[D];
-  const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int cg = t & 15, r0 = t >> 4;
   const bool follow = isk || (a.flags & VC_PERMUTE_Q);
   const bool smooth = SMOOTH && !isk;  // uniform over the workgroup
@@ -1201,7 +1200,7 @@ __global__ __launch_bounds__(256, 6) void k_ksum_v_stats(Args a) {
 // channel: sv = max/448, inv = 448/max; 1 with the 4-bit residual), and block
 // blk's mean in V code units (mu * inv).  Block 0 also stores the scales.  The
 // bf16 high/low pairs of the means that the restore MFMA reads are formed from
-// these by k_rep_select, which writes them in whole rows.
+// these by the repair selection (k_qk_quant_rep), which writes them in whole rows.
 __device__ __forceinline__ void v_channel(const Args& a, int bh, int blk, int c, float* mu_out, float* s_out,
                                           float* inv_out) {
   float s, inv;
@@ -1372,20 +1371,22 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
 // of RS_COPIES lanes of a wave counts into its own copy instead (no two lanes
 // of an instruction share an address), and the copies are summed for the scan.
 // The compaction gives each wave one contiguous run of positions, so it needs
-// two barriers rather than four per 1024 positions.
-constexpr int RS_COPIES = 32;
-__global__ __launch_bounds__(1024) void k_rep_select(Args a) {
-  __shared__ int hist[256][RS_COPIES];
+// two barriers rather than four per NTH positions.  One workgroup of NTH
+// threads per head; COPIES lane-private histogram copies.
+template <int NTH, int COPIES>
+__device__ __forceinline__ void rep_select_head(const Args& a, int bh) {
+  constexpr int NW = NTH / 64;
+  __shared__ int hist[256][COPIES];
   __shared__ unsigned long long s_prefix, s_mask;
   __shared__ int s_kth, s_kth_next, s_hsel;
-  __shared__ int wtot[16];
-  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ int wtot[NW];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   // the restore operand first: the bf16 high/low pair of every block mean in V
   // code units, [group of 16 blocks][high, low][channel][block in group], slots
   // past the last block 0.  A thread forms one (group, channel) row of 16
   // blocks and stores it whole (the quantisation workgroups, one per block,
   // would each write 2 bytes into every row).
-  for (int e = t; e < a.nch16 * D; e += 1024) {
+  for (int e = t; e < a.nch16 * D; e += NTH) {
     const int grp = e / D, c = e % D;
     const float* mp = a.mup + ((size_t)bh * a.nblk + grp * 16) * D + c;
     uint32_t hw[8], lw[8];
@@ -1410,7 +1411,7 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
     reinterpret_cast<uint4*>(dst + D * 16)[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
   }
   if (a.m == 0) return;  // no repair set (uniform)
-  const int cp = lane & (RS_COPIES - 1);
+  const int cp = lane & (COPIES - 1);
   const float* err = a.err + (size_t)bh * a.N;
   auto key_of = [&](int j, int e) { return ((unsigned long long)(~(unsigned)e) << 32) | (unsigned)j; };
   // the error bits of positions j0, j0 + step, ..., 8 at a time: all 8 loads
@@ -1428,27 +1429,27 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
     s_kth = a.m;
   }
   for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int e = t; e < 256 * RS_COPIES; e += 1024) (&hist[0][0])[e] = 0;
+    for (int e = t; e < 256 * COPIES; e += NTH) (&hist[0][0])[e] = 0;
     __syncthreads();
     const unsigned long long pre = s_prefix, msk = s_mask;
-    for (int jb = t; jb < a.N; jb += 1024 * 8) {
+    for (int jb = t; jb < a.N; jb += NTH * 8) {
       int e[8];
-      load8(jb, 1024, e);
+      load8(jb, NTH, e);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = jb + 1024 * u;
+        const int j = jb + NTH * u;
         const unsigned long long key = key_of(j, e[u]);
         if (j < a.N && (key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255][cp], 1);
       }
     }
     __syncthreads();
-    // bin totals (threads 0..255; copy i of bin t read at (i + t) mod RS_COPIES,
+    // bin totals (threads 0..255; copy i of bin t read at (i + t) mod COPIES,
     // so the lanes of a read hit distinct banks), then a parallel exclusive scan;
     // the one bin where the running count crosses kth fixes the next digit
     int h = 0, incl = 0;
     if (t < 256) {
 #pragma unroll 8
-      for (int i = 0; i < RS_COPIES; ++i) h += hist[t][(i + t) & (RS_COPIES - 1)];
+      for (int i = 0; i < COPIES; ++i) h += hist[t][(i + t) & (COPIES - 1)];
       incl = h;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -1485,7 +1486,7 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
                                             // above it and below the next one
   int* out = a.rep_pos + (size_t)bh * a.mpad;
   // wave w owns positions [j0, j1): count its selected keys, then write them
-  const int per = (((a.N + 15) / 16) + 63) & ~63;
+  const int per = (((a.N + NW - 1) / NW) + 63) & ~63;
   const int j0 = min(w * per, a.N), j1 = min(j0 + per, a.N);
   const unsigned long long lt = (1ull << lane) - 1ull;
   int cnt = 0;
@@ -1515,7 +1516,26 @@ __global__ __launch_bounds__(1024) void k_rep_select(Args a) {
       slot += __popcll(b);
     }
   }
-  for (int i = a.m + t; i < a.mpad; i += 1024) out[i] = -1;
+  for (int i = a.m + t; i < a.mpad; i += NTH) out[i] = -1;
+}
+
+// The repair selection and the Q/K codes in one launch.  The selection runs one
+// workgroup per head and leaves most of the chip idle; the code workgroups do
+// not depend on it, so they fill the chip around it.  grid 1-D: workgroups
+// x < BH select head x's repair set (first, so they start first); the rest are
+// the code workgroups in (block, head, Q/K) order.  Seven code workgroups per
+// CU (at eight the compiler spills); the selection's histogram keeps 8 copies
+// (8 KB of LDS) so that it does not lower that.
+template <bool SMOOTH>
+__global__ __launch_bounds__(256, SMOOTH ? 4 : 7) void k_qk_quant_rep(Args a) {
+  const unsigned x = blockIdx.x, BH = (unsigned)a.BH;
+  if (x < BH) {  // uniform over the workgroup
+    rep_select_head<256, 8>(a, (int)x);
+    return;
+  }
+  const unsigned q = x - BH, per = (unsigned)a.nblk * BH;
+  const unsigned r = q % per;
+  qk_quant_block<SMOOTH>(a, (int)(r % (unsigned)a.nblk), (int)(r / (unsigned)a.nblk), (int)(q / per));
 }
 
 // Residual error (bf16; V code units, real units with VC_V4) of the repaired
@@ -1664,18 +1684,19 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
   }
   // the K channel sums (needed by the K codes) with the V block statistics
   hipLaunchKernelGGL(k_ksum_v_stats, dim3(a.nkc + a.nblk, BH), dim3(256), 0, st, a);
-  if (a.flags & VC_SMOOTH_Q)
-    hipLaunchKernelGGL(k_qk_quant<true>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_qk_quant<false>, dim3(a.nblk, BH, 2), dim3(256), 0, st, a);
-  if (a.flags & VC_SMOOTH_Q)
-    hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 31) / 32, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   if (a.flags & VC_V4)
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
-  // the restore operand always; the repair set when there is one
-  hipLaunchKernelGGL(k_rep_select, dim3(BH), dim3(1024), 0, st, a);
+  // the restore operand always and the repair set when there is one (they need
+  // the V codes' criterion), beside the Q/K codes
+  const unsigned nqr = BH + 2u * (unsigned)a.nblk * BH;
+  if (a.flags & VC_SMOOTH_Q)
+    hipLaunchKernelGGL(k_qk_quant_rep<true>, dim3(nqr), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_qk_quant_rep<false>, dim3(nqr), dim3(256), 0, st, a);
+  if (a.flags & VC_SMOOTH_Q)
+    hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 31) / 32, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
   if (a.m > 0) hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);
   return hipGetLastError();
 }

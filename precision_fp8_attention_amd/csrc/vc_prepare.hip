@@ -1373,6 +1373,8 @@ __global__ __launch_bounds__(64) void k_v_quant4(Args a) {
 // The compaction gives each wave one contiguous run of positions, so it needs
 // two barriers rather than four per NTH positions.  One workgroup of NTH
 // threads per head; COPIES lane-private histogram copies.
+__device__ __forceinline__ void rep_delta_half(const Args& a, int bh, int gs, int c0);
+
 template <int NTH, int COPIES>
 __device__ __forceinline__ void rep_select_head(const Args& a, int bh) {
   constexpr int NW = NTH / 64;
@@ -1517,6 +1519,11 @@ __device__ __forceinline__ void rep_select_head(const Args& a, int bh) {
     }
   }
   for (int i = a.m + t; i < a.mpad; i += NTH) out[i] = -1;
+  // the repair deltas of the selected slots: two threads per slot, 64 channels
+  // each (the positions were stored by this workgroup before the barrier)
+  static_assert(NTH % 128 == 0, "whole slots per pass");
+  __syncthreads();
+  for (int e = t; e < 2 * a.mpad; e += NTH) rep_delta_half(a, bh, e % a.mpad, (e / a.mpad) * (D / 2));
 }
 
 // The repair selection and the Q/K codes in one launch.  The selection runs one
@@ -1538,75 +1545,62 @@ __global__ __launch_bounds__(256, SMOOTH ? 4 : 7) void k_qk_quant_rep(Args a) {
   qk_quant_block<SMOOTH>(a, (int)(r % (unsigned)a.nblk), (int)(r / (unsigned)a.nblk), (int)(q / per));
 }
 
-// Residual error (bf16; V code units, real units with VC_V4) of the repaired
-// positions, channel-major with the repair-slot interleave.  grid (mpad/128, BH), 128 threads = slots.
-__global__ __launch_bounds__(128) void k_rep_delta(Args a) {
-  __shared__ __align__(16) uint16_t tile[D * BLK];
-  const int grp = blockIdx.x, bh = blockIdx.y, s = threadIdx.x;
-  const int gs = grp * BLK + s;
-  const int col = rep_col(s);
+// Residual error (bf16; V code units, real units with VC_V4) of channels
+// c0 .. c0+63 of repair slot gs of head bh, stored straight into the
+// channel-major slot layout (rep_col interleave) that the forward's repair MFMA
+// reads; slots past m hold 0.  The V codes are recomputed exactly as the V code
+// kernels form them.
+__device__ __forceinline__ void rep_delta_half(const Args& a, int bh, int gs, int c0) {
+  const int grp = gs / BLK, col = rep_col(gs % BLK);
+  uint16_t* dst = a.rep_dt + ((size_t)bh * D + c0) * a.mpad + (size_t)grp * BLK + col;
   const int p = gs < a.m ? a.rep_pos[(size_t)bh * a.mpad + gs] : -1;
-  if (p >= 0 && (a.flags & VC_V4)) {
-    // 4-bit residual: the error of the E2M1 code under its group's power of two,
-    // in real units (the code is recomputed exactly as k_v_quant4 forms it)
-    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
-    const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
-    const uint8_t* xr = a.v4s + ((size_t)bh * a.nblk + p / BLK) * V4_SREC + 16 * v4_group(p % BLK) * 8;
-    // the whole row is loaded before the first wait
-    uint4 rw[D / 8];
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) rw[i] = *reinterpret_cast<const uint4*>(row + i * 8);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) pin_loaded(rw[i]);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = rw[i];
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = i * 8 + j;
-        const int X = (int)xr[(c & 15) * 8 + (c >> 4)] - 127;
-        const float x = bf2f((j & 1) ? (h[j >> 1] >> 16) : h[j >> 1]) - mu[c];
-        uint32_t code;
-        const float val = e2m1_round(__builtin_ldexpf(x, -X), &code);
-        tile[c * BLK + col] = f2bf_rne(x - __builtin_ldexpf(val, X));
-      }
-    }
-  } else if (p >= 0) {
-    const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D;
-    const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D;
-    const float* inv = a.inv + (size_t)bh * D;
-    // the whole row is loaded before the first wait
-    uint4 rw[D / 8];
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) rw[i] = *reinterpret_cast<const uint4*>(row + i * 8);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) pin_loaded(rw[i]);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = rw[i];
-      const uint32_t h[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = i * 8 + 2 * j;
-        const float x0 = (bf2f(h[j]) - mu[c]) * inv[c];
-        const float x1 = (bf2f(h[j] >> 16) - mu[c + 1]) * inv[c + 1];
-        const uint32_t cc = e4m3x2(x0, x1);
-        tile[c * BLK + col] = f2bf_rne(x0 - e4m3_val(cc & 0xff));
-        tile[(c + 1) * BLK + col] = f2bf_rne(x1 - e4m3_val(cc >> 8));
-      }
-    }
-  } else {
-    for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
+  if (p < 0) {
+#pragma unroll 8
+    for (int c = 0; c < D / 2; ++c) dst[(size_t)c * a.mpad] = 0;
+    return;
   }
-  __syncthreads();
-  uint16_t* dst = a.rep_dt + ((size_t)bh * D + s) * a.mpad + (size_t)grp * BLK;
+  const uint16_t* row = a.v + ((size_t)bh * a.N + a.perm[(size_t)bh * a.N + p]) * D + c0;
+  const float* mu = a.mu + ((size_t)bh * a.nblk + p / BLK) * D + c0;
+  const uint8_t* xr = a.v4s + ((size_t)bh * a.nblk + p / BLK) * V4_SREC + 16 * v4_group(p % BLK) * 8;
+  const float* inv = a.inv + (size_t)bh * D + c0;
+  // 32 channels at a time, their row words loaded before the first wait (the
+  // selection shares its launch with the Q/K codes and their register budget)
+  for (int q = 0; q < 2; ++q) {
+    uint4 rw[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    *reinterpret_cast<uint4*>(dst + 8 * i) = *reinterpret_cast<const uint4*>(tile + s * BLK + 8 * i);
+    for (int i = 0; i < 4; ++i) rw[i] = *reinterpret_cast<const uint4*>(row + 32 * q + i * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pin_loaded(rw[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h[4] = {rw[i].x, rw[i].y, rw[i].z, rw[i].w};
+      const int cb = 32 * q + 8 * i;  // channel c0 + cb of the chunk's first word
+      if (a.flags & VC_V4) {
+        // 4-bit residual: the error of the E2M1 code under its group's power
+        // of two, in real units
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + cb + j;
+          const int X = (int)xr[(c & 15) * 8 + (c >> 4)] - 127;
+          const float x = bf2f((j & 1) ? (h[j >> 1] >> 16) : h[j >> 1]) - mu[cb + j];
+          uint32_t code;
+          const float val = e2m1_round(__builtin_ldexpf(x, -X), &code);
+          dst[(size_t)(cb + j) * a.mpad] = f2bf_rne(x - __builtin_ldexpf(val, X));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = cb + 2 * j;
+          const float x0 = (bf2f(h[j]) - mu[c]) * inv[c];
+          const float x1 = (bf2f(h[j] >> 16) - mu[c + 1]) * inv[c + 1];
+          const uint32_t cc = e4m3x2(x0, x1);
+          dst[(size_t)c * a.mpad] = f2bf_rne(x0 - e4m3_val(cc & 0xff));
+          dst[(size_t)(c + 1) * a.mpad] = f2bf_rne(x1 - e4m3_val(cc >> 8));
+        }
+      }
+    }
+  }
 }
-
-// Header: marks the clusters valid for this shape.  grid 1, 64 threads.
 
 // Number of k-means chunks per head for a device with cus compute units.  The
 // assignment moves every token's 256 bytes once per iteration, and a CU's
@@ -1688,8 +1682,8 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
     hipLaunchKernelGGL(k_v_quant4, dim3(a.nblk, BH), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL(k_v_quant, dim3(a.nblk, BH), dim3(128), 0, st, a);
-  // the restore operand always and the repair set when there is one (they need
-  // the V codes' criterion), beside the Q/K codes
+  // the restore operand always, and the repair set with its deltas when there is
+  // one (they need the V codes' criterion), beside the Q/K codes
   const unsigned nqr = BH + 2u * (unsigned)a.nblk * BH;
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qk_quant_rep<true>, dim3(nqr), dim3(256), 0, st, a);
@@ -1697,7 +1691,6 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
     hipLaunchKernelGGL(k_qk_quant_rep<false>, dim3(nqr), dim3(256), 0, st, a);
   if (a.flags & VC_SMOOTH_Q)
     hipLaunchKernelGGL(k_qbias, dim3((a.nblk + 31) / 32, (a.Npad + 255) / 256, BH), dim3(256), 0, st, a);
-  if (a.m > 0) hipLaunchKernelGGL(k_rep_delta, dim3(a.mpad / BLK, BH), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

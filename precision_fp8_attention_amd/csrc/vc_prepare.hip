@@ -1263,11 +1263,13 @@ __global__ __launch_bounds__(128) void k_v_quant(Args a) {
     for (int c = 0; c < D; ++c) tile[c * BLK + col] = 0;
   }
   __syncthreads();
-  // 128 channel rows x 128 bytes: thread t stores row t
-  uint8_t* dst = a.v8t + ((size_t)bh * D + t) * a.Npad + (size_t)blk * BLK;
+  // 128 channel rows x 128 bytes, 8 lanes per row: each store writes 16 whole rows
+  uint8_t* dst = a.v8t + (size_t)bh * D * a.Npad + (size_t)blk * BLK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + t * BLK + 16 * i);
+  for (int i = 0; i < 8; ++i) {
+    const int c = 16 * i + (t >> 3), ch = t & 7;
+    *reinterpret_cast<uint4*>(dst + (size_t)c * a.Npad + 16 * ch) = *reinterpret_cast<const uint4*>(tile + c * BLK + 16 * ch);
+  }
 }
 
 // 4-bit residual codes (VC_V4) and the repair criterion.  The group exponents

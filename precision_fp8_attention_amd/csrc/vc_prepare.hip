@@ -663,13 +663,29 @@ __global__ __launch_bounds__(64 * KM_WAVES) __attribute__((amdgpu_waves_per_eu(N
         fixed_planes16<false>(cur.h0, cur.h1, s1, s2, bh0, bl0);
         fixed_planes16<false>(cur.l0, cur.l1, s1, s2, bh1, bl1);
       }
-      if (j < last) {
-        int8_t* ph = a.uhi + ((size_t)bh * a.N + j) * D;
-        int8_t* pl = a.ulo + ((size_t)bh * a.N + j) * D;
-        *reinterpret_cast<v4i*>(ph + 16 * g) = bh0;
-        *reinterpret_cast<v4i*>(ph + 64 + 16 * g) = bh1;
-        *reinterpret_cast<v4i*>(pl + 16 * g) = bl0;
-        *reinterpret_cast<v4i*>(pl + 64 + 16 * g) = bl1;
+      // Stored as whole 128-byte rows: lanes l16 and l16 ^ 8 swap one half of
+      // their token's row (a DPP rotation by 8 within the 16-lane row), so each
+      // store writes eight complete rows (chunk g from the lower eight lanes,
+      // chunk 4 + g from the upper eight) instead of sixteen half rows.
+      const bool up = l16 >= 8;
+      v4i sh0, sl0, sh1, sl1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int xh = __builtin_amdgcn_mov_dpp(up ? bh0[e] : bh1[e], 0x128, 0xf, 0xf, false);
+        const int xl = __builtin_amdgcn_mov_dpp(up ? bl0[e] : bl1[e], 0x128, 0xf, 0xf, false);
+        sh0[e] = up ? xh : bh0[e];
+        sh1[e] = up ? bh1[e] : xh;
+        sl0[e] = up ? xl : bl0[e];
+        sl1[e] = up ? bl1[e] : xl;
+      }
+      const int ra = first_tok + sub * 16 + (l16 & 7), rb = ra + 8, cb = 16 * g + (up ? 64 : 0);
+      if (ra < last) {
+        *reinterpret_cast<v4i*>(a.uhi + ((size_t)bh * a.N + ra) * D + cb) = sh0;
+        *reinterpret_cast<v4i*>(a.ulo + ((size_t)bh * a.N + ra) * D + cb) = sl0;
+      }
+      if (rb < last) {
+        *reinterpret_cast<v4i*>(a.uhi + ((size_t)bh * a.N + rb) * D + cb) = sh1;
+        *reinterpret_cast<v4i*>(a.ulo + ((size_t)bh * a.N + rb) * D + cb) = sl1;
       }
     } else {
       bh0 = cur.h0;

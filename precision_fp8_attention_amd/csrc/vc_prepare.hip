@@ -790,47 +790,95 @@ __device__ __forceinline__ void write_header(const Args& a, uint32_t clustered) 
   a.header->C = a.C;
 }
 
-__global__ __launch_bounds__(1024) void k_perm(Args a) {
+// Stable counting sort of a head's tokens by cluster id, over the k-means chunks
+// (grid (chunks, BH), 16 waves): k_perm_count writes each chunk's cluster counts
+// (into the k-means count buffer, free once the last update has run), then
+// k_perm_scatter places every token at
+//   (tokens of smaller clusters) + (same cluster, earlier chunks)
+//   + (same cluster, earlier waves of its chunk) + (same cluster, lower lanes of
+//   earlier steps and of its own step),
+// i.e. cluster order with ties in token order.  A wave takes a contiguous run of
+// its chunk 64 tokens per step; lanes with the same label find each other by a
+// ballot over the label bits.
+struct PermRun {
+  int j0, j1;  // the wave's tokens
+};
+__device__ __forceinline__ PermRun perm_run(const Args& a, int ch, int w) {
+  const int csz = ((a.N + a.nkm - 1) / a.nkm + 15) & ~15;  // the k-means chunks
+  const int first = min(ch * csz, a.N), last = min(first + csz, a.N);
+  const int per = (((csz + 15) / 16) + 63) & ~63;
+  const int j0 = min(first + w * per, last);
+  return {j0, min(j0 + per, last)};
+}
+// lanes with the same label as this lane (a lane past the run takes the sentinel
+// bucket MAX_CLUSTERS)
+__device__ __forceinline__ unsigned long long label_peers(int l) {
+  unsigned long long peers = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const unsigned long long m = __ballot((l >> b) & 1);
+    peers &= ((l >> b) & 1) ? m : ~m;
+  }
+  return peers;
+}
+// per-wave cluster counts of the wave's run into wcnt[w][.] (zeroed by the caller)
+__device__ __forceinline__ void perm_count_run(const int* lab, PermRun r, int lane, int* wrow) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int jb = r.j0; jb < r.j1; jb += 64) {
+    const int j = jb + lane;
+    const int l = j < r.j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = label_peers(l);
+    // the lowest lane of each label adds the label's count (distinct words)
+    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wrow[l] += __popcll(peers);
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_perm_count(Args a) {
+  __shared__ int wcnt[16][MAX_CLUSTERS + 1];
+  const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
+  for (int e = t; e < 16 * (MAX_CLUSTERS + 1); e += 1024) (&wcnt[0][0])[e] = 0;
+  __syncthreads();
+  perm_count_run(a.labels + (size_t)bh * a.N, perm_run(a, ch, w), lane, wcnt[w]);
+  __syncthreads();
+  if (t < C) {
+    int n = 0;
+#pragma unroll
+    for (int ww = 0; ww < 16; ++ww) n += wcnt[ww][t];
+    a.kmcnt[((size_t)bh * a.nkm + ch) * C + t] = n;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_perm_scatter(Args a) {
   __shared__ int wcnt[16][MAX_CLUSTERS + 1];  // per wave: count, then next position
-  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
+  __shared__ int tot[MAX_CLUSTERS], pre[MAX_CLUSTERS];
+  const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6, C = a.C;
   // the workspace now holds clusters for this shape (read back by later calls
   // that reuse them, after this launch has completed)
-  if (bh == 0 && t == 0) write_header(a, 1u);
+  if (bh == 0 && ch == 0 && t == 0) write_header(a, 1u);
   const int* lab = a.labels + (size_t)bh * a.N;
   int* perm = a.perm + (size_t)bh * a.N;
   int* iperm = a.iperm + (size_t)bh * a.N;
-  const int per = (((a.N + 15) / 16) + 63) & ~63;
-  const int j0 = min(w * per, a.N), j1 = min(j0 + per, a.N);
-  const unsigned long long lt = (1ull << lane) - 1ull;
+  const PermRun r = perm_run(a, ch, w);
   for (int e = t; e < 16 * (MAX_CLUSTERS + 1); e += 1024) (&wcnt[0][0])[e] = 0;
-  __syncthreads();
-  // lanes with the same label as this lane (ballot over the 7 label bits);
-  // a lane past the run takes the sentinel bucket MAX_CLUSTERS
-  auto peers_of = [&](int l) {
-    unsigned long long peers = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 7; ++b) {
-      const unsigned long long m = __ballot((l >> b) & 1);
-      peers &= ((l >> b) & 1) ? m : ~m;
-    }
-    return peers;
-  };
-  // (loading 8 steps' labels before the first wait measured 4 us slower here:
-  // the unrolled ballots outweigh the latency they hide)
-  for (int jb = j0; jb < j1; jb += 64) {
-    const int j = jb + lane;
-    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
-    const unsigned long long peers = peers_of(l);
-    // the lowest lane of each label adds the label's count (distinct words)
-    if (l < MAX_CLUSTERS && (peers & lt) == 0ull) wcnt[w][l] += __popcll(peers);
+  if (t < MAX_CLUSTERS) {
+    tot[t] = 0;
+    pre[t] = 0;
   }
   __syncthreads();
-  // first position of (wave, cluster): all tokens of smaller clusters, plus those
-  // of the same cluster in earlier runs
+  perm_count_run(lab, r, lane, wcnt[w]);
+  // every chunk's counts: cluster totals, and this cluster's tokens in earlier
+  // chunks (integer adds, any order)
+  const int* cnt = a.kmcnt + (size_t)bh * a.nkm * C;
+  for (int e = t; e < a.nkm * C; e += 1024) {
+    const int x = cnt[e], c = e % C;
+    atomicAdd(&tot[c], x);
+    if (e / C < ch) atomicAdd(&pre[c], x);
+  }
+  __syncthreads();
+  // first position of (wave, cluster)
   if (t < C) {
-    int below = 0;
-    for (int c = 0; c < t; ++c)
-      for (int ww = 0; ww < 16; ++ww) below += wcnt[ww][c];
+    int below = pre[t];
+    for (int c = 0; c < t; ++c) below += tot[c];
     for (int ww = 0; ww < 16; ++ww) {
       const int n = wcnt[ww][t];
       wcnt[ww][t] = below;
@@ -838,10 +886,11 @@ __global__ __launch_bounds__(1024) void k_perm(Args a) {
     }
   }
   __syncthreads();
-  for (int jb = j0; jb < j1; jb += 64) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int jb = r.j0; jb < r.j1; jb += 64) {
     const int j = jb + lane;
-    const int l = j < j1 ? lab[j] : MAX_CLUSTERS;
-    const unsigned long long peers = peers_of(l);
+    const int l = j < r.j1 ? lab[j] : MAX_CLUSTERS;
+    const unsigned long long peers = label_peers(l);
     if (l < MAX_CLUSTERS) {
       const int pos = wcnt[w][l] + __popcll(peers & lt);
       perm[pos] = j;
@@ -1690,7 +1739,8 @@ hipError_t launch_prepare(const Args& a_in, ClusterMode mode, hipStream_t st) {
         launch_assign<4>(a, first, kg, kb, sm, st);
       hipLaunchKernelGGL(k_km_update, dim3(a.C, BH), dim3(128), 0, st, a);
     }
-    hipLaunchKernelGGL(k_perm, dim3(BH), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(k_perm_count, dim3(a.nkm, BH), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(k_perm_scatter, dim3(a.nkm, BH), dim3(1024), 0, st, a);
   } else if (!vs) {
     hipLaunchKernelGGL(k_perm_identity, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a);
   }

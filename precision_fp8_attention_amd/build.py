@@ -15,7 +15,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvcattn.so")
-SOURCES = ["vc_api.cpp", "vc_prepare.hip", "vc_forward.hip"]
+# (source, object, extra flags): the forward source is compiled twice, its
+# plain and 4-bit-residual kernels with the max-ilp machine scheduler, its
+# smoothed-query and exact-score kernels with the default one
+SOURCES = [("vc_api.cpp", "vc_api.o", []), ("vc_prepare.hip", "vc_prepare.o", []),
+           ("vc_forward.hip", "vc_forward_ilp.o", ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+           ("vc_forward.hip", "vc_forward_default.o", ["-DVC_FWD_DEFAULT_SCHED"])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: fp32 decisions (k-means distances, E4M3 codes, the repair
@@ -30,14 +35,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
 # The max-ilp machine scheduler orders the forward's key loop for latency rather
 # than register pressure; it stays within the register budget (no spills) and
 # measured 0.6% faster with E4M3 V and 1.4% with the 4-bit V residual at
-# 2x24x16544, bit-identical.
-PER_FILE = {"vc_forward.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# 2x24x16544, bit-identical, but 13% slower for the smoothed-query kernel.
+PER_FILE = {"vc_forward.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(entry) -> str:
+    src, obj_name, extra = entry
+    obj = os.path.join(OBJDIR, obj_name)
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *PER_FILE.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *PER_FILE.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -803,14 +803,55 @@ __global__ __launch_bounds__(64 * (8 * QB / NS), 1) void k_fwd(Args a, int tile0
 
 }  // namespace
 
+// This file is compiled twice.  The plain and 4-bit-residual variants are
+// built with the max-ilp machine scheduler, which measured faster for them;
+// the smoothed-query and exact-score variants (VC_FWD_DEFAULT_SCHED) with the
+// default scheduler, which measured faster for the smoothed-query kernel.
+// variant = (exact ? 4 : 0) | (v4 ? 2 : 0) | (sq ? 1 : 0).
+#if defined(VC_FWD_DEFAULT_SCHED)
+#define VC_FWD_LAUNCH_PART launch_forward_default_sched
+#else
+#define VC_FWD_LAUNCH_PART launch_forward_ilp_sched
+#endif
+// two 16-query subtiles per wave (8 waves).  One subtile per wave (16 waves,
+// four per SIMD) caps a wave at 128 VGPRs: it spills in the key loop, reads
+// every K/V tile twice as often, and measured 8% slower.
+constexpr int kSubtiles = 2;
+
+void VC_FWD_LAUNCH_PART(int variant, unsigned full, unsigned rest, const Args& a, hipStream_t st) {
+  auto go = [&](auto qb_tag, auto ns_tag, unsigned nwg) {
+    constexpr int QB = decltype(qb_tag)::value, S = decltype(ns_tag)::value;
+    const dim3 grid(nwg), block(64 * (8 * QB / S));
+    const int tile0 = (int)full;
+#if defined(VC_FWD_DEFAULT_SCHED)
+    switch (variant) {
+      case 1: hipLaunchKernelGGL((k_fwd<false, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 3: hipLaunchKernelGGL((k_fwd<false, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 4: hipLaunchKernelGGL((k_fwd<true, false, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 5: hipLaunchKernelGGL((k_fwd<true, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
+      case 6: hipLaunchKernelGGL((k_fwd<true, true, false, S, QB>), grid, block, 0, st, a, tile0); break;
+      default: hipLaunchKernelGGL((k_fwd<true, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
+    }
+#else
+    if (variant == 2)
+      hipLaunchKernelGGL((k_fwd<false, true, false, S, QB>), grid, block, 0, st, a, tile0);
+    else
+      hipLaunchKernelGGL((k_fwd<false, false, false, S, QB>), grid, block, 0, st, a, tile0);
+#endif
+  };
+  if (full > 0) go(std::integral_constant<int, 2>{}, std::integral_constant<int, kSubtiles>{}, full);
+  if (rest > 0) go(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, 2 * rest);
+}
+
+#if !defined(VC_FWD_DEFAULT_SCHED)
+void launch_forward_default_sched(int variant, unsigned full, unsigned rest, const Args& a, hipStream_t st);
+
+static bool forward_variant_ilp(int variant) { return variant == 0 || variant == 2; }
+
 hipError_t launch_forward(const Args& a, hipStream_t st) {
   const unsigned tiles = (unsigned)a.BH * (unsigned)((a.nblk + 1) / 2);
   const bool exact = (a.flags & VC_EXACT_SCORES) != 0, v4 = (a.flags & VC_V4) != 0;
   const bool sq = (a.flags & VC_SMOOTH_Q) != 0;
-  // two 16-query subtiles per wave (8 waves).  One subtile per wave (16 waves,
-  // four per SIMD) caps a wave at 128 VGPRs: it spills in the key loop, reads
-  // every K/V tile twice as often, and measured 8% slower.
-  constexpr int NS = 2;
   // A tile workgroup fills its CU (one per CU), so the tiles run in rounds of
   // one per CU.  Whole rounds run as tiles.  The rest run as one-query-block
   // workgroups of 8 waves with one 16-query subtile each: half the work per
@@ -834,24 +875,12 @@ hipError_t launch_forward(const Args& a, hipStream_t st) {
     rest = 0;
   }
   const int variant = (exact ? 4 : 0) | (v4 ? 2 : 0) | (sq ? 1 : 0);
-  auto go = [&](auto qb_tag, auto ns_tag, unsigned nwg) {
-    constexpr int QB = decltype(qb_tag)::value, S = decltype(ns_tag)::value;
-    const dim3 grid(nwg), block(64 * (8 * QB / S));
-    const int tile0 = (int)full;
-    switch (variant) {
-      case 0: hipLaunchKernelGGL((k_fwd<false, false, false, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 1: hipLaunchKernelGGL((k_fwd<false, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 2: hipLaunchKernelGGL((k_fwd<false, true, false, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 3: hipLaunchKernelGGL((k_fwd<false, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 4: hipLaunchKernelGGL((k_fwd<true, false, false, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 5: hipLaunchKernelGGL((k_fwd<true, false, true, S, QB>), grid, block, 0, st, a, tile0); break;
-      case 6: hipLaunchKernelGGL((k_fwd<true, true, false, S, QB>), grid, block, 0, st, a, tile0); break;
-      default: hipLaunchKernelGGL((k_fwd<true, true, true, S, QB>), grid, block, 0, st, a, tile0); break;
-    }
-  };
-  if (full > 0) go(std::integral_constant<int, 2>{}, std::integral_constant<int, NS>{}, full);
-  if (rest > 0) go(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, 2 * rest);
+  if (forward_variant_ilp(variant))
+    launch_forward_ilp_sched(variant, full, rest, a, st);
+  else
+    launch_forward_default_sched(variant, full, rest, a, st);
   return hipGetLastError();
 }
+#endif
 
 }  // namespace vc

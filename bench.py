@@ -29,7 +29,6 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_flux2048cfg_traffic.json")
 FWD_SRC = os.path.join(ROOT, "precision_fp8_attention_amd", "csrc", "vc_forward.hip")
-BUILD_PY = os.path.join(ROOT, "precision_fp8_attention_amd", "build.py")  # holds the compile flags
 
 
 def _events_ms(fn, n):
@@ -62,15 +61,15 @@ def _events_each_ms(fn, n):
 def _traffic(launches_per_step: int):
     """HBM bytes per forward launch from the committed rocprofv3 counter summary,
     or None when it is missing or the kernel source or its compile flags
-    (the build script) changed since."""
+    changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
+        from precision_fp8_attention_amd import build as vc_build
         with open(FWD_SRC, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        with open(BUILD_PY, "rb") as f:
-            sha_build = hashlib.sha256(f.read()).hexdigest()
-        if t.get("kernel_source_sha256") != sha or t.get("build_script_sha256") != sha_build:
+        sha_flags = hashlib.sha256(json.dumps(vc_build.forward_compile_flags()).encode()).hexdigest()
+        if t.get("kernel_source_sha256") != sha or t.get("compile_flags_sha256") != sha_flags:
             return None
         return float(t["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
